@@ -1,0 +1,264 @@
+"""Benchmark: paged relative-bias attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+
+A step is one rpa_attn_varlen call (attention kernel + split combine) over
+one batch.  The headline workload is the batched decode batch (32 requests
+with 1024..8192 cached tokens, 32 q heads / 8 kv heads, head_dim 128, block
+size 16, rel_extent 128, planner-chosen splits); `value` is its algorithmic
+KV-and-operand bytes per second.  The same JSON line also carries the
+chunked-prefill batch (TFLOP/s against the bf16 MFMA peak), the 1M-token
+decode and the continuous-batching mix.  Inputs are resident in HBM before
+timing; the decode KV pool is rotated over three copies so that the 256 MB
+last-level cache cannot serve repeated steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode KV GB/s (% of HBM peak) and prefill TFLOP/s (% of bf16 MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+KERNEL_SOURCES = ["relative_bias_amd/csrc/rpa_kernels.hip", "relative_bias_amd/csrc/rpa_internal.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM traffic per launch from committed rocprofv3 --pmc summaries, if they
+    were taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def time_calls(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        fn(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms
+
+
+class Runner:
+    """Holds device buffers for one workload and times rpa_attn_varlen on it."""
+
+    def __init__(self, w, num_splits, pools=1):
+        import torch
+        from relative_bias_amd import binding as bnd
+        self.bnd = bnd
+        self.w = w
+        self.S = int(num_splits)
+        T, H, D = w.q.shape
+        dev = w.q.device
+        self.out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        nb = bnd.rpa_workspace_bytes(self.S, T, H, D)
+        self.ws = torch.empty((max(nb, 1),), dtype=torch.uint8, device=dev)
+        self.kv = [(w.key_cache, w.value_cache)]
+        for _ in range(pools - 1):
+            self.kv.append((w.key_cache.clone(), w.value_cache.clone()))
+
+    def call(self, i=0):
+        w = self.w
+        k, v = self.kv[i % len(self.kv)]
+        self.bnd.rpa_attn_varlen(
+            w.q, k, v, block_table=w.block_table, cache_seqlens=w.cache_seqlens,
+            cu_seqlens_q=w.cu_seqlens_q, max_seqlen_q=w.max_seqlen_q, softmax_scale=w.softmax_scale,
+            causal=w.causal, window_size=w.window_size, rel_extent=w.rel_extent,
+            rel_logits=w.rel_logits, num_splits=self.S, out=self.out, lse=self.lse, workspace=self.ws)
+
+    def combine_only(self, i=0):
+        """The split combine alone, on partial buffers of this call's shape."""
+        if not hasattr(self, "_po"):
+            import torch
+            T, H, D = self.w.q.shape
+            g = torch.Generator(device=self.w.q.device).manual_seed(1)
+            self._po = torch.randn((self.S, T, H, D), generator=g, device=self.w.q.device)
+            self._pl = torch.randn((self.S, T, H), generator=g, device=self.w.q.device)
+        self.bnd.rpa_split_combine(self._po, self._pl, out=self.out, lse=self.lse)
+
+
+def measure(runner, steps, warmup):
+    import torch
+    from relative_bias_amd import metrics
+    stream = torch.cuda.current_stream()
+    ms = time_calls(runner.call, steps, warmup, stream)
+    ms_comb = 0.0
+    if runner.S > 1:
+        ms_comb = time_calls(runner.combine_only, steps, warmup, stream)
+    wk = metrics.work(runner.w)
+    return ms, ms_comb, wk
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The fp64 oracle on a bounded sample of the decode batch (whole requests,
+    taken in order until about budget_s of CPU time), in GB/s of the same
+    algorithmic bytes."""
+    import torch
+    from oracle import attention as orc
+    from relative_bias_amd import metrics
+    wc = w.to("cpu")
+    cu = wc.cu_seqlens_q.tolist()
+    done_bytes, spent, nreq = 0, 0.0, 0
+    for b in range(wc.batch):
+        toks = list(range(cu[b], cu[b + 1]))
+        t0 = time.perf_counter()
+        orc.attention(wc.q, wc.key_cache, wc.value_cache, wc.block_table, wc.cache_seqlens,
+                      wc.cu_seqlens_q, wc.softmax_scale, wc.causal, wc.window_size, wc.rel_extent,
+                      wc.rel_logits, tokens=toks)
+        spent += time.perf_counter() - t0
+        sub = type("W", (), {})()
+        for k in ("num_heads", "num_kv_heads", "head_dim", "block_size", "rel_extent", "window_size",
+                  "causal"):
+            setattr(sub, k, getattr(wc, k))
+        sub.q_lens, sub.k_lens = [wc.q_lens[b]], [wc.k_lens[b]]
+        done_bytes += metrics.work(sub)["bytes"]
+        nreq += 1
+        if spent >= budget_s:
+            break
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": torch.get_num_threads(),
+            "kind": "oracle",
+            "sample": f"{nreq} of {wc.batch} requests of the batched decode batch (all 32 heads), "
+                      f"{spent:.1f} s of fp64 CPU work"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true", help="only the headline decode batch")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", default=None, help="run one workload: batched_decode, chunked_prefill, "
+                                                  "long_decode, continuous_batch")
+    a = ap.parse_args(argv)
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(see the sharding notes in the design document); run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    from relative_bias_amd import binding as bnd
+    from relative_bias_amd import workloads as wl
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    bnd.lib()
+    torch.manual_seed(0)
+    dev = "cuda"
+    results = {}
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    # Headline: batched decode.
+    run_main = a.only in (None, "batched_decode")
+    if run_main:
+        w = wl.batched_decode(device="cpu").to(dev)
+        S = bnd.rpa_choose_splits(w.batch, 1, w.num_heads, w.num_kv_heads, max(w.k_lens))
+        r = Runner(w, S, pools=3)
+        ms, ms_c, wk = measure(r, a.steps, a.warmup)
+        results["batched_decode"] = (w, S, ms, ms_c, wk)
+        log(f"batched_decode S={S}: {ms * 1e3:.1f} us/step (combine {ms_c * 1e3:.1f} us), "
+            f"{wk['bytes'] / ms / 1e6:.1f} GB/s")
+    if not a.no_extra or a.only:
+        if a.only in (None, "chunked_prefill"):
+            w3 = wl.chunked_prefill(device="cpu").to(dev)
+            r3 = Runner(w3, 1)
+            ms, ms_c, wk = measure(r3, max(5, a.steps // 2), a.warmup)
+            results["chunked_prefill"] = (w3, 1, ms, ms_c, wk)
+            log(f"chunked_prefill: {ms * 1e3:.1f} us/step, {wk['flops'] / ms / 1e9:.1f} TFLOP/s")
+            del r3, w3
+        if a.only in (None, "long_decode"):
+            w4 = wl.long_decode(device=dev)
+            S4 = bnd.rpa_choose_splits(1, 1, w4.num_heads, w4.num_kv_heads, max(w4.k_lens))
+            r4 = Runner(w4, S4)
+            ms, ms_c, wk = measure(r4, max(5, a.steps // 2), a.warmup)
+            results["long_decode"] = (w4, S4, ms, ms_c, wk)
+            log(f"long_decode S={S4}: {ms * 1e3:.1f} us/step, {wk['bytes'] / ms / 1e6:.1f} GB/s")
+            del r4, w4
+            torch.cuda.empty_cache()
+        if a.only in (None, "continuous_batch"):
+            w5 = wl.continuous_batch(device=dev)
+            r5 = Runner(w5, 1)
+            ms, ms_c, wk = measure(r5, max(5, a.steps // 2), a.warmup)
+            results["continuous_batch"] = (w5, 1, ms, ms_c, wk)
+            log(f"continuous_batch: {ms * 1e3:.1f} us/step, {wk['bytes'] / ms / 1e6:.1f} GB/s, "
+                f"{wk['flops'] / ms / 1e9:.1f} TFLOP/s")
+            del r5, w5
+            torch.cuda.empty_cache()
+
+    def summary(name):
+        w, S, ms, ms_c, wk = results[name]
+        return {"workload": name, "batch": w.batch, "num_tokens": w.num_tokens, "num_heads": w.num_heads,
+                "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                "rel_extent": w.rel_extent, "window": list(w.window_size), "num_splits": S,
+                "ms_per_step": round(ms, 5), "combine_ms": round(ms_c, 5),
+                "gbs": round(wk["bytes"] / ms / 1e6, 2), "tflops": round(wk["flops"] / ms / 1e9, 2),
+                "hbm_frac": round(wk["bytes"] / ms / 1e6 / HBM_PEAK_GBS, 4),
+                "mfma_frac": round(wk["flops"] / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "alg_bytes": wk["bytes"], "alg_flops": wk["flops"]}
+
+    head = a.only if a.only else "batched_decode"
+    w, S, ms, ms_c, wk = results[head]
+    kernel_ms = ms - ms_c
+    prefill_like = head == "chunked_prefill"
+    if prefill_like:
+        achieved = wk["flops"] / kernel_ms / 1e9
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+        value, unit = wk["flops"] / ms / 1e9, "TFLOP/s"
+    else:
+        achieved = wk["bytes"] / kernel_ms / 1e6
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        value, unit = wk["bytes"] / ms / 1e6, "GB/s"
+    roof["kernel"] = "attn_kernel<128>"
+    roof["kernel_ms"] = round(kernel_ms, 5)
+    roof["alg_bytes_per_launch"] = wk["bytes"]
+    roof["traffic"] = load_traffic(head)
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": summary(head), "roofline": roof,
+    }
+    for name in results:
+        if name != head:
+            line[name] = summary(name)
+    if not a.no_cpu and head == "batched_decode":
+        log("timing the CPU oracle on a sample ...")
+        line["cpu_baseline"] = cpu_baseline(w)
+    line["kernel_hash"] = kernel_hash()
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,155 @@
+/*
+ * rpa.h: paged, variable-length, causal attention with an additive relative
+ * position bias, for AMD MI355X (gfx950).  C ABI of librpa.so.
+ *
+ * The operation is the one the Inkling FA4 relative-attention walkthrough
+ * ("vllm中提取Inkling FA4 Relative Attention算子基础的base优化版本",
+ * nxmr.cn/news/19446) wraps around flash_attn_varlen_func: sections
+ * "_get_score_mod() 的内部" (the bias), "inkling_fa4_num_splits" (the split
+ * planner) and "主函数 inkling_fa4_rel_attention" (arguments and layouts).
+ * For request b with Lq = cu_seqlens_q[b+1] - cu_seqlens_q[b] query tokens
+ * and Lk = cache_seqlens[b] keys, query row i (packed token
+ * tok = cu_seqlens_q[b] + i) sits at absolute position qa = i + Lk - Lq and
+ * q head h reads kv head h / (H / Hkv).  Key t < Lk lives at
+ * key_cache[block_table[b, t / BS], t % BS, kv_head, :].  Key t is visible
+ * when causal implies t <= qa, window_left >= 0 implies t >= qa - left and
+ * window_right >= 0 implies t <= qa + right.  The logit of a visible key is
+ *     s = softmax_scale * <q[tok, h], k[t]>
+ *         + (0 <= qa - t < rel_extent ? rel_logits[tok, h, qa - t] : 0)
+ * and out[tok, h] = sum_t softmax(s)_t v[t], lse[tok, h] = ln sum_t exp(s_t).
+ * A row with no visible key gets out = 0 and lse = -inf.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers to contiguous row-major data
+ *     on the current HIP device; the caller owns them.  The library
+ *     allocates nothing and keeps no state between calls.
+ *   - Calls are asynchronous: they validate host-visible arguments, enqueue
+ *     kernels on `stream` (a hipStream_t; NULL = the default stream) and
+ *     return.  Any error status is returned BEFORE anything is enqueued,
+ *     except RPA_ERR_HIP, which reports a failed launch.
+ *   - bf16 means IEEE bfloat16 bit patterns (uint16 storage); outputs are
+ *     rounded to nearest even from fp32.
+ *   - Results are bitwise repeatable for fixed inputs and num_splits.
+ */
+#ifndef RPA_H
+#define RPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RPA_OK = 0,
+  RPA_ERR_NULL = -1,        /* a required pointer is NULL                         */
+  RPA_ERR_SHAPE = -2,       /* inconsistent or negative sizes                     */
+  RPA_ERR_UNSUPPORTED = -3, /* head_dim not 64/128, block_size not a multiple of 16 */
+  RPA_ERR_WORKSPACE = -4,   /* num_splits > 1 and the workspace is missing/small  */
+  RPA_ERR_HIP = -5          /* a HIP launch failed                                */
+} rpa_status;
+
+/* Largest num_splits accepted by rpa_attn_varlen. */
+#define RPA_MAX_SPLITS 128
+
+/*
+ * rpa_attn_varlen: the whole method in one call (attention kernel, plus the
+ * split combine when num_splits > 1).
+ *
+ *   q              bf16 [num_tokens, num_heads, head_dim], queries packed by
+ *                  cu_seqlens_q (already normalised / rotated by the caller).
+ *   key_cache,
+ *   value_cache    bf16 [num_blocks, block_size, num_kv_heads, head_dim].
+ *   block_table    int32 [batch, max_pages_per_seq]; only the first
+ *                  ceil(Lk / block_size) entries of a row are read and each
+ *                  must lie in [0, num_blocks); padding may hold any value.
+ *   cache_seqlens  int32 [batch]: Lk, the KV length INCLUDING this step's
+ *                  query tokens (their K/V are already in the cache).
+ *   cu_seqlens_q   int32 [batch + 1]: non-decreasing, cu[0] = 0,
+ *                  cu[batch] = num_tokens.
+ *   max_seqlen_q   must be >= every Lq.  It only bounds the launch grid: a
+ *                  larger value changes nothing, a smaller one drops work.
+ *   softmax_scale  multiplies <q, k>; the bias is added after scaling.
+ *   causal         nonzero = bottom-right causal mask.
+ *   window_left,
+ *   window_right   sliding window; -1 leaves that side unbounded.
+ *   rel_extent     R >= 0; 0 means no bias (rel_logits may then be NULL).
+ *   rel_logits     fp32 [num_tokens, num_heads, R].
+ *   num_splits     S in [1, RPA_MAX_SPLITS]: each work item's visible key
+ *                  range is cut into S contiguous chunks whose partial results
+ *                  are merged by the log-sum-exp combine.  rpa_choose_splits
+ *                  gives a default.  Any S gives the same result up to fp32
+ *                  rounding.
+ *   workspace      device scratch of at least rpa_workspace_bytes(S, ...)
+ *                  bytes when S > 1 (may be NULL when S == 1); holds split
+ *                  partials, consumed within this call on `stream`.
+ *   out            bf16 [num_tokens, num_heads, head_dim], written.
+ *   lse            fp32 [num_tokens, num_heads] natural-log LSE, or NULL.
+ *
+ * Device-resident metadata (block_table, cache_seqlens, cu_seqlens_q) is not
+ * checked; violating the preconditions above is undefined behaviour, except
+ * that Lk < Lq (rows with negative qa) and Lk == 0 are defined (empty rows).
+ * Supported: head_dim in {64, 128}; block_size a positive multiple of 16;
+ * num_heads a multiple of num_kv_heads.
+ */
+int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cache,
+                    const int32_t *block_table, int32_t max_pages_per_seq,
+                    const int32_t *cache_seqlens, const int32_t *cu_seqlens_q,
+                    int32_t batch, int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                    int32_t max_seqlen_q, float softmax_scale, int causal,
+                    int32_t window_left, int32_t window_right,
+                    int32_t rel_extent, const float *rel_logits,
+                    int32_t num_splits, void *workspace, size_t workspace_bytes,
+                    void *out, float *lse, void *stream);
+
+/*
+ * rpa_workspace_bytes: scratch needed by rpa_attn_varlen for num_splits
+ * partials: num_splits * num_tokens * num_heads * (head_dim + 1) * 4 bytes
+ * (fp32 partial outputs and LSEs), rounded up to 256; 0 when num_splits <= 1.
+ * Returns 0 for negative sizes.
+ */
+size_t rpa_workspace_bytes(int32_t num_splits, int32_t num_tokens, int32_t num_heads,
+                           int32_t head_dim);
+
+/*
+ * rpa_split_combine: merge split partials (the phase-2 reduction of
+ * partitioned attention, "paged_attention_v2_pytorch.py — BI-V100
+ * PagedAttention V2", dev.modelhub.org.cn, with NORMALISED partials):
+ *     M = max_s lse_s,  LSE = M + ln sum_s exp(lse_s - M),
+ *     out = sum_s exp(lse_s - LSE) * o_s;
+ * rows whose every lse_s is -inf give out = 0, lse = -inf.
+ *
+ *   partial_out  fp32 [num_splits, num_tokens, num_heads, head_dim]
+ *   partial_lse  fp32 [num_splits, num_tokens, num_heads], natural log
+ *   out          bf16 [num_tokens, num_heads, head_dim], written
+ *   lse          fp32 [num_tokens, num_heads], written, or NULL
+ * head_dim must be a positive multiple of 64 up to 256; num_splits in
+ * [1, RPA_MAX_SPLITS].
+ */
+int rpa_split_combine(const float *partial_out, const float *partial_lse, int32_t num_splits,
+                      int32_t num_tokens, int32_t num_heads, int32_t head_dim, void *out,
+                      float *lse, void *stream);
+
+/*
+ * rpa_choose_splits: default num_splits for a batch (host only, no HIP call).
+ * Same inputs as the walkthrough's inkling_fa4_num_splits (batch,
+ * max_seqlen_q, heads, kv heads, max KV length, whether a window is set),
+ * re-derived for a gfx950 with num_cus compute units (<= 0 means 256): work
+ * items are (request, q-tile, kv head); decode-shaped batches are split until
+ * about four workgroups per CU exist, keeping at least 512 keys per split;
+ * windowed (local) attention and prefill-heavy batches use 1.
+ * Returns a value in [1, RPA_MAX_SPLITS], or RPA_ERR_SHAPE for bad sizes.
+ */
+int rpa_choose_splits(int32_t batch, int32_t max_seqlen_q, int32_t num_heads,
+                      int32_t num_kv_heads, int64_t max_seqlen_k, int is_local, int32_t num_cus);
+
+/* rpa_status_string: static text for a status code (never NULL). */
+const char *rpa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RPA_H */

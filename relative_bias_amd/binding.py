@@ -1,0 +1,199 @@
+"""ctypes binding for librpa.so: argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels.  These
+wrappers check dtypes, devices and contiguity of torch tensors, allocate
+outputs and workspace with torch when the caller does not pass them, and
+forward raw device pointers plus the current HIP stream through the C ABI
+declared in include/rpa.h.  If the library is missing they raise; there is no
+fallback implementation.
+
+The keyword signature of ``rpa_attn_varlen`` mirrors the op wrapper in the
+Inkling FA4 relative-attention walkthrough ("主函数
+inkling_fa4_rel_attention"): window (-1, -1) means none, ``out=None``
+allocates, ``num_splits=None`` asks the planner.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librpa.so")
+
+RPA_OK = 0
+RPA_MAX_SPLITS = 128
+_STATUS = {0: "RPA_OK", -1: "RPA_ERR_NULL", -2: "RPA_ERR_SHAPE", -3: "RPA_ERR_UNSUPPORTED",
+           -4: "RPA_ERR_WORKSPACE", -5: "RPA_ERR_HIP"}
+
+_lib = None
+
+
+class RpaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().rpa_status_string(status).decode() if _lib is not None else ""
+        super().__init__(f"{where}: {_STATUS.get(status, status)} ({msg})")
+
+
+def lib():
+    """Load librpa.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m relative_bias_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    L.rpa_attn_varlen.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                  f32, ctypes.c_int, i32, i32, i32, vp, i32, vp, sz, vp, vp, vp]
+    L.rpa_attn_varlen.restype = ctypes.c_int
+    L.rpa_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.rpa_workspace_bytes.restype = sz
+    L.rpa_split_combine.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
+    L.rpa_split_combine.restype = ctypes.c_int
+    L.rpa_choose_splits.argtypes = [i32, i32, i32, i32, i64, ctypes.c_int, i32]
+    L.rpa_choose_splits.restype = ctypes.c_int
+    L.rpa_status_string.argtypes = [ctypes.c_int]
+    L.rpa_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype, device, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def rpa_workspace_bytes(num_splits: int, num_tokens: int, num_heads: int, head_dim: int) -> int:
+    return int(lib().rpa_workspace_bytes(num_splits, num_tokens, num_heads, head_dim))
+
+
+def rpa_choose_splits(batch: int, max_seqlen_q: int, num_heads: int, num_kv_heads: int,
+                      max_seqlen_k: int, is_local: bool = False, num_cus: int = 0) -> int:
+    s = int(lib().rpa_choose_splits(batch, max_seqlen_q, num_heads, num_kv_heads, max_seqlen_k,
+                                    int(bool(is_local)), num_cus))
+    if s < 0:
+        raise RpaError(s, "rpa_choose_splits")
+    return s
+
+
+def rpa_attn_varlen(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor, *,
+                    block_table: torch.Tensor, cache_seqlens: torch.Tensor,
+                    cu_seqlens_q: torch.Tensor, max_seqlen_q: int, softmax_scale: float,
+                    causal: bool = True, window_size: Tuple[int, int] = (-1, -1),
+                    rel_extent: int = 0, rel_logits: Optional[torch.Tensor] = None,
+                    num_splits: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Paged varlen causal attention with the additive relative bias.
+
+    Returns ``out`` (bf16 [T, H, D]), or ``(out, lse)`` when ``return_lse``
+    or an ``lse`` tensor is given.  ``num_splits=None`` uses
+    rpa_choose_splits, which needs ``max_seqlen_k`` (host int) to be given.
+    """
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    _check(q, "q", torch.bfloat16, dev, 3)
+    _check(key_cache, "key_cache", torch.bfloat16, dev, 4)
+    _check(value_cache, "value_cache", torch.bfloat16, dev, 4)
+    if key_cache.shape != value_cache.shape:
+        raise ValueError("key_cache and value_cache shapes differ")
+    _check(block_table, "block_table", torch.int32, dev, 2)
+    _check(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
+    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, 1)
+    T, H, D = q.shape
+    NB, BS, Hkv, Dk = key_cache.shape
+    if Dk != D:
+        raise ValueError("head_dim of q and the caches differ")
+    B = cache_seqlens.shape[0]
+    if cu_seqlens_q.shape[0] != B + 1 or block_table.shape[0] != B:
+        raise ValueError("batch sizes of cu_seqlens_q / block_table / cache_seqlens disagree")
+    R = int(rel_extent)
+    if R > 0:
+        if rel_logits is None:
+            raise ValueError("rel_extent > 0 needs rel_logits")
+        rel_logits = rel_logits.contiguous()  # the walkthrough's wrapper does the same
+        _check(rel_logits, "rel_logits", torch.float32, dev, 3)
+        if tuple(rel_logits.shape) != (T, H, R):
+            raise ValueError(f"rel_logits must be {(T, H, R)}, got {tuple(rel_logits.shape)}")
+    if num_splits is None:
+        if max_seqlen_k is None:
+            raise ValueError("num_splits=None needs max_seqlen_k for the planner")
+        is_local = tuple(window_size) != (-1, -1)
+        num_splits = rpa_choose_splits(B, max_seqlen_q, H, Hkv, max_seqlen_k, is_local)
+    S = int(num_splits)
+    if out is None:
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, dev, 3)
+    want_lse = return_lse or lse is not None
+    if want_lse and lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, dev, 2)
+    ws_bytes = rpa_workspace_bytes(S, T, H, D) if S > 1 else 0
+    if ws_bytes and workspace is None:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    st = lib().rpa_attn_varlen(
+        _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(block_table), block_table.shape[1],
+        _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB, BS, int(max_seqlen_q),
+        float(softmax_scale), int(bool(causal)), int(window_size[0]), int(window_size[1]), R,
+        _ptr(rel_logits) if R > 0 else None, S, _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _ptr(out), _ptr(lse), _stream(dev))
+    if st != RPA_OK:
+        raise RpaError(st, "rpa_attn_varlen")
+    return (out, lse) if want_lse else out
+
+
+def rpa_split_combine(partial_out: torch.Tensor, partial_lse: torch.Tensor,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Merge normalised split partials [S, T, H, D] / [S, T, H] -> (out, lse)."""
+    dev = partial_out.device
+    _check(partial_out, "partial_out", torch.float32, dev, 4)
+    _check(partial_lse, "partial_lse", torch.float32, dev, 3)
+    S, T, H, D = partial_out.shape
+    if tuple(partial_lse.shape) != (S, T, H):
+        raise ValueError("partial_lse shape does not match partial_out")
+    if out is None:
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _check(out, "out", torch.bfloat16, dev, 3)
+    _check(lse, "lse", torch.float32, dev, 2)
+    st = lib().rpa_split_combine(_ptr(partial_out), _ptr(partial_lse), S, T, H, D, _ptr(out),
+                                 _ptr(lse), _stream(dev))
+    if st != RPA_OK:
+        raise RpaError(st, "rpa_split_combine")
+    return out, lse
+
+
+def attn_workload(w, *, num_splits: Optional[int] = None, return_lse: bool = True, out=None, lse=None,
+                  workspace=None):
+    """Run rpa_attn_varlen on a relative_bias_amd.workloads.Workload (on the GPU)."""
+    S = num_splits if num_splits is not None else w.num_splits
+    return rpa_attn_varlen(
+        w.q, w.key_cache, w.value_cache, block_table=w.block_table, cache_seqlens=w.cache_seqlens,
+        cu_seqlens_q=w.cu_seqlens_q, max_seqlen_q=w.max_seqlen_q, softmax_scale=w.softmax_scale,
+        causal=w.causal, window_size=w.window_size, rel_extent=w.rel_extent, rel_logits=w.rel_logits,
+        num_splits=S, max_seqlen_k=max(w.k_lens + [0]), return_lse=return_lse, out=out, lse=lse,
+        workspace=workspace)

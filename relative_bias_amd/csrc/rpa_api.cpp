@@ -1,0 +1,177 @@
+// C-ABI host layer of librpa.so: argument validation, the split planner and
+// kernel launches.  Every check here runs before any HIP call, so error
+// paths are testable on a machine without a GPU.
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "rpa.h"
+#include "rpa_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Byte offset of the partial-LSE array inside the workspace.
+size_t part_lse_offset(int64_t S, int64_t T, int64_t H, int64_t D) {
+  return round_up((size_t)S * (size_t)T * (size_t)H * (size_t)D * sizeof(float), kAlign);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rpa_status_string(int status) {
+  switch (status) {
+    case RPA_OK: return "ok";
+    case RPA_ERR_NULL: return "a required pointer is NULL";
+    case RPA_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case RPA_ERR_UNSUPPORTED: return "unsupported head_dim or block_size";
+    case RPA_ERR_WORKSPACE: return "workspace missing or too small for num_splits";
+    case RPA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t rpa_workspace_bytes(int32_t num_splits, int32_t num_tokens, int32_t num_heads, int32_t head_dim) {
+  if (num_splits <= 1 || num_tokens < 0 || num_heads < 0 || head_dim < 0) return 0;
+  const size_t n = (size_t)num_splits * (size_t)num_tokens * (size_t)num_heads;
+  return round_up(part_lse_offset(num_splits, num_tokens, num_heads, head_dim) + n * sizeof(float), kAlign);
+}
+
+// Planner: work items are (request, q-tile, kv head); the split count is
+// raised until the grid offers about four workgroups per CU (decode) or two
+// (prefill-shaped batches), never below 512 keys per split and never above
+// RPA_MAX_SPLITS.  A window bounds the keys a row sees, so local attention
+// is not split, as in the walkthrough's inkling_fa4_num_splits.
+int rpa_choose_splits(int32_t batch, int32_t max_seqlen_q, int32_t num_heads, int32_t num_kv_heads,
+                      int64_t max_seqlen_k, int is_local, int32_t num_cus) {
+  if (batch < 0 || max_seqlen_q < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_seqlen_k < 0 ||
+      num_heads % num_kv_heads != 0)
+    return RPA_ERR_SHAPE;
+  if (num_cus <= 0) num_cus = 256;
+  if (batch == 0 || max_seqlen_q == 0 || max_seqlen_k == 0 || is_local) return 1;
+  const int64_t G = num_heads / num_kv_heads;
+  const int64_t items = rpa::items_for_request(max_seqlen_q, G);
+  const bool decode = G <= rpa::kDecCols && (int64_t)max_seqlen_q * G <= rpa::kDecCols;
+  const int64_t base = (int64_t)batch * num_kv_heads * items;
+  const int64_t target = (decode ? 4 : 2) * (int64_t)num_cus;
+  int64_t s = (target + base - 1) / base;
+  const int64_t by_len = max_seqlen_k / 512;
+  if (s > by_len) s = by_len;
+  if (s > RPA_MAX_SPLITS) s = RPA_MAX_SPLITS;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+int rpa_split_combine(const float *partial_out, const float *partial_lse, int32_t num_splits,
+                      int32_t num_tokens, int32_t num_heads, int32_t head_dim, void *out, float *lse,
+                      void *stream) {
+  if (num_splits < 1 || num_splits > RPA_MAX_SPLITS || num_tokens < 0 || num_heads <= 0 ||
+      head_dim <= 0)
+    return RPA_ERR_SHAPE;
+  if (head_dim % 64 != 0 || head_dim > 256) return RPA_ERR_UNSUPPORTED;
+  if ((int64_t)num_tokens * num_heads > INT32_MAX) return RPA_ERR_SHAPE;
+  if (num_tokens == 0) return RPA_OK;
+  if (!partial_out || !partial_lse || !out) return RPA_ERR_NULL;
+  rpa::CombineParams p;
+  p.part_out = partial_out;
+  p.part_lse = partial_lse;
+  p.out = static_cast<uint16_t *>(out);
+  p.lse = lse;
+  p.S = num_splits;
+  p.rows = num_tokens * num_heads;
+  p.D = head_dim;
+  if (rpa::launch_combine(p, static_cast<hipStream_t>(stream)) != hipSuccess) return RPA_ERR_HIP;
+  return RPA_OK;
+}
+
+int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cache,
+                    const int32_t *block_table, int32_t max_pages_per_seq,
+                    const int32_t *cache_seqlens, const int32_t *cu_seqlens_q, int32_t batch,
+                    int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t num_blocks, int32_t block_size, int32_t max_seqlen_q, float softmax_scale,
+                    int causal, int32_t window_left, int32_t window_right, int32_t rel_extent,
+                    const float *rel_logits, int32_t num_splits, void *workspace,
+                    size_t workspace_bytes, void *out, float *lse, void *stream) {
+  // Sizes.
+  if (batch < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_blocks < 0 || block_size <= 0 || max_pages_per_seq < 0 || max_seqlen_q < 0 ||
+      rel_extent < 0 || window_left < -1 || window_right < -1)
+    return RPA_ERR_SHAPE;
+  if (num_heads % num_kv_heads != 0) return RPA_ERR_SHAPE;
+  if (num_splits < 1 || num_splits > RPA_MAX_SPLITS) return RPA_ERR_SHAPE;
+  if (!std::isfinite(softmax_scale)) return RPA_ERR_SHAPE;
+  if (batch == 0 && num_tokens > 0) return RPA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return RPA_ERR_UNSUPPORTED;
+  if (block_size % 16 != 0) return RPA_ERR_UNSUPPORTED;
+  if ((int64_t)num_tokens * num_heads * head_dim > ((int64_t)1 << 40)) return RPA_ERR_SHAPE;
+  if (num_tokens == 0) return RPA_OK;
+  // Pointers.
+  if (!q || !key_cache || !value_cache || !block_table || !cache_seqlens || !cu_seqlens_q || !out)
+    return RPA_ERR_NULL;
+  if (rel_extent > 0 && !rel_logits) return RPA_ERR_NULL;
+  // Workspace for split partials.
+  if (num_splits > 1) {
+    if (!workspace) return RPA_ERR_WORKSPACE;
+    if (workspace_bytes < rpa_workspace_bytes(num_splits, num_tokens, num_heads, head_dim))
+      return RPA_ERR_WORKSPACE;
+  }
+  // Grid: an upper bound on the work items.  Each request gives at most
+  // ceil(Lq*G/128) + 1 items and at most items_for_request(max_seqlen_q).
+  const int64_t G = num_heads / num_kv_heads;
+  const int64_t ub_tokens = (int64_t)batch + ((int64_t)num_tokens * G + rpa::kTileRows - 1) / rpa::kTileRows;
+  const int64_t ub_maxq = (int64_t)batch * rpa::items_for_request(max_seqlen_q, G);
+  const int64_t n_items_ub = ub_tokens < ub_maxq ? ub_tokens : ub_maxq;
+  if (n_items_ub * num_kv_heads * num_splits > INT32_MAX) return RPA_ERR_SHAPE;
+
+  rpa::AttnParams p;
+  p.q = static_cast<const uint16_t *>(q);
+  p.k = static_cast<const uint16_t *>(key_cache);
+  p.v = static_cast<const uint16_t *>(value_cache);
+  p.block_table = block_table;
+  p.cache_seqlens = cache_seqlens;
+  p.cu_seqlens_q = cu_seqlens_q;
+  p.rel_logits = rel_extent > 0 ? rel_logits : nullptr;
+  p.out = static_cast<uint16_t *>(out);
+  p.lse = lse;
+  p.part_out = nullptr;
+  p.part_lse = nullptr;
+  if (num_splits > 1) {
+    p.part_out = static_cast<float *>(workspace);
+    p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                           part_lse_offset(num_splits, num_tokens, num_heads, head_dim));
+  }
+  p.batch = batch;
+  p.num_tokens = num_tokens;
+  p.H = num_heads;
+  p.Hkv = num_kv_heads;
+  p.G = (int32_t)G;
+  p.BS = block_size;
+  p.R = rel_extent;
+  p.S = num_splits;
+  p.P = max_pages_per_seq;
+  p.left = window_left;
+  p.right = window_right;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (rpa::launch_attention(p, head_dim, n_items_ub, st) != hipSuccess) return RPA_ERR_HIP;
+  if (num_splits > 1) {
+    rpa::CombineParams c;
+    c.part_out = p.part_out;
+    c.part_lse = p.part_lse;
+    c.out = p.out;
+    c.lse = lse;
+    c.S = num_splits;
+    c.rows = num_tokens * num_heads;
+    c.D = head_dim;
+    if (rpa::launch_combine(c, st) != hipSuccess) return RPA_ERR_HIP;
+  }
+  return RPA_OK;
+}
+
+}  // extern "C"

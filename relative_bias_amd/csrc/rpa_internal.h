@@ -1,0 +1,54 @@
+// Internal interface between the C-ABI host layer (rpa_api.cpp) and the HIP
+// kernels (rpa_kernels.hip).  Not installed; include/rpa.h is the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rpa {
+
+// Work decomposition shared by host and device.
+constexpr int kThreads = 256;      // 4 wave64 per workgroup
+constexpr int kTileRows = 128;     // prefill q-tile: (token, head) rows of one kv head
+constexpr int kTileKeys = 64;      // prefill KV tile
+constexpr int kDecCols = 16;       // decode item: up to 16 (token, head) columns
+constexpr int kDecWaveKeys = 32;   // keys per wave per decode iteration
+constexpr int kDecStep = 4 * kDecWaveKeys;  // keys per workgroup per decode iteration
+
+struct AttnParams {
+  const uint16_t *q;            // bf16 [T, H, D]
+  const uint16_t *k;            // bf16 [NB, BS, Hkv, D]
+  const uint16_t *v;            // bf16 [NB, BS, Hkv, D]
+  const int32_t *block_table;   // [B, P]
+  const int32_t *cache_seqlens; // [B]
+  const int32_t *cu_seqlens_q;  // [B+1]
+  const float *rel_logits;      // [T, H, R] or null
+  uint16_t *out;                // bf16 [T, H, D]
+  float *lse;                   // [T, H] or null
+  float *part_out;              // [S, T, H, D] when S > 1
+  float *part_lse;              // [S, T, H]   when S > 1
+  int32_t batch, num_tokens, H, Hkv, G, BS, R, S, P;
+  int32_t left, right, causal;
+  float scale_log2;             // softmax_scale * log2(e)
+};
+
+struct CombineParams {
+  const float *part_out;        // [S, T, H, D]
+  const float *part_lse;        // [S, T, H], natural log
+  uint16_t *out;                // bf16 [T, H, D]
+  float *lse;                   // [T, H] or null
+  int32_t S, rows, D;           // rows = T * H
+};
+
+// Number of work items a request with lq query tokens contributes.
+__host__ __device__ inline int64_t items_for_request(int64_t lq, int64_t G) {
+  if (lq <= 0) return 0;
+  if (G <= kDecCols && lq * G <= kDecCols) return 1;  // decode item
+  return (lq * G + kTileRows - 1) / kTileRows;        // prefill q-tiles
+}
+
+hipError_t launch_attention(const AttnParams &p, int head_dim, int64_t n_items_ub,
+                            hipStream_t stream);
+hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
+
+}  // namespace rpa

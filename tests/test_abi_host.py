@@ -1,0 +1,141 @@
+"""Host-side checks of librpa.so that need no GPU: the library loads, exports
+every entry point include/rpa.h declares, and rejects bad arguments before
+any HIP call.  The split planner is checked for its stated properties only
+(its exact choices are our own tuning, not a formula the pages fix)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from relative_bias_amd import binding as bnd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rpa.h")
+
+OK, NULL, SHAPE, UNSUP, WS = 0, -1, -2, -3, -4
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bnd.LIB_PATH):
+        from relative_bias_amd import build
+        build.build()
+    return bnd.lib()
+
+
+def _declared():
+    with open(HEADER) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"\b(rpa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("rpa_attn_varlen", "rpa_split_combine", "rpa_choose_splits", "rpa_workspace_bytes",
+              "rpa_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for n in _declared():
+        assert hasattr(L, n), f"{n} declared in rpa.h but not exported"
+
+
+def test_status_strings(L):
+    for s in (0, -1, -2, -3, -4, -5, 7):
+        assert L.rpa_status_string(s)
+
+
+def test_workspace_bytes(L):
+    assert bnd.rpa_workspace_bytes(1, 100, 8, 128) == 0
+    assert bnd.rpa_workspace_bytes(0, 100, 8, 128) == 0
+    assert bnd.rpa_workspace_bytes(4, -1, 8, 128) == 0
+    for S, T, H, D in [(2, 1, 1, 64), (4, 32, 32, 128), (128, 1, 64, 128), (3, 17, 6, 64)]:
+        n = bnd.rpa_workspace_bytes(S, T, H, D)
+        assert n >= S * T * H * (D + 1) * 4
+        assert n % 256 == 0
+        assert n < S * T * H * (D + 1) * 4 + 512
+
+
+def _attn(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, P=4, seqlens=FAKE, cu=FAKE, B=2, T=3, H=4, Hkv=2, D=64,
+             NB=8, BS=16, maxq=2, scale=0.125, causal=1, left=-1, right=-1, R=0, rel=None, S=1,
+             ws=None, wsb=0, out=FAKE, lse=None)
+    a.update(kw)
+    return L.rpa_attn_varlen(a["q"], a["k"], a["v"], a["bt"], a["P"], a["seqlens"], a["cu"], a["B"],
+                             a["T"], a["H"], a["Hkv"], a["D"], a["NB"], a["BS"], a["maxq"], a["scale"],
+                             a["causal"], a["left"], a["right"], a["R"], a["rel"], a["S"], a["ws"],
+                             a["wsb"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "bt", "seqlens", "cu", "out"])
+def test_null_pointers(L, field):
+    assert _attn(L, **{field: None}) == NULL
+
+
+def test_rel_logits_required_when_extent_positive(L):
+    assert _attn(L, R=8, rel=None) == NULL
+
+
+@pytest.mark.parametrize("kw", [dict(H=6, Hkv=4), dict(S=0), dict(S=129), dict(B=-1), dict(T=-2),
+                                dict(H=0), dict(Hkv=0), dict(BS=0), dict(left=-2), dict(right=-5),
+                                dict(R=-1), dict(maxq=-1), dict(P=-1), dict(B=0, T=3),
+                                dict(scale=float("nan")), dict(scale=float("inf"))])
+def test_bad_shapes(L, kw):
+    assert _attn(L, **kw) == SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(D=96), dict(D=256), dict(D=32), dict(BS=8), dict(BS=24)])
+def test_unsupported(L, kw):
+    assert _attn(L, **kw) == UNSUP
+
+
+def test_workspace_checks(L):
+    assert _attn(L, S=4, ws=None) == WS
+    need = bnd.rpa_workspace_bytes(4, 3, 4, 64)
+    assert _attn(L, S=4, ws=FAKE, wsb=need - 1) == WS
+
+
+def test_empty_batch_is_a_no_op(L):
+    # Nothing to compute: returns OK before touching any pointer or HIP.
+    assert _attn(L, T=0, B=0, q=None, out=None) == OK
+    assert _attn(L, T=0, B=3) == OK
+
+
+def test_combine_argument_errors(L):
+    c = L.rpa_split_combine
+    assert c(FAKE, FAKE, 0, 4, 2, 64, FAKE, None, None) == SHAPE
+    assert c(FAKE, FAKE, 129, 4, 2, 64, FAKE, None, None) == SHAPE
+    assert c(FAKE, FAKE, 2, 4, 2, 96, FAKE, None, None) == UNSUP
+    assert c(None, FAKE, 2, 4, 2, 64, FAKE, None, None) == NULL
+    assert c(FAKE, FAKE, 2, 4, 2, 64, None, None, None) == NULL
+    assert c(None, None, 2, 0, 2, 64, None, None, None) == OK
+
+
+# ------------------------------------------------------------------ planner
+
+def test_planner_rejects_bad_sizes(L):
+    assert L.rpa_choose_splits(1, 1, 6, 4, 100, 0, 256) == SHAPE
+    assert L.rpa_choose_splits(-1, 1, 8, 8, 100, 0, 256) == SHAPE
+    assert L.rpa_choose_splits(1, 1, 8, 0, 100, 0, 256) == SHAPE
+
+
+@pytest.mark.parametrize("B,maxq,H,Hkv,maxk", [(32, 1, 32, 8, 8192), (1, 1, 64, 8, 1 << 20),
+                                               (8, 2048, 32, 8, 6144), (68, 1024, 64, 8, 131072),
+                                               (3, 16, 4, 2, 312), (1, 1, 8, 1, 100), (256, 1, 32, 8, 4096),
+                                               (1, 4, 64, 8, 1 << 20)])
+def test_planner_properties(L, B, maxq, H, Hkv, maxk):
+    s = bnd.rpa_choose_splits(B, maxq, H, Hkv, maxk)
+    assert 1 <= s <= bnd.RPA_MAX_SPLITS
+    if s > 1:
+        assert maxk // s >= 512          # at least 512 keys per split
+    assert bnd.rpa_choose_splits(B, maxq, H, Hkv, maxk, is_local=True) == 1
+    # more requests never ask for more splits
+    assert bnd.rpa_choose_splits(2 * B, maxq, H, Hkv, maxk) <= s
+
+
+def test_planner_long_context_decode_uses_many_splits(L):
+    assert bnd.rpa_choose_splits(1, 1, 64, 8, 1 << 20) >= 16
+    assert bnd.rpa_choose_splits(8, 2048, 32, 8, 6144) == 1

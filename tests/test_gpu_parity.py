@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Tolerances (bf16 inputs, bf16 output, fp32 accumulation):
+    out  max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3
+    lse  max |gpu - oracle| <= 1e-3, and -inf exactly where the oracle has it.
+Small cases are compared element by element on every output; the full-size
+workloads, in the split configuration the benchmark times, are compared on
+sampled tokens / heads that the oracle computes one by one.
+"""
+import math
+
+import pytest
+import torch
+
+from oracle import attention as orc
+from relative_bias_amd import binding as bnd
+from relative_bias_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+OUT_MAX, OUT_MEAN, LSE_MAX = 2e-2, 2e-3, 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "these tests need a GPU"
+    bnd.lib()
+
+
+def _oracle(w, **kw):
+    return orc.attention(w.q, w.key_cache, w.value_cache, w.block_table, w.cache_seqlens,
+                         w.cu_seqlens_q, w.softmax_scale, w.causal, w.window_size, w.rel_extent,
+                         w.rel_logits, **kw)
+
+
+def _gpu_run(wg, S, **kw):
+    out, lse = bnd.attn_workload(wg, num_splits=S, return_lse=True, **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu().double(), lse.cpu().double()
+
+
+def _compare(out, lse, ref_out, ref_lse, tokens=None, heads=None, tag=""):
+    if tokens is not None:
+        idx = torch.as_tensor(sorted(set(tokens)), dtype=torch.long)
+        out, lse, ref_out, ref_lse = out[idx], lse[idx], ref_out[idx], ref_lse[idx]
+    if heads is not None:
+        hidx = torch.as_tensor(sorted(set(heads)), dtype=torch.long)
+        out, lse, ref_out, ref_lse = out[:, hidx], lse[:, hidx], ref_out[:, hidx], ref_lse[:, hidx]
+    assert not torch.isnan(ref_out).any(), "oracle rows missing from the comparison set"
+    assert not torch.isnan(out).any(), f"{tag}: NaN in GPU output"
+    assert not torch.isnan(lse).any(), f"{tag}: NaN in GPU lse"
+    err = (out - ref_out).abs()
+    assert err.max().item() <= OUT_MAX, f"{tag}: out max err {err.max().item():.3e}"
+    assert err.mean().item() <= OUT_MEAN, f"{tag}: out mean err {err.mean().item():.3e}"
+    ref_inf = torch.isinf(ref_lse)
+    assert torch.equal(torch.isinf(lse), ref_inf), f"{tag}: lse -inf pattern differs"
+    if ref_inf.any():
+        assert (lse[ref_inf] == -math.inf).all()
+        assert (out[ref_inf] == 0).all(), f"{tag}: empty rows must give 0"
+    fin = ~ref_inf
+    if fin.any():
+        le = (lse[fin] - ref_lse[fin]).abs().max().item()
+        assert le <= LSE_MAX, f"{tag}: lse max err {le:.3e}"
+
+
+# ------------------------------------------------------------- small cases
+
+@pytest.mark.parametrize("S", [1, 4])
+def test_tiny_mixed_batch(S):
+    w = wl.tiny(num_splits=S)
+    ref = _oracle(w)
+    out, lse = _gpu_run(w.to("cuda"), S)
+    _compare(out, lse, *ref, tag=f"tiny S={S}")
+
+
+CASES = {
+    # name: (q_lens, k_lens, H, Hkv, D, BS, R, causal, window)
+    "decode_gqa4_d128": ([1, 1, 1, 1], [1, 17, 300, 1024], 8, 2, 128, 16, 64, True, (-1, -1)),
+    "decode_gqa8_d128": ([1, 1, 1], [33, 129, 700], 16, 2, 128, 16, 40, True, (-1, -1)),
+    "decode_gqa16": ([1, 1], [250, 77], 16, 1, 64, 16, 8, True, (-1, -1)),
+    "decode_two_tokens": ([2, 2, 3], [40, 259, 3], 8, 2, 128, 16, 16, True, (-1, -1)),
+    "prefill_ragged_d128": ([200, 37, 129], [300, 37, 700], 8, 2, 128, 16, 32, True, (-1, -1)),
+    "prefill_ragged_d64": ([150, 65], [150, 400], 6, 2, 64, 16, 5, True, (-1, -1)),
+    "prefill_mha": ([70], [130], 4, 4, 128, 32, 12, True, (-1, -1)),
+    "prefill_gqa32": ([3, 1], [90, 50], 32, 1, 64, 16, 9, True, (-1, -1)),
+    "window_left": ([100, 1, 1], [500, 900, 30], 8, 2, 128, 16, 64, True, (63, 0)),
+    "window_both_noncausal": ([40, 1], [200, 120], 4, 2, 64, 16, 10, False, (20, 7)),
+    "noncausal_full": ([33, 5], [90, 70], 4, 1, 128, 48, 0, False, (-1, -1)),
+    "no_bias": ([50, 1], [200, 333], 8, 2, 128, 16, 0, True, (-1, -1)),
+    "bias_wider_than_kv": ([20, 1], [25, 40], 4, 2, 64, 16, 512, True, (-1, -1)),
+    "empty_rows": ([5, 0, 3, 1], [2, 10, 0, 0], 4, 2, 64, 16, 4, True, (-1, -1)),
+    "block_size_64": ([9, 1], [300, 170], 8, 2, 128, 64, 32, True, (-1, -1)),
+}
+
+
+@pytest.mark.parametrize("S", [1, 3])
+@pytest.mark.parametrize("name", list(CASES))
+def test_small_cases(name, S):
+    ql, kl, H, Hkv, D, BS, R, causal, win = CASES[name]
+    w = wl.build(ql, kl, num_heads=H, num_kv_heads=Hkv, head_dim=D, block_size=BS, rel_extent=R,
+                 causal=causal, window_size=win, seed=sum(map(ord, name)), extra_pages=3, poison=True)
+    ref = _oracle(w)
+    out, lse = _gpu_run(w.to("cuda"), S)
+    _compare(out, lse, *ref, tag=f"{name} S={S}")
+
+
+def test_many_splits_with_short_ranges():
+    """More splits than key tiles: most splits are empty and give (0, -inf)
+    partials that the combine must ignore."""
+    w = wl.build([1, 4, 1], [20, 90, 600], num_heads=8, num_kv_heads=2, head_dim=128, rel_extent=16,
+                 seed=5)
+    ref = _oracle(w)
+    out, lse = _gpu_run(w.to("cuda"), 128)
+    _compare(out, lse, *ref, tag="S=128")
+
+
+def test_split_combine_entry_point():
+    g = torch.Generator().manual_seed(3)
+    S, T, H, D = 5, 7, 3, 128
+    po = torch.randn((S, T, H, D), generator=g, dtype=torch.float32)
+    pl = 3 * torch.randn((S, T, H), generator=g, dtype=torch.float32)
+    pl[:, 0, 0] = -math.inf       # every split empty
+    pl[1:, 1, 1] = -math.inf      # one split only
+    pl[2, 2, 2] = -math.inf
+    po[pl == -math.inf] = 0
+    ref_o, ref_l = orc.combine(po.double(), pl.double())
+    out, lse = bnd.rpa_split_combine(po.cuda(), pl.cuda())
+    torch.cuda.synchronize()
+    _compare(out.float().cpu().double(), lse.cpu().double(), ref_o, ref_l, tag="combine")
+
+
+# --------------------------------------------------------------- invariants
+
+def test_bitwise_repeatable_and_page_permutation_exact():
+    w = wl.build([1, 70, 1], [500, 300, 2000], num_heads=8, num_kv_heads=2, head_dim=128,
+                 rel_extent=64, seed=21, extra_pages=4)
+    wg = w.to("cuda")
+    a = bnd.attn_workload(wg, num_splits=4)
+    b = bnd.attn_workload(wg, num_splits=4)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    # Physically permute the pages and remap the table: same bits.
+    nb = w.key_cache.shape[0]
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(9))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(nb)
+    w2 = w.to("cpu")
+    w2.key_cache = w.key_cache[perm].contiguous()
+    w2.value_cache = w.value_cache[perm].contiguous()
+    bt = w.block_table.clone()
+    m = bt >= 0
+    bt[m] = inv[bt[m].long()].int()
+    w2.block_table = bt
+    c = bnd.attn_workload(w2.to("cuda"), num_splits=4)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
+
+
+def test_nan_poison_changes_no_bits():
+    kw = dict(num_heads=8, num_kv_heads=2, head_dim=128, rel_extent=32, seed=22, extra_pages=3)
+    a = wl.build([1, 40], [333, 97], poison=False, **kw)
+    b = wl.build([1, 40], [333, 97], poison=True, **kw)
+    for S in (1, 2):
+        oa = bnd.attn_workload(a.to("cuda"), num_splits=S)
+        ob = bnd.attn_workload(b.to("cuda"), num_splits=S)
+        torch.cuda.synchronize()
+        assert torch.equal(oa[0], ob[0]) and torch.equal(oa[1], ob[1])
+
+
+def test_split_count_invariance():
+    w = wl.build([1, 1, 30], [3000, 1500, 2048], num_heads=16, num_kv_heads=2, head_dim=128,
+                 rel_extent=128, seed=23).to("cuda")
+    base = _gpu_run(w, 1)
+    for S in (2, 7, 16, 64):
+        o, l = _gpu_run(w, S)
+        assert (o - base[0]).abs().max().item() <= 1e-2
+        fin = torch.isfinite(base[1])
+        assert (l[fin] - base[1][fin]).abs().max().item() <= 1e-4
+
+
+def test_zero_bias_equals_no_bias_on_gpu():
+    w = wl.build([1, 50], [700, 300], num_heads=8, num_kv_heads=2, head_dim=128, rel_extent=64, seed=24)
+    wg = w.to("cuda")
+    a = bnd.attn_workload(wg, num_splits=2)
+    wg.rel_logits.zero_()
+    b = bnd.attn_workload(wg, num_splits=2)
+    wg.rel_extent, wg.rel_logits = 0, None
+    c = bnd.attn_workload(wg, num_splits=2)
+    torch.cuda.synchronize()
+    assert torch.equal(b[0], c[0]) and torch.equal(b[1], c[1])
+    assert not torch.equal(a[0], b[0])
+
+
+# ------------------------------------------------- full-size workloads
+
+def _sample_tokens(w, per_req=4, seed=0):
+    g = torch.Generator().manual_seed(seed)
+    cu = w.cu_seqlens_q.tolist()
+    toks = []
+    for b in range(w.batch):
+        a, e = cu[b], cu[b + 1]
+        if e <= a:
+            continue
+        toks += [a, e - 1]
+        toks += [int(x) for x in torch.randint(a, e, (per_req,), generator=g)]
+    return sorted(set(toks))
+
+
+@pytest.mark.timeout(600)
+def test_batched_decode_full():
+    w = wl.batched_decode()
+    S = bnd.rpa_choose_splits(w.batch, 1, w.num_heads, w.num_kv_heads, max(w.k_lens))
+    ref = _oracle(w)
+    out, lse = _gpu_run(w.to("cuda"), S)
+    _compare(out, lse, *ref, tag=f"batched_decode S={S}")
+
+
+@pytest.mark.timeout(600)
+def test_chunked_prefill_sampled():
+    w = wl.chunked_prefill()
+    toks = _sample_tokens(w, per_req=3)
+    ref = _oracle(w, tokens=toks)
+    out, lse = _gpu_run(w.to("cuda"), 1)
+    _compare(out, lse, *ref, tokens=toks, tag="chunked_prefill")
+
+
+@pytest.mark.timeout(600)
+def test_continuous_batch_sampled():
+    w = wl.continuous_batch()
+    cu = w.cu_seqlens_q.tolist()
+    toks = _sample_tokens(w, per_req=2)
+    toks = [t for t in toks if t < cu[4]] + list(range(cu[4], cu[-1], 4))
+    ref = _oracle(w, tokens=toks)
+    out, lse = _gpu_run(w.to("cuda"), 1)
+    _compare(out, lse, *ref, tokens=toks, tag="continuous_batch")
+
+
+@pytest.mark.timeout(600)
+def test_long_decode_sampled_heads():
+    """1,048,576-token decode, generated on the GPU; the oracle checks two kv
+    groups (16 q heads) for the split counts the benchmark uses."""
+    wg = wl.long_decode(device="cuda")
+    heads = list(range(0, 8)) + list(range(56, 64))
+    wc = wg.to("cpu")
+    ref = _oracle(wc, heads=heads)
+    del wc
+    for S in (bnd.rpa_choose_splits(1, 1, 64, 8, 1 << 20), 16):
+        out, lse = _gpu_run(wg, S)
+        _compare(out, lse, *ref, heads=heads, tag=f"long_decode S={S}")
