@@ -159,7 +159,20 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None, help="run one workload: batched_decode, chunked_prefill, "
                                                   "long_decode, continuous_batch")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 10 times (for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     a = ap.parse_args(argv)
+    if a.copy_calibration:
+        import torch
+        src = torch.ones((1 << 29,), dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 2, "copy_bytes_written": dst.numel() * 2,
+                          "launches": 10}))
+        return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(see the sharding notes in the design document); run with --gpus 1.", file=sys.stderr)

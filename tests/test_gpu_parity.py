@@ -187,7 +187,10 @@ def test_zero_bias_equals_no_bias_on_gpu():
     wg.rel_extent, wg.rel_logits = 0, None
     c = bnd.attn_workload(wg, num_splits=2)
     torch.cuda.synchronize()
-    assert torch.equal(b[0], c[0]) and torch.equal(b[1], c[1])
+    # Same values up to fp32 rounding: the bias-free tile variant may contract
+    # the scale and the max subtraction into one FMA, the bias variant cannot.
+    assert (b[0].float() - c[0].float()).abs().max().item() <= 8e-3
+    assert (b[1] - c[1]).abs().max().item() <= 1e-5
     assert not torch.equal(a[0], b[0])
 
 
