@@ -159,6 +159,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None, help="run one workload: batched_decode, chunked_prefill, "
                                                   "long_decode, continuous_batch")
+    ap.add_argument("--splits", type=int, default=None,
+                    help="override the planner's num_splits for the headline decode batch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -195,6 +197,8 @@ def main(argv=None):
     if run_main:
         w = wl.batched_decode(device="cpu").to(dev)
         S = bnd.rpa_choose_splits(w.batch, 1, w.num_heads, w.num_kv_heads, max(w.k_lens))
+        if a.splits:
+            S = a.splits
         r = Runner(w, S, pools=3)
         ms, ms_c, wk = measure(r, a.steps, a.warmup)
         results["batched_decode"] = (w, S, ms, ms_c, wk)

@@ -125,6 +125,7 @@ int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cach
   const int64_t ub_tokens = (int64_t)batch + ((int64_t)num_tokens * G + rpa::kTileRows - 1) / rpa::kTileRows;
   const int64_t ub_maxq = (int64_t)batch * rpa::items_for_request(max_seqlen_q, G);
   const int64_t n_items_ub = ub_tokens < ub_maxq ? ub_tokens : ub_maxq;
+  const bool decode_only = G <= rpa::kDecCols && (int64_t)max_seqlen_q * G <= rpa::kDecCols;
   if (n_items_ub * num_kv_heads * num_splits > INT32_MAX) return RPA_ERR_SHAPE;
 
   rpa::AttnParams p;
@@ -159,7 +160,7 @@ int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cach
   p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (rpa::launch_attention(p, head_dim, n_items_ub, st) != hipSuccess) return RPA_ERR_HIP;
+  if (rpa::launch_attention(p, head_dim, n_items_ub, decode_only, st) != hipSuccess) return RPA_ERR_HIP;
   if (num_splits > 1) {
     rpa::CombineParams c;
     c.part_out = p.part_out;

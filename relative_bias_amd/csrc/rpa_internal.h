@@ -47,7 +47,9 @@ __host__ __device__ inline int64_t items_for_request(int64_t lq, int64_t G) {
   return (lq * G + kTileRows - 1) / kTileRows;        // prefill q-tiles
 }
 
-hipError_t launch_attention(const AttnParams &p, int head_dim, int64_t n_items_ub,
+// decode_only: every request has Lq * G <= kDecCols (the prefill path is
+// then left out of the launched kernel).
+hipError_t launch_attention(const AttnParams &p, int head_dim, int64_t n_items_ub, bool decode_only,
                             hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
 

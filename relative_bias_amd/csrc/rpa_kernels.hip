@@ -10,21 +10,28 @@
 // ("paged_attention_v2_pytorch.py — BI-V100 PagedAttention V2", phase 2).
 //
 // One launch serves a whole mixed batch.  Workgroup id = (item, kv head,
-// split); each workgroup finds its request by scanning cu_seqlens_q on the
-// device, so no host-side metadata and no device->host copy is needed.
+// split); each workgroup finds its item by scanning cu_seqlens_q on the
+// device (no host metadata, no device->host copy).  Prefill q-tiles are
+// numbered first, heaviest tile of each request first, then decode items.
 //   * prefill item: 128 (token, q-head) rows of one kv head.  Four waves,
 //     32 rows each.  S^T = K·Q^T and O^T = V^T·P^T on 32x32x16 bf16 MFMA so
 //     that each lane owns one query row: softmax statistics stay lane-local
-//     except one exchange with the partner lane 32 away.
-//   * decode item: up to 16 (token, q-head) columns of one kv head (the GQA
-//     group shares every K/V row it reads).  Four waves stream disjoint
-//     32-key blocks straight from HBM into 16x16x32 MFMA operands and merge
-//     their softmax states through LDS at the end.
-// K rows feed MFMA A operands directly (16-byte loads).  V is transposed to
-// V^T in LDS (register 8x8 / 4x8 transposes) so that each lane reads eight
-// consecutive keys of one head_dim column.  The key order inside each 16/32
-// key chunk is permuted so that the softmax output already sits in the P^T
-// operand layout; K/V operands follow the same permutation.
+//     except one exchange with the partner lane 32 away.  K and V^T tiles of
+//     64 keys are double-buffered in LDS (one barrier per tile); the global
+//     loads of tile i+1 and the block-table reads of tile i+2 are in flight
+//     while tile i is computed.
+//   * decode item (Lq*G <= 16): up to 16 (token, q-head) columns of one kv
+//     head; the GQA group shares every K/V row it reads.  The split's page
+//     ids are staged in LDS; four waves stream disjoint 32-key blocks from
+//     HBM (K straight into 16x16x32 MFMA operands, V through a per-wave LDS
+//     transpose), loads of the next block in flight, and merge their
+//     softmax states through LDS at the end.
+// The key order inside each 16/32-key chunk is permuted so that the softmax
+// output already sits in the P^T operand layout; V^T follows the same
+// permutation.  The running max is only raised when a row's new maximum
+// exceeds it by more than kTau (log2 units), so the O rescale is skipped on
+// most tiles; exp2 arguments then stay <= kTau, and the final normalisation
+// uses the same running max, so the result is unchanged.
 #include "rpa_internal.h"
 
 namespace rpa {
@@ -39,6 +46,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kTau = 8.0f;      // lazy-rescale threshold (log2 units)
+constexpr int kPageCache = 512;   // decode: block-table entries staged in LDS
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -73,6 +82,26 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Cross-lane exchanges.  permlane32_swap with both operands = v leaves, in
+// every lane, v of lane l%32 in one result and v of lane l%32 + 32 in the
+// other; permlane16_swap does the same for lanes l and l ^ 16.
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Orders this wave's LDS writes before its later LDS reads (and vice versa).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -85,24 +114,54 @@ struct BoolTag {
   static constexpr bool value = B;
 };
 
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ bool is_decode(int lq, int G) { return lq > 0 && G <= kDecCols && lq * G <= kDecCols; }
+__device__ __forceinline__ int prefill_tiles(int lq, int G) {
+  return (lq <= 0 || is_decode(lq, G)) ? 0 : (int)(((int64_t)lq * G + kTileRows - 1) / kTileRows);
+}
+
 struct Item {
   int b;     // request
   int tile;  // q-tile within the request (prefill)
   int kind;  // 0 none, 1 prefill, 2 decode
+  int kmax;  // longest cache_seqlens in the batch (sets the split chunk)
 };
 
-// Maps a linear work-item index to (request, tile).  Items are numbered in
-// request order; request b contributes items_for_request(Lq_b, G) of them.
-// Every wave scans independently (the reads hit cache), so no barrier.
-__device__ Item resolve_item(const AttnParams &p, int item) {
+// Maps a linear work-item index to (request, tile).  Items [0, NP) are the
+// prefill q-tiles in request order, the heaviest (last) tile of a request
+// first; items [NP, NP + ND) are the decode items in request order.  Every
+// wave scans independently (the reads hit cache), so no barrier is needed.
+__device__ Item resolve_item(const AttnParams &p, int item, bool decode_only) {
   const int lane = threadIdx.x & 63;
+  int np = 0, kmax = 0;
+  for (int c = 0; c < p.batch; c += 64) {
+    const int b = c + lane;
+    if (b < p.batch) {
+      kmax = max(kmax, p.cache_seqlens[b]);
+      if (!decode_only) np += prefill_tiles(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b], p.G);
+    }
+  }
+  kmax = wave_max_i(kmax);
+  np = wave_sum_i(np);
+  const bool pre = item < np;
+  const int target = pre ? item : item - np;
   int base = 0;
   for (int c = 0; c < p.batch; c += 64) {
     const int b = c + lane;
-    int n = 0, lq = 0;
+    int n = 0;
     if (b < p.batch) {
-      lq = p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b];
-      n = (int)items_for_request(lq, p.G);
+      const int lq = p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b];
+      n = pre ? prefill_tiles(lq, p.G) : (is_decode(lq, p.G) ? 1 : 0);
     }
     int incl = n;
 #pragma unroll
@@ -111,18 +170,17 @@ __device__ Item resolve_item(const AttnParams &p, int item) {
       if (lane >= o) incl += t;
     }
     const int excl = incl - n;
-    const bool hit = item >= base + excl && item < base + incl;
-    const unsigned long long mask = __ballot(hit);
+    const unsigned long long mask = __ballot(target >= base + excl && target < base + incl);
     if (mask) {
       const int src = __ffsll((long long)mask) - 1;
       const int e = __shfl(excl, src);
-      const int lqs = __shfl(lq, src);
-      const bool dec = (int64_t)lqs * p.G <= kDecCols && p.G <= kDecCols;
-      return Item{c + src, item - base - e, dec ? 2 : 1};
+      const int nb = __shfl(n, src);
+      const int k = target - base - e;
+      return Item{c + src, pre ? nb - 1 - k : 0, pre ? 1 : 2, kmax};
     }
     base += __shfl(incl, 63);
   }
-  return Item{-1, 0, 0};
+  return Item{-1, 0, 0, kmax};
 }
 
 // Key range [lo, hi) visible to rows with absolute positions in
@@ -139,13 +197,14 @@ __device__ __forceinline__ Range visible_range(const AttnParams &p, int lk, int 
   return Range{lo, hi};
 }
 
-// Contiguous cut s of S over [lo aligned down to 16, hi), chunks rounded to
-// `align` keys.  Empty when t0 >= t1.
-__device__ __forceinline__ Range split_range(Range r, int S, int s, int align) {
+// Split s of S: the range starts at lo aligned down to 16 and is cut into
+// chunks of ceil(kmax / S) keys rounded up to `align`, the same chunk size
+// for every item of the batch (so split workgroups carry equal work); an
+// item shorter than kmax leaves its last splits empty.
+__device__ __forceinline__ Range split_range(Range r, int kmax, int S, int s, int align) {
   const int lo_a = r.lo & ~15;
-  const int span = r.hi - lo_a;
-  if (span <= 0) return Range{0, 0};
-  int chunk = (span + S - 1) / S;
+  if (r.hi <= lo_a) return Range{0, 0};
+  int chunk = (kmax + S - 1) / S;
   chunk = (chunk + align - 1) / align * align;
   const int t0 = lo_a + s * chunk;
   return Range{t0, min(r.hi, t0 + chunk)};
@@ -159,7 +218,8 @@ struct PrefillLds {
   static constexpr int VS = kTileKeys + 8;  // V^T row stride (bf16): +16 B pad
   static constexpr int kBytes = kTileKeys * KS * 2;
   static constexpr int vBytes = D * VS * 2;
-  static constexpr int bytes = kBytes + vBytes;
+  static constexpr int bufBytes = kBytes + vBytes;
+  static constexpr int bytes = 2 * bufBytes;  // double buffered
 };
 
 // Position of key kl (0..63) of a prefill KV tile inside a V^T row.  Within
@@ -174,12 +234,24 @@ template <int D, bool MASK, bool BIAS>
 __device__ __forceinline__ void prefill_tile_step(const uint16_t *Ks, const uint16_t *Vt,
                                                   const bf16x8 *qf, f32x16 *oacc, float &m_run,
                                                   float &l_run, int kb, int lo_r, int hi_r, int qa,
-                                                  const float *rel_row, int R, float scale_log2,
+                                                  const float *rel_row, int R, float c, bool pos_scale,
                                                   int l32, int hf) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
   constexpr int KS = PrefillLds<D>::KS;
   constexpr int VS = PrefillLds<D>::VS;
+  // Lane (l32, hf) holds S[row l32][key kb + 32 kb2 + 8 (j/4) + 4 hf + j%4].
+  float bv[2][16];
+  if constexpr (BIAS) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int d = qa - (kb + 32 * kb2 + 8 * (j >> 2) + 4 * hf + (j & 3));
+        bv[kb2][j] = (unsigned)d < (unsigned)R ? rel_row[d] : 0.f;
+      }
+    }
+  }
   f32x16 sacc[2];
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -188,58 +260,74 @@ __device__ __forceinline__ void prefill_tile_step(const uint16_t *Ks, const uint
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) sacc[kb2] = mfma32(as_bf16x8(ld16(kp + 16 * ks)), qf[ks], sacc[kb2]);
   }
-  // Lane (l32, hf) holds S[row l32][key kb + 32 kb2 + 8 (j/4) + 4 hf + j%4].
-  float x[2][16];
+  constexpr bool PLAIN = !MASK && !BIAS;
   float mx = neg_inf();
+  if constexpr (PLAIN) {
+    if (pos_scale) {
+      float ms = neg_inf();
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int t = kb + 32 * kb2 + 8 * (j >> 2) + 4 * hf + (j & 3);
-      float v = sacc[kb2][j] * scale_log2;
-      if (BIAS) {
-        const int d = qa - t;
-        if ((unsigned)d < (unsigned)R) v = __builtin_fmaf(rel_row[d], kLog2e, v);
+        for (int j = 0; j < 16; ++j) ms = fmaxf(ms, sacc[kb2][j]);
+      mx = ms * c;
+    } else {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb2][j] * c);
+    }
+  } else {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float v = sacc[kb2][j] * c;
+        if constexpr (BIAS) v = __builtin_fmaf(bv[kb2][j], kLog2e, v);
+        if constexpr (MASK) {
+          const int t = kb + 32 * kb2 + 8 * (j >> 2) + 4 * hf + (j & 3);
+          if (t < lo_r || t > hi_r) v = neg_inf();
+        }
+        sacc[kb2][j] = v;
+        mx = fmaxf(mx, v);
       }
-      if (MASK) {
-        if (t < lo_r || t > hi_r) v = neg_inf();
-      }
-      x[kb2][j] = v;
-      mx = fmaxf(mx, v);
     }
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(m_run, mx);
-  const float m_use = m_new == neg_inf() ? 0.f : m_new;
-  const float alpha = exp2_fast(m_run - m_use);
-  m_run = m_new;
+  mx = xor32_max(mx);
+  if (__any(mx > m_run + kTau)) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_new == neg_inf() ? 1.f : exp2_fast(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+  }
+  const float m_use = m_run == neg_inf() ? 0.f : m_run;
   float psum = 0.f;
   bf16x8 pb[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int cc = 0; cc < 4; ++cc) {
     float pe[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      pe[i] = exp2_fast(x[c >> 1][8 * (c & 1) + i] - m_use);
+      const float sv = sacc[cc >> 1][8 * (cc & 1) + i];
+      pe[i] = exp2_fast(PLAIN ? __builtin_fmaf(sv, c, -m_use) : sv - m_use);
       psum += pe[i];
     }
-    pb[c] = pack8_bf16(pe);
+    pb[cc] = pack8_bf16(pe);
   }
-  l_run = l_run * alpha + psum;
+  l_run += psum;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int cc = 0; cc < 4; ++cc) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const bf16x8 a = as_bf16x8(ld16(Vt + (32 * db + l32) * VS + 16 * c + 8 * hf));
-      oacc[db] = mfma32(a, pb[c], oacc[db]);
+      const bf16x8 a = as_bf16x8(ld16(Vt + (32 * db + l32) * VS + 16 * cc + 8 * hf));
+      oacc[db] = mfma32(a, pb[cc], oacc[db]);
     }
   }
 }
 
 template <int D>
-__device__ void prefill_item(const AttnParams &p, int b, int tile, int g, int s, char *smem) {
+__device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, char *smem) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
   constexpr int CH = D / 8;                          // 16-byte chunks per K/V row
@@ -248,9 +336,8 @@ __device__ void prefill_item(const AttnParams &p, int b, int tile, int g, int s,
   constexpr int KS = PrefillLds<D>::KS;
   constexpr int VS = PrefillLds<D>::VS;
   static_assert(KPT == 4 || KPT == 2, "staging layout");
-  uint16_t *Ks = reinterpret_cast<uint16_t *>(smem);
-  uint16_t *Vt = reinterpret_cast<uint16_t *>(smem + PrefillLds<D>::kBytes);
 
+  const int b = it.b;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int tok0 = p.cu_seqlens_q[b];
@@ -258,7 +345,7 @@ __device__ void prefill_item(const AttnParams &p, int b, int tile, int g, int s,
   const int lk = p.cache_seqlens[b];
   const int G = p.G;
   const int nrows = lq * G;
-  const int row0 = tile * kTileRows;
+  const int row0 = it.tile * kTileRows;
   const int row_last = min(row0 + kTileRows, nrows) - 1;
   int r = row0 + 32 * w + l32;
   const bool row_valid = r <= row_last;
@@ -270,20 +357,23 @@ __device__ void prefill_item(const AttnParams &p, int b, int tile, int g, int s,
   const int qa_min = row0 / G + lk - lq;
   const int qa_max = row_last / G + lk - lq;
 
-  const Range sr = split_range(visible_range(p, lk, qa_min, qa_max), p.S, s, kTileKeys);
+  const Range sr = split_range(visible_range(p, lk, qa_min, qa_max), it.kmax, p.S, s, kTileKeys);
   const int t0 = sr.lo, t1 = sr.hi;
+  const int kend = min(lk, t1);  // keys at or past this are neither loaded nor visible
   // This lane's visible keys inside the split: [lo_r, hi_r].
-  int lo_r = t0, hi_r = min(lk, t1) - 1;
+  int lo_r = t0, hi_r = kend - 1;
   if (p.left >= 0) lo_r = max(lo_r, qa - p.left);
   if (p.causal) hi_r = min(hi_r, qa);
   if (p.right >= 0) hi_r = min(hi_r, qa + p.right);
   // Keys in [in_lo, in_hi] are visible to every row of the tile.
-  int in_lo = t0, in_hi = min(lk, t1) - 1;
+  int in_lo = t0, in_hi = kend - 1;
   if (p.left >= 0) in_lo = max(in_lo, qa_max - p.left);
   if (p.causal) in_hi = min(in_hi, qa_min);
   if (p.right >= 0) in_hi = min(in_hi, qa_min + p.right);
   const int band_lo = qa_min - p.R + 1, band_hi = qa_max;
   const float *rel_row = p.R > 0 ? p.rel_logits + ((int64_t)tok * p.H + head) * p.R : nullptr;
+  const float c = p.scale_log2;
+  const bool pos_scale = c > 0.f;
 
   bf16x8 qf[KSTEPS];
   {
@@ -305,22 +395,15 @@ __device__ void prefill_item(const AttnParams &p, int b, int tile, int g, int s,
   const int kgv = tid % NKG, dcv = tid / NKG;
   u32x4 kreg[KPT], vreg[KPT];
 
-  auto load_rows = [&](const uint16_t *base, int key0, int dc, u32x4 *regs) {
-    if (key0 < lk) {
-      const int page = bt[key0 / p.BS];
-      const int64_t off = (((int64_t)page * p.BS + key0 % p.BS) * p.Hkv + g) * D + dc * 8;
+  auto page_of = [&](int key) { return key < kend ? bt[key / p.BS] : 0; };
+  auto load_rows = [&](const uint16_t *base, int key0, int page, int dc, u32x4 *regs) {
+    const int64_t off = (((int64_t)page * p.BS + key0 % p.BS) * p.Hkv + g) * D + dc * 8;
 #pragma unroll
-      for (int rr = 0; rr < KPT; ++rr) regs[rr] = (key0 + rr < lk) ? ld16(base + off + rr * tok_stride) : zero16();
-    } else {
-#pragma unroll
-      for (int rr = 0; rr < KPT; ++rr) regs[rr] = zero16();
-    }
+    for (int rr = 0; rr < KPT; ++rr) regs[rr] = (key0 + rr < kend) ? ld16(base + off + rr * tok_stride) : zero16();
   };
-  auto stage_load = [&](int kb) {
-    load_rows(p.k, kb + kgk * KPT, dck, kreg);
-    load_rows(p.v, kb + kgv * KPT, dcv, vreg);
-  };
-  auto stage_store = [&]() {
+  auto stage_store = [&](int buf) {
+    uint16_t *Ks = reinterpret_cast<uint16_t *>(smem + buf * PrefillLds<D>::bufBytes);
+    uint16_t *Vt = reinterpret_cast<uint16_t *>(smem + buf * PrefillLds<D>::bufBytes + PrefillLds<D>::kBytes);
 #pragma unroll
     for (int rr = 0; rr < KPT; ++rr)
       *reinterpret_cast<u32x4 *>(Ks + (kgk * KPT + rr) * KS + dck * 8) = kreg[rr];
@@ -337,30 +420,46 @@ __device__ void prefill_item(const AttnParams &p, int b, int tile, int g, int s,
   };
 
   if (t0 < t1) {
-    stage_load(t0);
+    // Prologue: tile 0 into buffer 0; block-table entries of tile 1 in flight.
+    load_rows(p.k, t0 + kgk * KPT, page_of(t0 + kgk * KPT), dck, kreg);
+    load_rows(p.v, t0 + kgv * KPT, page_of(t0 + kgv * KPT), dcv, vreg);
+    int pgk = page_of(t0 + kTileKeys + kgk * KPT);
+    int pgv = page_of(t0 + kTileKeys + kgv * KPT);
+    stage_store(0);
+    __syncthreads();
+    int buf = 0;
     for (int kb = t0; kb < t1; kb += kTileKeys) {
-      __syncthreads();
-      stage_store();
-      __syncthreads();
-      if (kb + kTileKeys < t1) stage_load(kb + kTileKeys);
+      const bool more = kb + kTileKeys < t1;
+      if (more) {
+        const int nk = kb + kTileKeys;
+        load_rows(p.k, nk + kgk * KPT, pgk, dck, kreg);
+        load_rows(p.v, nk + kgv * KPT, pgv, dcv, vreg);
+        pgk = page_of(nk + kTileKeys + kgk * KPT);
+        pgv = page_of(nk + kTileKeys + kgv * KPT);
+      }
+      const uint16_t *Ks = reinterpret_cast<const uint16_t *>(smem + buf * PrefillLds<D>::bufBytes);
+      const uint16_t *Vt = reinterpret_cast<const uint16_t *>(smem + buf * PrefillLds<D>::bufBytes + PrefillLds<D>::kBytes);
       const bool interior = kb >= in_lo && kb + kTileKeys - 1 <= in_hi;
       const bool bias = p.R > 0 && kb <= band_hi && kb + kTileKeys - 1 >= band_lo;
       if (interior) {
         if (bias)
-          prefill_tile_step<D, false, true>(Ks, Vt, qf, oacc, m_run, l_run, kb, lo_r, hi_r, qa, rel_row, p.R, p.scale_log2, l32, hf);
+          prefill_tile_step<D, false, true>(Ks, Vt, qf, oacc, m_run, l_run, kb, lo_r, hi_r, qa, rel_row, p.R, c, pos_scale, l32, hf);
         else
-          prefill_tile_step<D, false, false>(Ks, Vt, qf, oacc, m_run, l_run, kb, lo_r, hi_r, qa, rel_row, p.R, p.scale_log2, l32, hf);
+          prefill_tile_step<D, false, false>(Ks, Vt, qf, oacc, m_run, l_run, kb, lo_r, hi_r, qa, rel_row, p.R, c, pos_scale, l32, hf);
       } else {
         if (bias)
-          prefill_tile_step<D, true, true>(Ks, Vt, qf, oacc, m_run, l_run, kb, lo_r, hi_r, qa, rel_row, p.R, p.scale_log2, l32, hf);
+          prefill_tile_step<D, true, true>(Ks, Vt, qf, oacc, m_run, l_run, kb, lo_r, hi_r, qa, rel_row, p.R, c, pos_scale, l32, hf);
         else
-          prefill_tile_step<D, true, false>(Ks, Vt, qf, oacc, m_run, l_run, kb, lo_r, hi_r, qa, rel_row, p.R, p.scale_log2, l32, hf);
+          prefill_tile_step<D, true, false>(Ks, Vt, qf, oacc, m_run, l_run, kb, lo_r, hi_r, qa, rel_row, p.R, c, pos_scale, l32, hf);
       }
+      if (more) stage_store(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
     }
   }
 
   // Epilogue: lane (l32, hf) holds O^T[d = 32 db + 8 (j/4) + 4 hf + j%4][row l32].
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xor32_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_v = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : neg_inf();
   if (!row_valid) return;
@@ -400,8 +499,10 @@ struct DecodeLds {
   static constexpr int VS = kDecWaveKeys + 8;              // V^T row stride (bf16): 80 B
   static constexpr int vtBytes = 4 * D * VS * 2;           // one V^T tile per wave
   static constexpr int redOBytes = 4 * D * kDecCols * 4;   // per-wave O^T partials
+  static constexpr int mainBytes = vtBytes > redOBytes ? vtBytes : redOBytes;
   static constexpr int redMLBytes = 2 * 4 * kDecCols * 4;  // per-wave m and l
-  static constexpr int bytes = (vtBytes > redOBytes ? vtBytes : redOBytes) + redMLBytes;
+  static constexpr int pageBytes = kPageCache * 4;
+  static constexpr int bytes = mainBytes + redMLBytes + pageBytes;
 };
 
 // Key (0..31, relative to the wave's block) held at V^T slot p: slot 8q + i
@@ -418,7 +519,7 @@ struct DecodeRegs {
 };
 
 template <int D>
-__device__ void decode_item(const AttnParams &p, int b, int g, int s, char *smem) {
+__device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, char *smem) {
   constexpr int QK = D / 32;       // 16x16x32 k-steps over head_dim
   constexpr int DB = D / 16;       // 16-row blocks of O^T
   constexpr int DQ = D / 4;        // head_dim span of one lane group in K operands
@@ -428,9 +529,11 @@ __device__ void decode_item(const AttnParams &p, int b, int g, int s, char *smem
   constexpr int VS = DecodeLds<D>::VS;
   static_assert(KPL == 8 || KPL == 4, "staging layout");
 
+  const int b = it.b;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c16 = lane & 15, q = lane >> 4;
   uint16_t *Vt = reinterpret_cast<uint16_t *>(smem) + w * D * VS;
+  int32_t *pcache = reinterpret_cast<int32_t *>(smem + DecodeLds<D>::mainBytes + DecodeLds<D>::redMLBytes);
 
   const int tok0 = p.cu_seqlens_q[b];
   const int lq = p.cu_seqlens_q[b + 1] - tok0;
@@ -444,18 +547,21 @@ __device__ void decode_item(const AttnParams &p, int b, int g, int s, char *smem
   const int qa = qi + lk - lq;
   const int qa_min = lk - lq;
   const int qa_max = (ncols - 1) / G + lk - lq;
-  const Range sr = split_range(visible_range(p, lk, qa_min, qa_max), p.S, s, kDecStep);
+  const Range sr = split_range(visible_range(p, lk, qa_min, qa_max), it.kmax, p.S, s, kDecStep);
   const int t0 = sr.lo, t1 = sr.hi;
-  int lo_c = t0, hi_c = min(lk, t1) - 1;
+  const int kend = min(lk, t1);
+  int lo_c = t0, hi_c = kend - 1;
   if (p.left >= 0) lo_c = max(lo_c, qa - p.left);
   if (p.causal) hi_c = min(hi_c, qa);
   if (p.right >= 0) hi_c = min(hi_c, qa + p.right);
-  int in_lo = t0, in_hi = min(lk, t1) - 1;
+  int in_lo = t0, in_hi = kend - 1;
   if (p.left >= 0) in_lo = max(in_lo, qa_max - p.left);
   if (p.causal) in_hi = min(in_hi, qa_min);
   if (p.right >= 0) in_hi = min(in_hi, qa_min + p.right);
   const int band_lo = qa_min - p.R + 1, band_hi = qa_max;
   const float *rel_row = p.R > 0 ? p.rel_logits + ((int64_t)tok * p.H + head) * p.R : nullptr;
+  const float c = p.scale_log2;
+  const bool pos_scale = c > 0.f;
 
   bf16x8 qf[QK];
   {
@@ -471,38 +577,46 @@ __device__ void decode_item(const AttnParams &p, int b, int g, int s, char *smem
   const int64_t tok_stride = (int64_t)p.Hkv * D;
   const int32_t *bt = p.block_table + (int64_t)b * p.P;
   const int vg = lane % NG, vdc = lane / NG;
+  int pfirst = 0;  // block-table index of pcache[0]
 
   auto issue = [&](DecodeRegs<D> &Rg, int base) {
     int64_t row0[2];  // element offset of slot 0 of each 16-key block
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int kb = base + 16 * blk;
-      int page = 0, slot0 = 0;
-      if (kb < lk) {
-        page = bt[kb / p.BS];
-        slot0 = kb % p.BS;
-      }
-      row0[blk] = (((int64_t)page * p.BS + slot0) * p.Hkv + g) * D;
+      int page = 0;
+      if (kb < kend) page = pcache[kb / p.BS - pfirst];
+      row0[blk] = (((int64_t)page * p.BS + kb % p.BS) * p.Hkv + g) * D;
     }
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int key = base + 16 * blk + c16;
       const uint16_t *src = p.k + row0[blk] + c16 * tok_stride + q * DQ;
 #pragma unroll
-      for (int ks = 0; ks < QK; ++ks) Rg.k[blk][ks] = key < lk ? ld16(src + 8 * ks) : zero16();
+      for (int ks = 0; ks < QK; ++ks) Rg.k[blk][ks] = key < kend ? ld16(src + 8 * ks) : zero16();
     }
 #pragma unroll
     for (int rr = 0; rr < KPL; ++rr) {
       const int kr = decode_key_of_slot(vg * KPL + rr);
-      const int blk = kr >> 4;
       const int key = base + kr;
-      Rg.v[rr] = key < lk ? ld16(p.v + row0[blk] + (kr & 15) * tok_stride + vdc * 8) : zero16();
+      Rg.v[rr] = key < kend ? ld16(p.v + row0[kr >> 4] + (kr & 15) * tok_stride + vdc * 8) : zero16();
     }
   };
 
   auto compute = [&](DecodeRegs<D> &Rg, int base, auto mask_tag, auto bias_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr bool BIAS = decltype(bias_tag)::value;
+    constexpr bool PLAIN = !MASK && !BIAS;
+    float bv[2][4];
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = qa - (base + 16 * blk + 4 * q + j);
+          bv[blk][j] = (unsigned)d < (unsigned)p.R ? rel_row[d] : 0.f;
+        }
+    }
     wave_lds_sync();
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -523,42 +637,58 @@ __device__ void decode_item(const AttnParams &p, int b, int g, int s, char *smem
       for (int ks = 0; ks < QK; ++ks) sacc[blk] = mfma16(as_bf16x8(Rg.k[blk][ks]), qf[ks], sacc[blk]);
     }
     // Lane (c16, q) holds S[col c16][key base + 16 blk + 4 q + j].
-    float x[2][4];
     float mx = neg_inf();
+    if constexpr (PLAIN) {
+      if (pos_scale) {
+        float ms = neg_inf();
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+        for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = base + 16 * blk + 4 * q + j;
-        float v = sacc[blk][j] * p.scale_log2;
-        if (BIAS) {
-          const int d = qa - t;
-          if ((unsigned)d < (unsigned)p.R) v = __builtin_fmaf(rel_row[d], kLog2e, v);
+          for (int j = 0; j < 4; ++j) ms = fmaxf(ms, sacc[blk][j]);
+        mx = ms * c;
+      } else {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sacc[blk][j] * c);
+      }
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float v = sacc[blk][j] * c;
+          if constexpr (BIAS) v = __builtin_fmaf(bv[blk][j], kLog2e, v);
+          if constexpr (MASK) {
+            const int t = base + 16 * blk + 4 * q + j;
+            if (t < lo_c || t > hi_c) v = neg_inf();
+          }
+          sacc[blk][j] = v;
+          mx = fmaxf(mx, v);
         }
-        if (MASK) {
-          if (t < lo_c || t > hi_c) v = neg_inf();
-        }
-        x[blk][j] = v;
-        mx = fmaxf(mx, v);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == neg_inf() ? 0.f : m_new;
-    const float alpha = exp2_fast(m_run - m_use);
-    m_run = m_new;
+    mx = xor16_max(mx);
+    mx = xor32_max(mx);
+    if (__any(mx > m_run + kTau)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == neg_inf() ? 1.f : exp2_fast(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+    const float m_use = m_run == neg_inf() ? 0.f : m_run;
     float pe[8];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      pe[i] = exp2_fast(x[i >> 2][i & 3] - m_use);
+      const float sv = sacc[i >> 2][i & 3];
+      pe[i] = exp2_fast(PLAIN ? __builtin_fmaf(sv, c, -m_use) : sv - m_use);
       psum += pe[i];
     }
-    l_run = l_run * alpha + psum;
+    l_run += psum;
     const bf16x8 pf = pack8_bf16(pe);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     wave_lds_sync();
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -579,26 +709,38 @@ __device__ void decode_item(const AttnParams &p, int b, int g, int s, char *smem
     }
   };
 
-  // Wave w takes 32-key blocks w, w + 4, w + 8, ... of the split; loads for
-  // the next block are in flight while the current one is computed.
-  const int nblk = t1 > t0 ? (t1 - t0 + kDecWaveKeys - 1) / kDecWaveKeys : 0;
-  const int my_n = nblk > w ? (nblk - w + 3) / 4 : 0;
-  DecodeRegs<D> RA, RB;
-  if (my_n > 0) issue(RA, t0 + kDecWaveKeys * w);
-  for (int it = 0; it < my_n; it += 2) {
-    if (it + 1 < my_n) issue(RB, t0 + kDecWaveKeys * (w + 4 * (it + 1)));
-    step(RA, t0 + kDecWaveKeys * (w + 4 * it));
-    if (it + 1 >= my_n) break;
-    if (it + 2 < my_n) issue(RA, t0 + kDecWaveKeys * (w + 4 * (it + 2)));
-    step(RB, t0 + kDecWaveKeys * (w + 4 * (it + 1)));
+  // The split is walked in segments whose block-table entries fit the LDS
+  // page cache.  Inside a segment, wave w takes 32-key blocks w, w + 4, ...
+  // with the loads of its next block in flight while the current one is
+  // computed.
+  const int seg_keys = ((kPageCache - 2) * p.BS) / kDecStep * kDecStep;
+  for (int sg0 = t0; sg0 < t1; sg0 += seg_keys) {
+    const int sg1 = min(t1, sg0 + seg_keys);
+    __syncthreads();  // every wave is done with the previous segment's pages
+    if (sg0 < kend) {
+      pfirst = sg0 / p.BS;
+      const int np = (min(sg1, kend) - 1) / p.BS - pfirst + 1;
+      for (int i = tid; i < np; i += kThreads) pcache[i] = bt[pfirst + i];
+    }
+    __syncthreads();
+    const int nblk = (sg1 - sg0 + kDecWaveKeys - 1) / kDecWaveKeys;
+    const int my_n = nblk > w ? (nblk - w + 3) / 4 : 0;
+    DecodeRegs<D> RA, RB;
+    if (my_n > 0) issue(RA, sg0 + kDecWaveKeys * w);
+    for (int i = 0; i < my_n; i += 2) {
+      if (i + 1 < my_n) issue(RB, sg0 + kDecWaveKeys * (w + 4 * (i + 1)));
+      step(RA, sg0 + kDecWaveKeys * (w + 4 * i));
+      if (i + 1 >= my_n) break;
+      if (i + 2 < my_n) issue(RA, sg0 + kDecWaveKeys * (w + 4 * (i + 2)));
+      step(RB, sg0 + kDecWaveKeys * (w + 4 * (i + 1)));
+    }
   }
 
   // Merge the four waves' (m, l, O^T) through LDS.
-  float l_col = l_run + __shfl_xor(l_run, 16);
-  l_col += __shfl_xor(l_col, 32);
+  const float l_col = xor32_sum(xor16_sum(l_run));
   __syncthreads();
   float *red_o = reinterpret_cast<float *>(smem);  // [4][D][16]
-  float *red_m = reinterpret_cast<float *>(smem + (DecodeLds<D>::bytes - DecodeLds<D>::redMLBytes));
+  float *red_m = reinterpret_cast<float *>(smem + DecodeLds<D>::mainBytes);
   float *red_l = red_m + 4 * kDecCols;
   if (q == 0) {
     red_m[w * kDecCols + c16] = m_run;
@@ -657,24 +799,26 @@ __device__ void decode_item(const AttnParams &p, int b, int g, int s, char *smem
   }
 }
 
-template <int D>
+template <int D, bool DECODE_ONLY>
 constexpr int attn_lds_bytes() {
-  return PrefillLds<D>::bytes > DecodeLds<D>::bytes ? PrefillLds<D>::bytes : DecodeLds<D>::bytes;
+  return (DECODE_ONLY || PrefillLds<D>::bytes < DecodeLds<D>::bytes) ? DecodeLds<D>::bytes : PrefillLds<D>::bytes;
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[attn_lds_bytes<D>()];
+// DECODE_ONLY: every request of the batch has Lq*G <= 16 (known on the host
+// from max_seqlen_q), so the prefill path is not compiled in.
+template <int D, bool DECODE_ONLY>
+__global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[attn_lds_bytes<D, DECODE_ONLY>()];
   const int bid = blockIdx.x;
   const int s = bid % p.S;
   const int rest = bid / p.S;
   const int g = rest % p.Hkv;
   const int item = rest / p.Hkv;
-  const Item it = resolve_item(p, item);
-  if (it.kind == 1) {
-    prefill_item<D>(p, it.b, it.tile, g, s, smem);
-  } else if (it.kind == 2) {
-    decode_item<D>(p, it.b, g, s, smem);
+  const Item it = resolve_item(p, item, DECODE_ONLY);
+  if (it.kind == 2) {
+    decode_item<D>(p, it, g, s, smem);
+  } else if constexpr (!DECODE_ONLY) {
+    if (it.kind == 1) prefill_item<D>(p, it, g, s, smem);
   }
 }
 
@@ -717,14 +861,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
 
 }  // namespace
 
-hipError_t launch_attention(const AttnParams &p, int head_dim, int64_t n_items_ub, hipStream_t stream) {
+hipError_t launch_attention(const AttnParams &p, int head_dim, int64_t n_items_ub, bool decode_only,
+                            hipStream_t stream) {
   const int64_t blocks = n_items_ub * p.Hkv * p.S;
   if (blocks <= 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(kThreads);
   if (head_dim == 128) {
-    hipLaunchKernelGGL(attn_kernel<128>, grid, block, 0, stream, p);
+    if (decode_only) hipLaunchKernelGGL((attn_kernel<128, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((attn_kernel<128, false>), grid, block, 0, stream, p);
   } else {
-    hipLaunchKernelGGL(attn_kernel<64>, grid, block, 0, stream, p);
+    if (decode_only) hipLaunchKernelGGL((attn_kernel<64, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((attn_kernel<64, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
