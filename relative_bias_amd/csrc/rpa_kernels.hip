@@ -241,17 +241,6 @@ __device__ __forceinline__ void prefill_tile_step(const uint16_t *Ks, const uint
   constexpr int KS = PrefillLds<D>::KS;
   constexpr int VS = PrefillLds<D>::VS;
   // Lane (l32, hf) holds S[row l32][key kb + 32 kb2 + 8 (j/4) + 4 hf + j%4].
-  float bv[2][16];
-  if constexpr (BIAS) {
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int d = qa - (kb + 32 * kb2 + 8 * (j >> 2) + 4 * hf + (j & 3));
-        bv[kb2][j] = (unsigned)d < (unsigned)R ? rel_row[d] : 0.f;
-      }
-    }
-  }
   f32x16 sacc[2];
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -281,10 +270,13 @@ __device__ __forceinline__ void prefill_tile_step(const uint16_t *Ks, const uint
     for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
+        const int t = kb + 32 * kb2 + 8 * (j >> 2) + 4 * hf + (j & 3);
         float v = sacc[kb2][j] * c;
-        if constexpr (BIAS) v = __builtin_fmaf(bv[kb2][j], kLog2e, v);
+        if constexpr (BIAS) {
+          const int d = qa - t;
+          v = __builtin_fmaf((unsigned)d < (unsigned)R ? rel_row[d] : 0.f, kLog2e, v);
+        }
         if constexpr (MASK) {
-          const int t = kb + 32 * kb2 + 8 * (j >> 2) + 4 * hf + (j & 3);
           if (t < lo_r || t > hi_r) v = neg_inf();
         }
         sacc[kb2][j] = v;
@@ -441,17 +433,12 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       const uint16_t *Vt = reinterpret_cast<const uint16_t *>(smem + buf * PrefillLds<D>::bufBytes + PrefillLds<D>::kBytes);
       const bool interior = kb >= in_lo && kb + kTileKeys - 1 <= in_hi;
       const bool bias = p.R > 0 && kb <= band_hi && kb + kTileKeys - 1 >= band_lo;
-      if (interior) {
-        if (bias)
-          prefill_tile_step<D, false, true>(Ks, Vt, qf, oacc, m_run, l_run, kb, lo_r, hi_r, qa, rel_row, p.R, c, pos_scale, l32, hf);
-        else
-          prefill_tile_step<D, false, false>(Ks, Vt, qf, oacc, m_run, l_run, kb, lo_r, hi_r, qa, rel_row, p.R, c, pos_scale, l32, hf);
-      } else {
-        if (bias)
-          prefill_tile_step<D, true, true>(Ks, Vt, qf, oacc, m_run, l_run, kb, lo_r, hi_r, qa, rel_row, p.R, c, pos_scale, l32, hf);
-        else
-          prefill_tile_step<D, true, false>(Ks, Vt, qf, oacc, m_run, l_run, kb, lo_r, hi_r, qa, rel_row, p.R, c, pos_scale, l32, hf);
-      }
+      // Two variants only: more inlined copies raise register pressure past
+      // the 256 VGPRs that two workgroups per CU allow.
+      if (interior && !bias)
+        prefill_tile_step<D, false, false>(Ks, Vt, qf, oacc, m_run, l_run, kb, lo_r, hi_r, qa, rel_row, p.R, c, pos_scale, l32, hf);
+      else
+        prefill_tile_step<D, true, true>(Ks, Vt, qf, oacc, m_run, l_run, kb, lo_r, hi_r, qa, rel_row, p.R, c, pos_scale, l32, hf);
       if (more) stage_store(buf ^ 1);
       __syncthreads();
       buf ^= 1;
@@ -579,8 +566,8 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
   const int vg = lane % NG, vdc = lane / NG;
   int pfirst = 0;  // block-table index of pcache[0]
 
-  auto issue = [&](DecodeRegs<D> &Rg, int base) {
-    int64_t row0[2];  // element offset of slot 0 of each 16-key block
+  // Element offsets of slot 0 of the two 16-key blocks at `base`.
+  auto rows_of = [&](int base, int64_t *row0) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int kb = base + 16 * blk;
@@ -588,6 +575,8 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
       if (kb < kend) page = pcache[kb / p.BS - pfirst];
       row0[blk] = (((int64_t)page * p.BS + kb % p.BS) * p.Hkv + g) * D;
     }
+  };
+  auto issue_k = [&](DecodeRegs<D> &Rg, const int64_t *row0, int base) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int key = base + 16 * blk + c16;
@@ -595,6 +584,8 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
 #pragma unroll
       for (int ks = 0; ks < QK; ++ks) Rg.k[blk][ks] = key < kend ? ld16(src + 8 * ks) : zero16();
     }
+  };
+  auto issue_v = [&](DecodeRegs<D> &Rg, const int64_t *row0, int base) {
 #pragma unroll
     for (int rr = 0; rr < KPL; ++rr) {
       const int kr = decode_key_of_slot(vg * KPL + rr);
@@ -603,20 +594,15 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
     }
   };
 
-  auto compute = [&](DecodeRegs<D> &Rg, int base, auto mask_tag, auto bias_tag) {
+  // One 32-key block.  A single register set carries the block: V is moved
+  // to LDS first and its registers immediately receive the next block's V;
+  // once the QK MFMAs have read K, the next block's K loads land there too.
+  auto compute = [&](DecodeRegs<D> &Rg, int base, int nbase, bool has_next, auto mask_tag, auto bias_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr bool BIAS = decltype(bias_tag)::value;
     constexpr bool PLAIN = !MASK && !BIAS;
-    float bv[2][4];
-    if constexpr (BIAS) {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = qa - (base + 16 * blk + 4 * q + j);
-          bv[blk][j] = (unsigned)d < (unsigned)p.R ? rel_row[d] : 0.f;
-        }
-    }
+    int64_t nrow0[2];
+    if (has_next) rows_of(nbase, nrow0);
     wave_lds_sync();
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -629,6 +615,7 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
         *reinterpret_cast<u32x2 *>(dst) = u32x2{pair_elem(Rg.v[0], Rg.v[1], e), pair_elem(Rg.v[2], Rg.v[3], e)};
       }
     }
+    if (has_next) issue_v(Rg, nrow0, nbase);
     f32x4 sacc[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -636,6 +623,7 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
 #pragma unroll
       for (int ks = 0; ks < QK; ++ks) sacc[blk] = mfma16(as_bf16x8(Rg.k[blk][ks]), qf[ks], sacc[blk]);
     }
+    if (has_next) issue_k(Rg, nrow0, nbase);
     // Lane (c16, q) holds S[col c16][key base + 16 blk + 4 q + j].
     float mx = neg_inf();
     if constexpr (PLAIN) {
@@ -657,10 +645,13 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
       for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+          const int t = base + 16 * blk + 4 * q + j;
           float v = sacc[blk][j] * c;
-          if constexpr (BIAS) v = __builtin_fmaf(bv[blk][j], kLog2e, v);
+          if constexpr (BIAS) {
+            const int d = qa - t;
+            v = __builtin_fmaf((unsigned)d < (unsigned)p.R ? rel_row[d] : 0.f, kLog2e, v);
+          }
           if constexpr (MASK) {
-            const int t = base + 16 * blk + 4 * q + j;
             if (t < lo_c || t > hi_c) v = neg_inf();
           }
           sacc[blk][j] = v;
@@ -697,16 +688,11 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
     }
   };
 
-  auto step = [&](DecodeRegs<D> &Rg, int base) {
+  auto step = [&](DecodeRegs<D> &Rg, int base, int nbase, bool has_next) {
     const bool interior = base >= in_lo && base + kDecWaveKeys - 1 <= in_hi;
     const bool bias = p.R > 0 && base <= band_hi && base + kDecWaveKeys - 1 >= band_lo;
-    if (interior) {
-      if (bias) compute(Rg, base, BoolTag<false>{}, BoolTag<true>{});
-      else compute(Rg, base, BoolTag<false>{}, BoolTag<false>{});
-    } else {
-      if (bias) compute(Rg, base, BoolTag<true>{}, BoolTag<true>{});
-      else compute(Rg, base, BoolTag<true>{}, BoolTag<false>{});
-    }
+    if (interior && !bias) compute(Rg, base, nbase, has_next, BoolTag<false>{}, BoolTag<false>{});
+    else compute(Rg, base, nbase, has_next, BoolTag<true>{}, BoolTag<true>{});
   };
 
   // The split is walked in segments whose block-table entries fit the LDS
@@ -725,14 +711,17 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
     __syncthreads();
     const int nblk = (sg1 - sg0 + kDecWaveKeys - 1) / kDecWaveKeys;
     const int my_n = nblk > w ? (nblk - w + 3) / 4 : 0;
-    DecodeRegs<D> RA, RB;
-    if (my_n > 0) issue(RA, sg0 + kDecWaveKeys * w);
-    for (int i = 0; i < my_n; i += 2) {
-      if (i + 1 < my_n) issue(RB, sg0 + kDecWaveKeys * (w + 4 * (i + 1)));
-      step(RA, sg0 + kDecWaveKeys * (w + 4 * i));
-      if (i + 1 >= my_n) break;
-      if (i + 2 < my_n) issue(RA, sg0 + kDecWaveKeys * (w + 4 * (i + 2)));
-      step(RB, sg0 + kDecWaveKeys * (w + 4 * (i + 1)));
+    DecodeRegs<D> Rg;
+    if (my_n > 0) {
+      int64_t row0[2];
+      const int base0 = sg0 + kDecWaveKeys * w;
+      rows_of(base0, row0);
+      issue_k(Rg, row0, base0);
+      issue_v(Rg, row0, base0);
+    }
+    for (int i = 0; i < my_n; ++i) {
+      const int base = sg0 + kDecWaveKeys * (w + 4 * i);
+      step(Rg, base, base + kDecStep, i + 1 < my_n);
     }
   }
 
@@ -807,7 +796,7 @@ constexpr int attn_lds_bytes() {
 // DECODE_ONLY: every request of the batch has Lq*G <= 16 (known on the host
 // from max_seqlen_q), so the prefill path is not compiled in.
 template <int D, bool DECODE_ONLY>
-__global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char smem[attn_lds_bytes<D, DECODE_ONLY>()];
   const int bid = blockIdx.x;
   const int s = bid % p.S;
