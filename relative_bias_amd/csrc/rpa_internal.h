@@ -29,6 +29,7 @@ struct AttnParams {
   float *part_lse;              // [S, T, H]   when S > 1
   int32_t batch, num_tokens, H, Hkv, G, BS, R, S, P;
   int32_t left, right, causal;
+  int32_t bs_shift;             // log2(BS) when BS is a power of two, else -1
   float scale_log2;             // softmax_scale * log2(e)
 };
 

@@ -73,6 +73,21 @@ __device__ __forceinline__ uint32_t pair_elem(u32x4 a, u32x4 b, int e) {
 }
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 layout, stride 0):
+// loads at offsets past the range return zeros without touching memory.
+// Both arguments must be wave-uniform; they are passed through readfirstlane
+// so that the descriptor is built in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void *ub = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+}
 __device__ __forceinline__ u32x4 zero16() { return u32x4{0u, 0u, 0u, 0u}; }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -176,7 +191,10 @@ __device__ Item resolve_item(const AttnParams &p, int item, bool decode_only) {
       const int e = __shfl(excl, src);
       const int nb = __shfl(n, src);
       const int k = target - base - e;
-      return Item{c + src, pre ? nb - 1 - k : 0, pre ? 1 : 2, kmax};
+      // Wave-uniform by construction; readfirstlane lets the compiler keep
+      // everything derived from the item in scalar registers.
+      return Item{__builtin_amdgcn_readfirstlane(c + src), __builtin_amdgcn_readfirstlane(pre ? nb - 1 - k : 0),
+                  pre ? 1 : 2, __builtin_amdgcn_readfirstlane(kmax)};
     }
     base += __shfl(incl, 63);
   }
@@ -214,44 +232,82 @@ __device__ __forceinline__ Range split_range(Range r, int kmax, int S, int s, in
 
 template <int D>
 struct PrefillLds {
-  static constexpr int KS = D + 8;          // K tile row stride (bf16): +16 B pad
-  static constexpr int VS = kTileKeys + 8;  // V^T row stride (bf16): +16 B pad
-  static constexpr int kBytes = kTileKeys * KS * 2;
-  static constexpr int vBytes = D * VS * 2;
-  static constexpr int bufBytes = kBytes + vBytes;
-  static constexpr int bytes = 2 * bufBytes;  // double buffered
+  static constexpr int UNITS = D / 8;                 // 16-byte units per key row
+  static constexpr int ROWB = D * 2;                  // bytes per key row (unpadded)
+  static constexpr int tileBytes = kTileKeys * ROWB;  // 16 KB for head_dim 128
+  static constexpr int NK = 2, NV = 2;                // double-buffered K and V tiles
+  static constexpr int kOff(int i) { return i * tileBytes; }
+  static constexpr int vOff(int i) { return (NK + i) * tileBytes; }
+  static constexpr int bytes = (NK + NV) * tileBytes;
 };
 
-// Position of key kl (0..63) of a prefill KV tile inside a V^T row.  Within
-// each 16-key chunk c, slot 8h + i (h = half-wave, i = operand element)
-// holds key 16c + 8(i/4) + 4h + i%4: the keys that lane (row, h) of the
-// 32x32 S^T accumulator holds for that chunk.
-__device__ __forceinline__ int prefill_vpos(int kl) {
-  return 16 * (kl >> 4) + 8 * ((kl >> 2) & 1) + 4 * ((kl >> 3) & 1) + (kl & 3);
+// K and V tiles are stored row-major (one key per row) with the 16-byte
+// units of each row XOR-swizzled, instead of padded, so that they can be
+// filled by direct buffer->LDS loads.  K: unit u of row r sits at
+// u ^ swz_k(r), which spreads the 16 consecutive rows one MFMA operand read
+// touches over all banks.  V: unit u sits at u ^ swz_v(r), which does the
+// same for the transposing reads of four consecutive keys.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return (4 * (r & 3)) & (D / 8 - 1); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane j receives 16-bit
+// element j%4 of the 8-byte rows addressed by lanes j/4, 4 + j/4, 8 + j/4
+// and 12 + j/4 of the group.
+__device__ __forceinline__ s16x4 lds_read_tr(const char *addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(addr));
 }
 
-template <int D, bool MASK, bool BIAS>
-__device__ __forceinline__ void prefill_tile_step(const uint16_t *Ks, const uint16_t *Vt,
-                                                  const bf16x8 *qf, f32x16 *oacc, float &m_run,
-                                                  float &l_run, int kb, int lo_r, int hi_r, int qa,
-                                                  const float *rel_row, int R, float c, bool pos_scale,
-                                                  int l32, int hf) {
+// S^T = K·Q^T for a 64-key tile: lane (l32, hf) gets
+// S[row l32][key 32 kb2 + 8 (j/4) + 4 hf + j%4] in sacc[kb2][j].
+template <int D>
+__device__ __forceinline__ void qk_tile(const char *Kb, const bf16x8 *qf, f32x16 *sacc, int l32, int hf) {
   constexpr int KSTEPS = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int KS = PrefillLds<D>::KS;
-  constexpr int VS = PrefillLds<D>::VS;
-  // Lane (l32, hf) holds S[row l32][key kb + 32 kb2 + 8 (j/4) + 4 hf + j%4].
-  f32x16 sacc[2];
+  constexpr int ROWB = PrefillLds<D>::ROWB;
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
     sacc[kb2] = f32x16{};
-    const uint16_t *kp = Ks + (32 * kb2 + l32) * KS + 8 * hf;
+    const int r = 32 * kb2 + l32;
+    const char *rowp = Kb + r * ROWB;
+    const int sw = swz_k<D>(r);
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) sacc[kb2] = mfma32(as_bf16x8(ld16(kp + 16 * ks)), qf[ks], sacc[kb2]);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const u32x4 a = *reinterpret_cast<const u32x4 *>(rowp + (((2 * ks + hf) ^ sw) << 4));
+      sacc[kb2] = mfma32(as_bf16x8(a), qf[ks], sacc[kb2]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  constexpr bool PLAIN = !MASK && !BIAS;
+}
+
+// Bias of a 64-key tile for this lane's row, in the S^T accumulator layout:
+// rel_row[qa - t] for keys t in the band 0 <= qa - t < R, else 0.  The
+// index is clamped so every load is valid and the value is selected after,
+// which keeps the loads branch-free.
+__device__ __forceinline__ void tile_bias(float (*bias)[16], int kb, int qa, const float *rel_row, int R, int hf) {
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int d = qa - (kb + 32 * kb2 + 8 * (j >> 2) + 4 * hf + (j & 3));
+      const float v = rel_row[min(max(d, 0), R - 1)];
+      bias[kb2][j] = (unsigned)d < (unsigned)R ? v : 0.f;
+    }
+  }
+}
+
+// Row max of a score tile in log2 units.  The general form (edge or band
+// tiles) rewrites the tile in place as scale*s + bias (bias prefetched, zero
+// outside the band), -inf for keys this row may not see; the plain form
+// leaves it raw.
+template <bool GENERAL>
+__device__ __forceinline__ float tile_rowmax(f32x16 *sacc, int kb, int lo_r, int hi_r, int qa,
+                                             const float (*bias)[16], float c, bool pos_scale, int hf) {
   float mx = neg_inf();
-  if constexpr (PLAIN) {
+  if constexpr (!GENERAL) {
     if (pos_scale) {
       float ms = neg_inf();
 #pragma unroll
@@ -271,50 +327,61 @@ __device__ __forceinline__ void prefill_tile_step(const uint16_t *Ks, const uint
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int t = kb + 32 * kb2 + 8 * (j >> 2) + 4 * hf + (j & 3);
-        float v = sacc[kb2][j] * c;
-        if constexpr (BIAS) {
-          const int d = qa - t;
-          v = __builtin_fmaf((unsigned)d < (unsigned)R ? rel_row[d] : 0.f, kLog2e, v);
-        }
-        if constexpr (MASK) {
-          if (t < lo_r || t > hi_r) v = neg_inf();
-        }
+        float v = __builtin_fmaf(bias[kb2][j], kLog2e, sacc[kb2][j] * c);
+        if (t < lo_r || t > hi_r) v = neg_inf();
         sacc[kb2][j] = v;
         mx = fmaxf(mx, v);
       }
     }
   }
-  mx = xor32_max(mx);
-  if (__any(mx > m_run + kTau)) {
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = m_new == neg_inf() ? 1.f : exp2_fast(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-  }
-  const float m_use = m_run == neg_inf() ? 0.f : m_run;
+  return xor32_max(mx);
+}
+
+// P = exp2(cc*s - m) as bf16 PV operands (pb[c] covers keys 16c .. 16c+15 of
+// the tile in V^T slot order); returns this lane's part of the row sum.
+__device__ __forceinline__ float tile_exp(const f32x16 *sacc, float cc, float m_use, bf16x8 *pb) {
   float psum = 0.f;
-  bf16x8 pb[4];
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
+  for (int c4 = 0; c4 < 4; ++c4) {
     float pe[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float sv = sacc[cc >> 1][8 * (cc & 1) + i];
-      pe[i] = exp2_fast(PLAIN ? __builtin_fmaf(sv, c, -m_use) : sv - m_use);
+      pe[i] = exp2_fast(__builtin_fmaf(sacc[c4 >> 1][8 * (c4 & 1) + i], cc, -m_use));
       psum += pe[i];
     }
-    pb[cc] = pack8_bf16(pe);
+    pb[c4] = pack8_bf16(pe);
   }
-  l_run += psum;
+  return psum;
+}
+
+// O^T += V^T·P^T for a 64-key tile.  The V^T operand (row d = lane%32, eight
+// keys of slot order) is read from the row-major V tile by two transposing
+// reads: lane i of each 16-lane group addresses 4 head_dim values of one key,
+// lane j receives one head_dim value of four keys.
+template <int D>
+__device__ __forceinline__ void pv_tile(const char *Vb, const bf16x8 *pb, f32x16 *oacc, int lane) {
+  constexpr int DB = D / 32;
+  constexpr int ROWB = PrefillLds<D>::ROWB;
+  const int grp = lane >> 4, h = grp >> 1, dh = grp & 1;
+  const int k = (lane >> 2) & 3, q = lane & 3;
+  const int key_lo = 4 * h + k;           // + 16 c4 (+ 8 for slots 4..7)
+  const int sw = swz_v<D>(key_lo);       // same for key_lo + 16 c4 + 8
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
+  for (int c4 = 0; c4 < 4; ++c4) {
+    const char *r1 = Vb + (16 * c4 + key_lo) * ROWB;
+    const char *r2 = r1 + 8 * ROWB;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const bf16x8 a = as_bf16x8(ld16(Vt + (32 * db + l32) * VS + 16 * cc + 8 * hf));
-      oacc[db] = mfma32(a, pb[cc], oacc[db]);
+      const int d0 = 32 * db + 16 * dh + 4 * q;
+      const int off = (((d0 >> 3) ^ sw) << 4) + ((d0 & 7) << 1);
+      const s16x4 lo = lds_read_tr(r1 + off);
+      const s16x4 hi = lds_read_tr(r2 + off);
+      const u32x4 a = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                       __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+      oacc[db] = mfma32(as_bf16x8(a), pb[c4], oacc[db]);
     }
+    // Keep each chunk's operand reads next to its MFMAs (bounds live VGPRs).
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -322,19 +389,15 @@ template <int D>
 __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, char *smem) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int CH = D / 8;                          // 16-byte chunks per K/V row
-  constexpr int KPT = kTileKeys * CH / kThreads;     // staged keys per thread (4 or 2)
-  constexpr int NKG = kTileKeys / KPT;               // key groups per tile
-  constexpr int KS = PrefillLds<D>::KS;
-  constexpr int VS = PrefillLds<D>::VS;
-  static_assert(KPT == 4 || KPT == 2, "staging layout");
 
   const int b = it.b;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
-  const int tok0 = p.cu_seqlens_q[b];
-  const int lq = p.cu_seqlens_q[b + 1] - tok0;
-  const int lk = p.cache_seqlens[b];
+  // Per-request scalars (uniform: kept in SGPRs so the range arithmetic runs
+  // on the scalar unit).
+  const int tok0 = __builtin_amdgcn_readfirstlane(p.cu_seqlens_q[b]);
+  const int lq = __builtin_amdgcn_readfirstlane(p.cu_seqlens_q[b + 1]) - tok0;
+  const int lk = __builtin_amdgcn_readfirstlane(p.cache_seqlens[b]);
   const int G = p.G;
   const int nrows = lq * G;
   const int row0 = it.tile * kTileRows;
@@ -380,68 +443,100 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   float m_run = neg_inf(), l_run = 0.f;
 
   const int64_t tok_stride = (int64_t)p.Hkv * D;     // elements between consecutive slots
+  const uint32_t slot_bytes = (uint32_t)(tok_stride * 2);
   const int32_t *bt = p.block_table + (int64_t)b * p.P;
-  // K staging: 16-byte chunk dck of keys kgk*KPT .. +KPT-1 (chunk index fastest).
-  const int dck = tid % CH, kgk = tid / CH;
-  // V staging: key group fastest, so the transposed LDS writes spread over banks.
-  const int kgv = tid % NKG, dcv = tid / NKG;
-  u32x4 kreg[KPT], vreg[KPT];
-
-  auto page_of = [&](int key) { return key < kend ? bt[key / p.BS] : 0; };
-  auto load_rows = [&](const uint16_t *base, int key0, int page, int dc, u32x4 *regs) {
-    const int64_t off = (((int64_t)page * p.BS + key0 % p.BS) * p.Hkv + g) * D + dc * 8;
+  auto pidx = [&](int key) { return p.bs_shift >= 0 ? key >> p.bs_shift : key / p.BS; };
+  auto pslot = [&](int key) { return p.bs_shift >= 0 ? key & (p.BS - 1) : key % p.BS; };
+  // Staging: wave w fills rows 16w .. 16w+15 of each K and V tile (one
+  // 16-key block, hence one page) with direct buffer->LDS loads through a
+  // scalar buffer resource over the block's keys below kend; keys past it
+  // arrive as zeros.  Each load instruction writes 1 KB of LDS in lane order,
+  // RPI rows of UNITS 16-byte units; lane l brings the unit that the swizzle
+  // places at its position.
+  constexpr int UNITS = PrefillLds<D>::UNITS;
+  constexpr int ROWB = PrefillLds<D>::ROWB;
+  constexpr int RPI = 64 / UNITS;      // rows per load instruction
+  constexpr int NI = 16 / RPI;         // load instructions per wave per operand
+  const int kbw = 16 * w;
+  uint32_t voff_k[NI], voff_v[NI];
 #pragma unroll
-    for (int rr = 0; rr < KPT; ++rr) regs[rr] = (key0 + rr < kend) ? ld16(base + off + rr * tok_stride) : zero16();
+  for (int n = 0; n < NI; ++n) {
+    const int rr = RPI * n + lane / UNITS;  // row within the wave's block
+    const int pu = lane % UNITS;
+    voff_k[n] = (uint32_t)rr * slot_bytes + (uint32_t)((pu ^ swz_k<D>(kbw + rr)) << 4);
+    voff_v[n] = (uint32_t)rr * slot_bytes + (uint32_t)((pu ^ swz_v<D>(kbw + rr)) << 4);
+  }
+  auto page_of_tile = [&](int kb) { const int key = kb + kbw; return key < kend ? bt[pidx(key)] : 0; };
+  auto dma = [&](const uint16_t *cache, int kb, int page, int lds_off, const uint32_t *voff) {
+    const int key = kb + kbw;
+    const int nvalid = min(max(kend - key, 0), 16);
+    const int64_t off = (((int64_t)__builtin_amdgcn_readfirstlane(page) * p.BS + pslot(key)) * p.Hkv + g) * D;
+    const auto rs = make_rsrc(cache + off, (uint32_t)nvalid * slot_bytes);
+#pragma unroll
+    for (int n = 0; n < NI; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void *)(smem + lds_off + (kbw + RPI * n) * ROWB), 16, voff[n], 0, 0, 0);
   };
-  auto stage_store = [&](int buf) {
-    uint16_t *Ks = reinterpret_cast<uint16_t *>(smem + buf * PrefillLds<D>::bufBytes);
-    uint16_t *Vt = reinterpret_cast<uint16_t *>(smem + buf * PrefillLds<D>::bufBytes + PrefillLds<D>::kBytes);
-#pragma unroll
-    for (int rr = 0; rr < KPT; ++rr)
-      *reinterpret_cast<u32x4 *>(Ks + (kgk * KPT + rr) * KS + dck * 8) = kreg[rr];
-    const int pos = prefill_vpos(kgv * KPT);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint16_t *dst = Vt + (dcv * 8 + e) * VS + pos;
-      if constexpr (KPT == 4) {
-        *reinterpret_cast<u32x2 *>(dst) = u32x2{pair_elem(vreg[0], vreg[1], e), pair_elem(vreg[2], vreg[3], e)};
-      } else {
-        *reinterpret_cast<uint32_t *>(dst) = pair_elem(vreg[0], vreg[1], e);
-      }
-    }
-  };
+  // The LDS writes of direct loads are tracked by vmcnt only: wait for them
+  // before the barrier that publishes a tile.
+  auto wait_dma = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
 
-  if (t0 < t1) {
-    // Prologue: tile 0 into buffer 0; block-table entries of tile 1 in flight.
-    load_rows(p.k, t0 + kgk * KPT, page_of(t0 + kgk * KPT), dck, kreg);
-    load_rows(p.v, t0 + kgv * KPT, page_of(t0 + kgv * KPT), dcv, vreg);
-    int pgk = page_of(t0 + kTileKeys + kgk * KPT);
-    int pgv = page_of(t0 + kTileKeys + kgv * KPT);
-    stage_store(0);
+  // Tile j (keys t0 + 64 j ..) lives in K and V slot j%2.  While it is
+  // computed, the direct loads of tile j+1 fill the other slots and, when
+  // tile j+1 meets the bias band, this lane's bias values for it are loaded
+  // into registers, so neither latency sits on the critical path.
+  auto is_band = [&](int kb) { return p.R > 0 && kb <= band_hi && kb + kTileKeys - 1 >= band_lo; };
+  const int nt = t0 < t1 ? (t1 - t0 + kTileKeys - 1) / kTileKeys : 0;
+  if (nt > 0) {
+    float bias[2][16];
+    int pg1 = page_of_tile(t0 + kTileKeys);  // page of tile j+1
+    const int pg0 = page_of_tile(t0);
+    dma(p.k, t0, pg0, PrefillLds<D>::kOff(0), voff_k);
+    dma(p.v, t0, pg0, PrefillLds<D>::vOff(0), voff_v);
+    if (is_band(t0)) tile_bias(bias, t0, qa, rel_row, p.R, hf);
+    wait_dma();
     __syncthreads();
-    int buf = 0;
-    for (int kb = t0; kb < t1; kb += kTileKeys) {
-      const bool more = kb + kTileKeys < t1;
-      if (more) {
-        const int nk = kb + kTileKeys;
-        load_rows(p.k, nk + kgk * KPT, pgk, dck, kreg);
-        load_rows(p.v, nk + kgv * KPT, pgv, dcv, vreg);
-        pgk = page_of(nk + kTileKeys + kgk * KPT);
-        pgv = page_of(nk + kTileKeys + kgv * KPT);
+    for (int j = 0; j < nt; ++j) {
+      const int kb = t0 + j * kTileKeys;
+      const int pg2 = page_of_tile(kb + 2 * kTileKeys);
+      if (j + 1 < nt) {
+        dma(p.k, kb + kTileKeys, pg1, PrefillLds<D>::kOff((j + 1) & 1), voff_k);
+        dma(p.v, kb + kTileKeys, pg1, PrefillLds<D>::vOff((j + 1) & 1), voff_v);
       }
-      const uint16_t *Ks = reinterpret_cast<const uint16_t *>(smem + buf * PrefillLds<D>::bufBytes);
-      const uint16_t *Vt = reinterpret_cast<const uint16_t *>(smem + buf * PrefillLds<D>::bufBytes + PrefillLds<D>::kBytes);
+      f32x16 sacc[2];
+      qk_tile<D>(smem + PrefillLds<D>::kOff(j & 1), qf, sacc, l32, hf);
       const bool interior = kb >= in_lo && kb + kTileKeys - 1 <= in_hi;
-      const bool bias = p.R > 0 && kb <= band_hi && kb + kTileKeys - 1 >= band_lo;
-      // Two variants only: more inlined copies raise register pressure past
-      // the 256 VGPRs that two workgroups per CU allow.
-      if (interior && !bias)
-        prefill_tile_step<D, false, false>(Ks, Vt, qf, oacc, m_run, l_run, kb, lo_r, hi_r, qa, rel_row, p.R, c, pos_scale, l32, hf);
-      else
-        prefill_tile_step<D, true, true>(Ks, Vt, qf, oacc, m_run, l_run, kb, lo_r, hi_r, qa, rel_row, p.R, c, pos_scale, l32, hf);
-      if (more) stage_store(buf ^ 1);
+      const bool band = is_band(kb);
+      const bool plain = interior && !band;
+      float mx;
+      if (plain) {
+        mx = tile_rowmax<false>(sacc, kb, lo_r, hi_r, qa, bias, c, pos_scale, hf);
+      } else {
+        if (!band) {
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) bias[kb2][jj] = 0.f;
+        }
+        mx = tile_rowmax<true>(sacc, kb, lo_r, hi_r, qa, bias, c, pos_scale, hf);
+      }
+      if (j + 1 < nt && is_band(kb + kTileKeys)) tile_bias(bias, kb + kTileKeys, qa, rel_row, p.R, hf);
+      if (__any(mx > m_run + kTau)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == neg_inf() ? 1.f : exp2_fast(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      }
+      const float m_use = m_run == neg_inf() ? 0.f : m_run;
+      const float cc = plain ? c : 1.f;  // general tiles are already in log2 units
+      bf16x8 pb[4];
+      l_run += tile_exp(sacc, cc, m_use, pb);
+      pv_tile<D>(smem + PrefillLds<D>::vOff(j & 1), pb, oacc, lane);
+      wait_dma();
       __syncthreads();
-      buf ^= 1;
+      pg1 = pg2;
     }
   }
 
@@ -505,7 +600,10 @@ struct DecodeRegs {
   u32x4 v[D / 16];
 };
 
-template <int D>
+// NSET register sets form a ring: while block i is computed, the loads of
+// blocks i+1 .. i+NSET-1 (and, once block i's registers are consumed, of
+// block i+NSET) are in flight.
+template <int D, int NSET>
 __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, char *smem) {
   constexpr int QK = D / 32;       // 16x16x32 k-steps over head_dim
   constexpr int DB = D / 16;       // 16-row blocks of O^T
@@ -517,14 +615,16 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
   static_assert(KPL == 8 || KPL == 4, "staging layout");
 
   const int b = it.b;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15, q = lane >> 4;
   uint16_t *Vt = reinterpret_cast<uint16_t *>(smem) + w * D * VS;
   int32_t *pcache = reinterpret_cast<int32_t *>(smem + DecodeLds<D>::mainBytes + DecodeLds<D>::redMLBytes);
 
-  const int tok0 = p.cu_seqlens_q[b];
-  const int lq = p.cu_seqlens_q[b + 1] - tok0;
-  const int lk = p.cache_seqlens[b];
+  // Per-request scalars (uniform: kept in SGPRs so the range arithmetic runs
+  // on the scalar unit).
+  const int tok0 = __builtin_amdgcn_readfirstlane(p.cu_seqlens_q[b]);
+  const int lq = __builtin_amdgcn_readfirstlane(p.cu_seqlens_q[b + 1]) - tok0;
+  const int lk = __builtin_amdgcn_readfirstlane(p.cache_seqlens[b]);
   const int G = p.G;
   const int ncols = lq * G;
   const int col = c16 < ncols ? c16 : ncols - 1;  // idle columns shadow the last one
@@ -566,31 +666,50 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
   const int vg = lane % NG, vdc = lane / NG;
   int pfirst = 0;  // block-table index of pcache[0]
 
-  // Element offsets of slot 0 of the two 16-key blocks at `base`.
-  auto rows_of = [&](int base, int64_t *row0) {
+  // Buffer resources over the two 16-key blocks at `base`, one per cache:
+  // the page id is wave-uniform, so the address arithmetic runs on the
+  // scalar unit, and each resource covers only the block's keys below kend,
+  // so the hardware returns zeros for the rest.
+  struct BlockRsrc {
+    __amdgpu_buffer_rsrc_t k[2], v[2];
+  };
+  const uint32_t slot_bytes = (uint32_t)(tok_stride * 2);
+  auto rows_of = [&](int base, BlockRsrc &br) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const int kb = base + 16 * blk;
-      int page = 0;
-      if (kb < kend) page = pcache[kb / p.BS - pfirst];
-      row0[blk] = (((int64_t)page * p.BS + kb % p.BS) * p.Hkv + g) * D;
+      const int kb = __builtin_amdgcn_readfirstlane(base + 16 * blk);
+      const int nvalid = __builtin_amdgcn_readfirstlane(min(max(kend - kb, 0), 16));
+      int page = 0, slot0 = 0;
+      if (nvalid > 0) {
+        const int pidx = p.bs_shift >= 0 ? (kb >> p.bs_shift) : kb / p.BS;
+        slot0 = p.bs_shift >= 0 ? (kb & (p.BS - 1)) : kb % p.BS;
+        page = __builtin_amdgcn_readfirstlane(pcache[pidx - pfirst]);
+      }
+      const int64_t off = (((int64_t)page * p.BS + slot0) * p.Hkv + g) * D;
+      br.k[blk] = make_rsrc(p.k + off, (uint32_t)nvalid * slot_bytes);
+      br.v[blk] = make_rsrc(p.v + off, (uint32_t)nvalid * slot_bytes);
     }
   };
-  auto issue_k = [&](DecodeRegs<D> &Rg, const int64_t *row0, int base) {
+  // Per-lane byte offsets inside a block (fixed for the whole loop).
+  uint32_t koff[QK], voff[KPL];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int key = base + 16 * blk + c16;
-      const uint16_t *src = p.k + row0[blk] + c16 * tok_stride + q * DQ;
+  for (int ks = 0; ks < QK; ++ks) koff[ks] = c16 * slot_bytes + (uint32_t)(q * DQ + 8 * ks) * 2;
 #pragma unroll
-      for (int ks = 0; ks < QK; ++ks) Rg.k[blk][ks] = key < kend ? ld16(src + 8 * ks) : zero16();
-    }
+  for (int rr = 0; rr < KPL; ++rr) {
+    const int kr = decode_key_of_slot(vg * KPL + rr);
+    voff[rr] = (kr & 15) * slot_bytes + (uint32_t)vdc * 16;
+  }
+  auto issue_k = [&](DecodeRegs<D> &Rg, const BlockRsrc &br) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int ks = 0; ks < QK; ++ks) Rg.k[blk][ks] = bload16(br.k[blk], koff[ks]);
   };
-  auto issue_v = [&](DecodeRegs<D> &Rg, const int64_t *row0, int base) {
+  auto issue_v = [&](DecodeRegs<D> &Rg, const BlockRsrc &br) {
 #pragma unroll
     for (int rr = 0; rr < KPL; ++rr) {
       const int kr = decode_key_of_slot(vg * KPL + rr);
-      const int key = base + kr;
-      Rg.v[rr] = key < kend ? ld16(p.v + row0[kr >> 4] + (kr & 15) * tok_stride + vdc * 8) : zero16();
+      Rg.v[rr] = bload16(br.v[kr >> 4], voff[rr]);
     }
   };
 
@@ -601,8 +720,8 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr bool BIAS = decltype(bias_tag)::value;
     constexpr bool PLAIN = !MASK && !BIAS;
-    int64_t nrow0[2];
-    if (has_next) rows_of(nbase, nrow0);
+    BlockRsrc nbr;
+    if (has_next) rows_of(nbase, nbr);
     wave_lds_sync();
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -615,7 +734,7 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
         *reinterpret_cast<u32x2 *>(dst) = u32x2{pair_elem(Rg.v[0], Rg.v[1], e), pair_elem(Rg.v[2], Rg.v[3], e)};
       }
     }
-    if (has_next) issue_v(Rg, nrow0, nbase);
+    if (has_next) issue_v(Rg, nbr);
     f32x4 sacc[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -623,7 +742,7 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
 #pragma unroll
       for (int ks = 0; ks < QK; ++ks) sacc[blk] = mfma16(as_bf16x8(Rg.k[blk][ks]), qf[ks], sacc[blk]);
     }
-    if (has_next) issue_k(Rg, nrow0, nbase);
+    if (has_next) issue_k(Rg, nbr);
     // Lane (c16, q) holds S[col c16][key base + 16 blk + 4 q + j].
     float mx = neg_inf();
     if constexpr (PLAIN) {
@@ -711,17 +830,24 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
     __syncthreads();
     const int nblk = (sg1 - sg0 + kDecWaveKeys - 1) / kDecWaveKeys;
     const int my_n = nblk > w ? (nblk - w + 3) / 4 : 0;
-    DecodeRegs<D> Rg;
-    if (my_n > 0) {
-      int64_t row0[2];
-      const int base0 = sg0 + kDecWaveKeys * w;
-      rows_of(base0, row0);
-      issue_k(Rg, row0, base0);
-      issue_v(Rg, row0, base0);
+    DecodeRegs<D> Rg[NSET];
+#pragma unroll
+    for (int j = 0; j < NSET; ++j) {
+      if (j < my_n) {
+        BlockRsrc br;
+        rows_of(sg0 + kDecWaveKeys * (w + 4 * j), br);
+        issue_k(Rg[j], br);
+        issue_v(Rg[j], br);
+      }
     }
-    for (int i = 0; i < my_n; ++i) {
-      const int base = sg0 + kDecWaveKeys * (w + 4 * i);
-      step(Rg, base, base + kDecStep, i + 1 < my_n);
+    for (int i = 0; i < my_n; i += NSET) {
+#pragma unroll
+      for (int j = 0; j < NSET; ++j) {
+        if (i + j < my_n) {
+          const int base = sg0 + kDecWaveKeys * (w + 4 * (i + j));
+          step(Rg[j], base, base + NSET * kDecStep, i + j + NSET < my_n);
+        }
+      }
     }
   }
 
@@ -795,6 +921,8 @@ constexpr int attn_lds_bytes() {
 
 // DECODE_ONLY: every request of the batch has Lq*G <= 16 (known on the host
 // from max_seqlen_q), so the prefill path is not compiled in.
+// Two workgroups per CU for both variants (a deeper decode load ring at one
+// workgroup per CU measured slower).
 template <int D, bool DECODE_ONLY>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char smem[attn_lds_bytes<D, DECODE_ONLY>()];
@@ -804,10 +932,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnParams p) {
   const int g = rest % p.Hkv;
   const int item = rest / p.Hkv;
   const Item it = resolve_item(p, item, DECODE_ONLY);
-  if (it.kind == 2) {
-    decode_item<D>(p, it, g, s, smem);
+  const int kind = __builtin_amdgcn_readfirstlane(it.kind);
+  if (kind == 2) {
+    decode_item<D, 1>(p, it, g, s, smem);
   } else if constexpr (!DECODE_ONLY) {
-    if (it.kind == 1) prefill_item<D>(p, it, g, s, smem);
+    if (kind == 1) prefill_item<D>(p, it, g, s, smem);
   }
 }
 
