@@ -160,6 +160,7 @@ int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cach
   p.bs_shift = -1;
   for (int sh = 4; sh < 31; ++sh)
     if ((1 << sh) == block_size) p.bs_shift = sh;
+  p.scale = softmax_scale;
   p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
 
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -30,6 +30,7 @@ struct AttnParams {
   int32_t batch, num_tokens, H, Hkv, G, BS, R, S, P;
   int32_t left, right, causal;
   int32_t bs_shift;             // log2(BS) when BS is a power of two, else -1
+  float scale;                  // softmax_scale
   float scale_log2;             // softmax_scale * log2(e)
 };
 

@@ -128,6 +128,18 @@ template <bool B>
 struct BoolTag {
   static constexpr bool value = B;
 };
+template <int I>
+struct IntTag {
+  static constexpr int value = I;
+};
+// Calls f(IntTag<I>{}) for I = B .. E-1 (compile-time unrolled).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(IntTag<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 __device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
@@ -262,133 +274,230 @@ __device__ __forceinline__ s16x4 lds_read_tr(const char *addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(addr));
 }
 
-// S^T = K·Q^T for a 64-key tile: lane (l32, hf) gets
-// S[row l32][key 32 kb2 + 8 (j/4) + 4 hf + j%4] in sacc[kb2][j].
-template <int D>
-__device__ __forceinline__ void qk_tile(const char *Kb, const bf16x8 *qf, f32x16 *sacc, int l32, int hf) {
-  constexpr int KSTEPS = D / 16;
-  constexpr int ROWB = PrefillLds<D>::ROWB;
+// Raw bias values of a 64-key tile for this lane's row, in the S^T
+// accumulator layout: rel_row[qa - t] for the lane's keys t.  Band
+// membership is applied later by tile_init, so nothing waits on these loads
+// here.
+//
+// Fast form: the lane's keys come in eight groups of four consecutive keys,
+// i.e. four consecutive logits in descending order, fetched by one 16-byte
+// load each through a buffer resource over the tile's rel_logits rows plus a
+// margin of 4 values on either side.  A group that runs past its row's band
+// picks up values of the neighbouring row (or zeros past the resource) that
+// the band select discards; lane_base is the byte offset of the group of
+// keys kb - 3 .. kb of this lane, so offsets below the resource wrap and read
+// as zeros.
+__device__ __forceinline__ void tile_bias_load4(f32x16 *sacc, __amdgpu_buffer_rsrc_t rs, uint32_t lane_base, int kb) {
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
-    sacc[kb2] = f32x16{};
-    const int r = 32 * kb2 + l32;
-    const char *rowp = Kb + r * ROWB;
-    const int sw = swz_k<D>(r);
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const u32x4 a = *reinterpret_cast<const u32x4 *>(rowp + (((2 * ks + hf) ^ sw) << 4));
-      sacc[kb2] = mfma32(as_bf16x8(a), qf[ks], sacc[kb2]);
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const uint32_t voff = lane_base - 4u * (uint32_t)(kb + 32 * kb2 + 8 * g4);
+      const u32x4 v = bload16(rs, voff);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) sacc[kb2][4 * g4 + m] = __uint_as_float(v[3 - m]);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Bias of a 64-key tile for this lane's row, in the S^T accumulator layout:
-// rel_row[qa - t] for keys t in the band 0 <= qa - t < R, else 0.  The
-// index is clamped so every load is valid and the value is selected after,
-// which keeps the loads branch-free.
-__device__ __forceinline__ void tile_bias(float (*bias)[16], int kb, int qa, const float *rel_row, int R, int hf) {
+// Slow form, for tiles whose rows sit at either end of rel_logits (where the
+// margin of the fast form does not exist): clamped per-value loads.
+__device__ __forceinline__ void tile_bias_load(f32x16 *sacc, int kb, int qa, const float *rel_row, int R, int hf) {
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int d = qa - (kb + 32 * kb2 + 8 * (j >> 2) + 4 * hf + (j & 3));
-      const float v = rel_row[min(max(d, 0), R - 1)];
-      bias[kb2][j] = (unsigned)d < (unsigned)R ? v : 0.f;
+      sacc[kb2][j] = rel_row[min(max(d, 0), R - 1)];
     }
   }
 }
 
-// Row max of a score tile in log2 units.  The general form (edge or band
-// tiles) rewrites the tile in place as scale*s + bias (bias prefetched, zero
-// outside the band), -inf for keys this row may not see; the plain form
-// leaves it raw.
-template <bool GENERAL>
-__device__ __forceinline__ float tile_rowmax(f32x16 *sacc, int kb, int lo_r, int hi_r, int qa,
-                                             const float (*bias)[16], float c, bool pos_scale, int hf) {
+// Key offset, within a tile, of accumulator element (kb2, j) of a lane with
+// hf = 0 (lanes with hf = 1 hold keys 4 further on).
+__device__ __forceinline__ constexpr int key_of(int kb2, int j) { return 32 * kb2 + 8 * (j >> 2) + (j & 3); }
+
+// Per-lane bounds of one tile, relative to the lane's first key kb + 4 hf:
+// element keys k in [vis_lo, vis_hi] are visible, keys in [band_lo, band_hi]
+// get the bias.
+struct TileBounds {
+  int vis_lo, vis_hi, band_lo, band_hi;
+};
+
+// Initial value of the score accumulator of a general tile (a mask edge or
+// the bias band), so that the MFMA chain yields s + bias/scale directly:
+// bias/scale inside the band (sacc holds the raw loaded values when BAND),
+// 0 outside it, and masked (an infinity that the scaled exp2 sends to 0)
+// where the row may not see the key.
+template <bool BAND>
+__device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv_scale, float masked) {
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int k = key_of(kb2, j);
+      float v = 0.f;
+      if constexpr (BAND) v = (k >= tb.band_lo && k <= tb.band_hi) ? sacc[kb2][j] * inv_scale : 0.f;
+      sacc[kb2][j] = (k < tb.vis_lo || k > tb.vis_hi) ? masked : v;
+    }
+  }
+}
+
+// Row max of a tile in raw score units (the scale is positive).
+__device__ __forceinline__ float tile_rowmax(const f32x16 *sacc) {
   float mx = neg_inf();
-  if constexpr (!GENERAL) {
-    if (pos_scale) {
-      float ms = neg_inf();
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+  for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) ms = fmaxf(ms, sacc[kb2][j]);
-      mx = ms * c;
-    } else {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb2][j] * c);
-    }
-  } else {
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int t = kb + 32 * kb2 + 8 * (j >> 2) + 4 * hf + (j & 3);
-        float v = __builtin_fmaf(bias[kb2][j], kLog2e, sacc[kb2][j] * c);
-        if (t < lo_r || t > hi_r) v = neg_inf();
-        sacc[kb2][j] = v;
-        mx = fmaxf(mx, v);
-      }
-    }
-  }
-  return xor32_max(mx);
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb2][j]);
+  return mx;
 }
 
-// P = exp2(cc*s - m) as bf16 PV operands (pb[c] covers keys 16c .. 16c+15 of
-// the tile in V^T slot order); returns this lane's part of the row sum.
-__device__ __forceinline__ float tile_exp(const f32x16 *sacc, float cc, float m_use, bf16x8 *pb) {
+// S^T = K·Q^T (+ the initial sacc when INIT) for a 64-key tile: lane
+// (l32, hf) gets S[row l32][key 32 kb2 + 8 (j/4) + 4 hf + j%4] in
+// sacc[kb2][j].  The two 32-key halves are independent accumulation chains,
+// issued alternately.  Unit 2 ks + hf of row r sits at (2 ks + hf) ^ sw(r),
+// i.e. at byte offset off0 ^ 32 ks.
+template <int D, bool INIT>
+__device__ __forceinline__ void qk_mfma(const char *Kb, const bf16x8 *qf, f32x16 *sacc, int l32, int hf) {
+  constexpr int KSTEPS = D / 16;
+  constexpr int ROWB = PrefillLds<D>::ROWB;
+  const char *row = Kb + l32 * ROWB;  // row l32 + 32 shares the swizzle of row l32
+  const int off0 = (hf ^ swz_k<D>(l32)) << 4;
+  if constexpr (!INIT) {
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
+  }
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const int off = off0 ^ (ks << 5);
+    const u32x4 a0 = *reinterpret_cast<const u32x4 *>(row + off);
+    const u32x4 a1 = *reinterpret_cast<const u32x4 *>(row + 32 * ROWB + off);
+    sacc[0] = mfma32(as_bf16x8(a0), qf[ks], sacc[0]);
+    sacc[1] = mfma32(as_bf16x8(a1), qf[ks], sacc[1]);
+  }
+}
+
+// The two overlapped phases of a pipeline iteration.  Each is written out
+// in the order it should issue, in groups of one MFMA (32 cycles on the
+// matrix pipe), the LDS read of the operand needed a few MFMAs later, and a
+// slice of the other phase's VALU work; sched_barrier keeps the groups in
+// that order, so the wave issues VALU instructions while its MFMAs run.
+
+// Phase A: S^T(next) = K·Q^T (+ the initial sacc) on the MFMA pipe, and
+// P = exp2(c*s - m) of the current tile as bf16 PV operands (pb[c] covers keys
+// 16c .. 16c+15 in V^T slot order); returns this lane's part of the row sum.
+template <int D>
+__device__ __forceinline__ float phase_a(const char *Kb, const bf16x8 *qf, f32x16 *sn, const f32x16 *sc,
+                                         float c, float m_use, bf16x8 *pb, int l32, int hf) {
+  constexpr int KSTEPS = D / 16;
+  constexpr int NM = 2 * KSTEPS;     // MFMAs
+  constexpr int EPM = 32 / NM;       // exp elements per MFMA group
+  constexpr int AHEAD = 3;           // operand reads in flight
+  constexpr int ROWB = PrefillLds<D>::ROWB;
+  const char *row = Kb + l32 * ROWB;  // row l32 + 32 shares the swizzle of row l32
+  const int off0 = (hf ^ swz_k<D>(l32)) << 4;
+  u32x4 a[NM];
+  auto rd = [&](int i) __attribute__((always_inline)) {
+    a[i] = *reinterpret_cast<const u32x4 *>(row + (i & 1) * 32 * ROWB + (off0 ^ ((i >> 1) << 5)));
+  };
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) rd(i);
+  float pe[32];
   float psum = 0.f;
 #pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) {
-    float pe[8];
+  for (int i = 0; i < NM; ++i) {
+    sn[i & 1] = mfma32(as_bf16x8(a[i]), qf[i >> 1], sn[i & 1]);
+    if (i + AHEAD < NM) rd(i + AHEAD);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pe[i] = exp2_fast(__builtin_fmaf(sacc[c4 >> 1][8 * (c4 & 1) + i], cc, -m_use));
-      psum += pe[i];
+    for (int e = 0; e < EPM; ++e) {
+      const int x = i * EPM + e;
+      pe[x] = exp2_fast(__builtin_fmaf(sc[x >> 4][x & 15], c, -m_use));
+      psum += pe[x];
     }
-    pb[c4] = pack8_bf16(pe);
+    if (((i + 1) * EPM) % 8 == 0) {
+      const int c4 = (i + 1) * EPM / 8 - 1;
+      pb[c4] = pack8_bf16(&pe[8 * c4]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   return psum;
 }
 
-// O^T += V^T·P^T for a 64-key tile.  The V^T operand (row d = lane%32, eight
-// keys of slot order) is read from the row-major V tile by two transposing
-// reads: lane i of each 16-lane group addresses 4 head_dim values of one key,
-// lane j receives one head_dim value of four keys.
-template <int D>
-__device__ __forceinline__ void pv_tile(const char *Vb, const bf16x8 *pb, f32x16 *oacc, int lane) {
+// Phase B: O^T += V^T·P^T on the MFMA pipe (the V^T operand of row
+// d = lane%32 and eight slot-order keys comes from two transposing reads of
+// the row-major V tile), and the row max (raw units) of the next tile plus
+// the zeroing of the released register set sz on the VALU.
+//
+// The transposing reads are issued as inline asm: the compiler cannot tell
+// them apart from the direct loads in flight into the other V slot and would
+// wait for those (vmcnt(0)) before the first read.  Their completion is
+// awaited explicitly: each wait names the operand it guards, and LDS reads
+// complete in order, so lgkmcnt(n) with n = reads issued after the operand's
+// two is sufficient (other LGKM traffic only makes it stricter).
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr_asm(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
+  return v;
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait_for(u32x4 &a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
+}
+
+template <int D, int VOFF>
+__device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32x16 *oacc, int lane,
+                                         const f32x16 *sn, f32x16 *sz) {
   constexpr int DB = D / 32;
+  constexpr int NM = 4 * DB;
+  constexpr int EPM = 32 / NM;
+  constexpr int AHEAD = 3;
   constexpr int ROWB = PrefillLds<D>::ROWB;
   const int grp = lane >> 4, h = grp >> 1, dh = grp & 1;
   const int k = (lane >> 2) & 3, q = lane & 3;
   const int key_lo = 4 * h + k;           // + 16 c4 (+ 8 for slots 4..7)
   const int sw = swz_v<D>(key_lo);       // same for key_lo + 16 c4 + 8
+  // Per-lane address of head_dim block db; the slot, the 16-key chunk c4 and
+  // the +8 keys of the second read are immediate offsets.
+  uint32_t base[DB];
 #pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) {
-    const char *r1 = Vb + (16 * c4 + key_lo) * ROWB;
-    const char *r2 = r1 + 8 * ROWB;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d0 = 32 * db + 16 * dh + 4 * q;
-      const int off = (((d0 >> 3) ^ sw) << 4) + ((d0 & 7) << 1);
-      const s16x4 lo = lds_read_tr(r1 + off);
-      const s16x4 hi = lds_read_tr(r2 + off);
-      const u32x4 a = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                       __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
-      oacc[db] = mfma32(as_bf16x8(a), pb[c4], oacc[db]);
-    }
-    // Keep each chunk's operand reads next to its MFMAs (bounds live VGPRs).
-    __builtin_amdgcn_sched_barrier(0);
+  for (int db = 0; db < DB; ++db) {
+    const int d0 = 32 * db + 16 * dh + 4 * q;
+    base[db] = (uint32_t)(uintptr_t)smem + key_lo * ROWB + ((((d0 >> 3) ^ sw) << 4) + ((d0 & 7) << 1));
   }
+  u32x4 a[NM];
+  auto rd = [&](auto i_tag) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_tag)::value;
+    constexpr int c4 = i / DB, db = i % DB;
+    const u32x2 lo = lds_read_tr_asm<VOFF + 16 * c4 * ROWB>(base[db]);
+    const u32x2 hi = lds_read_tr_asm<VOFF + (16 * c4 + 8) * ROWB>(base[db]);
+    a[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  float mx = neg_inf();
+  static_for<0, AHEAD>([&](auto i_tag) __attribute__((always_inline)) { rd(i_tag); });
+  static_for<0, NM>([&](auto i_tag) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_tag)::value;
+    constexpr int newer = 2 * (NM - 1 - i < AHEAD - 1 ? NM - 1 - i : AHEAD - 1);
+    lgkm_wait_for<newer>(a[i]);
+    oacc[i % DB] = mfma32(as_bf16x8(a[i]), pb[i / DB], oacc[i % DB]);
+    if constexpr (i + AHEAD < NM) rd(IntTag<i + AHEAD>{});
+#pragma unroll
+    for (int e = 0; e < EPM; ++e) {
+      const int x = i * EPM + e;
+      mx = fmaxf(mx, sn[x >> 4][x & 15]);
+      sz[x >> 4][x & 15] = 0.f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  return mx;
 }
 
 template <int D>
 __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, char *smem) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
+  using L = PrefillLds<D>;
 
   const int b = it.b;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -413,7 +522,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   const int qa_max = row_last / G + lk - lq;
 
   const Range sr = split_range(visible_range(p, lk, qa_min, qa_max), it.kmax, p.S, s, kTileKeys);
-  const int t0 = sr.lo, t1 = sr.hi;
+  const int t0 = __builtin_amdgcn_readfirstlane(sr.lo), t1 = __builtin_amdgcn_readfirstlane(sr.hi);
   const int kend = min(lk, t1);  // keys at or past this are neither loaded nor visible
   // This lane's visible keys inside the split: [lo_r, hi_r].
   int lo_r = t0, hi_r = kend - 1;
@@ -425,16 +534,44 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   if (p.left >= 0) in_lo = max(in_lo, qa_max - p.left);
   if (p.causal) in_hi = min(in_hi, qa_min);
   if (p.right >= 0) in_hi = min(in_hi, qa_min + p.right);
-  const int band_lo = qa_min - p.R + 1, band_hi = qa_max;
+  in_lo = __builtin_amdgcn_readfirstlane(in_lo);
+  in_hi = __builtin_amdgcn_readfirstlane(in_hi);
+  const int band_lo = __builtin_amdgcn_readfirstlane(qa_min - p.R + 1);
+  const int band_hi = __builtin_amdgcn_readfirstlane(qa_max);
   const float *rel_row = p.R > 0 ? p.rel_logits + ((int64_t)tok * p.H + head) * p.R : nullptr;
-  const float c = p.scale_log2;
-  const bool pos_scale = c > 0.f;
+  // Fast bias loads: resource over rel_logits rows first .. last of this
+  // tile (row index tok * H + head) with a 4-value margin on either side.
+  const int64_t first_row = (int64_t)(tok0 + row0 / G) * p.H + g * G + row0 % G;
+  const int64_t last_row = (int64_t)(tok0 + row_last / G) * p.H + g * G + row_last % G;
+  const int64_t bias_lo = first_row * p.R - 4, bias_hi = (last_row + 1) * p.R + 4;
+  const bool bias_fast = p.R > 0 && bias_lo >= 0 && bias_hi <= (int64_t)p.num_tokens * p.H * p.R &&
+                         (bias_hi - bias_lo) * 4 < ((int64_t)1 << 31);
+  __amdgpu_buffer_rsrc_t bias_rs = make_rsrc(p.rel_logits, 0);
+  uint32_t bias_lane_base = 0;
+  if (bias_fast) {
+    bias_rs = make_rsrc(p.rel_logits + bias_lo, (uint32_t)((bias_hi - bias_lo) * 4));
+    const int64_t row_rel = ((int64_t)tok * p.H + head) * p.R - bias_lo;
+    bias_lane_base = (uint32_t)(4 * (row_rel + qa - 4 * hf - 3));
+  }
+  // The bias enters the score accumulator as bias/scale, and the scale is
+  // made positive: a negative scale negates Q instead (exact in bf16), and a
+  // scale below 2^-100 in magnitude is treated as 0 (its q·k term then
+  // changes no fp32 logit), which zeroes Q and leaves the bias alone.
+  const bool zero_scale = fabsf(p.scale) < 0x1p-100f;
+  const bool neg_scale = !zero_scale && p.scale < 0.f;
+  const float c = zero_scale ? kLog2e : fabsf(p.scale_log2);
+  const float inv_scale = zero_scale ? 1.f : 1.f / fabsf(p.scale);
+  const float masked = neg_inf();
 
   bf16x8 qf[KSTEPS];
   {
     const uint16_t *qp = p.q + ((int64_t)tok * p.H + head) * D + 8 * hf;
+    const uint32_t flip = neg_scale ? 0x80008000u : 0u;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = as_bf16x8(ld16(qp + 16 * ks));
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const u32x4 v = ld16(qp + 16 * ks);
+      qf[ks] = zero_scale ? bf16x8{} : as_bf16x8(u32x4{v[0] ^ flip, v[1] ^ flip, v[2] ^ flip, v[3] ^ flip});
+    }
   }
 
   f32x16 oacc[DB];
@@ -444,6 +581,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
 
   const int64_t tok_stride = (int64_t)p.Hkv * D;     // elements between consecutive slots
   const uint32_t slot_bytes = (uint32_t)(tok_stride * 2);
+  const uint64_t page_bytes = (uint64_t)p.BS * slot_bytes;
   const int32_t *bt = p.block_table + (int64_t)b * p.P;
   auto pidx = [&](int key) { return p.bs_shift >= 0 ? key >> p.bs_shift : key / p.BS; };
   auto pslot = [&](int key) { return p.bs_shift >= 0 ? key & (p.BS - 1) : key % p.BS; };
@@ -453,8 +591,8 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   // arrive as zeros.  Each load instruction writes 1 KB of LDS in lane order,
   // RPI rows of UNITS 16-byte units; lane l brings the unit that the swizzle
   // places at its position.
-  constexpr int UNITS = PrefillLds<D>::UNITS;
-  constexpr int ROWB = PrefillLds<D>::ROWB;
+  constexpr int UNITS = L::UNITS;
+  constexpr int ROWB = L::ROWB;
   constexpr int RPI = 64 / UNITS;      // rows per load instruction
   constexpr int NI = 16 / RPI;         // load instructions per wave per operand
   const int kbw = 16 * w;
@@ -466,77 +604,156 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     voff_k[n] = (uint32_t)rr * slot_bytes + (uint32_t)((pu ^ swz_k<D>(kbw + rr)) << 4);
     voff_v[n] = (uint32_t)rr * slot_bytes + (uint32_t)((pu ^ swz_v<D>(kbw + rr)) << 4);
   }
-  auto page_of_tile = [&](int kb) { const int key = kb + kbw; return key < kend ? bt[pidx(key)] : 0; };
-  auto dma = [&](const uint16_t *cache, int kb, int page, int lds_off, const uint32_t *voff) {
+  // Page ids of this wave's 16-key block for a window of 64 tiles, one per
+  // lane, read back with readlane (no memory access in the loop); the next
+  // window is loaded 64 tiles ahead.
+  auto load_pages = [&](int tile0) {
+    const int key = t0 + (tile0 + lane) * kTileKeys + kbw;
+    return key < kend ? bt[pidx(key)] : 0;
+  };
+  int pc_base = 0;
+  int pc = load_pages(0);
+  int pc_next = load_pages(64);
+  auto page_t = [&](int jt) { return __builtin_amdgcn_readlane(pc, jt - pc_base); };
+  const char *kcache = reinterpret_cast<const char *>(p.k) + (uint64_t)g * D * 2;
+  const char *vcache = reinterpret_cast<const char *>(p.v) + (uint64_t)g * D * 2;
+  auto dma = [&](const char *cache, int kb, int page, int lds_off, const uint32_t *voff) __attribute__((always_inline)) {
     const int key = kb + kbw;
     const int nvalid = min(max(kend - key, 0), 16);
-    const int64_t off = (((int64_t)__builtin_amdgcn_readfirstlane(page) * p.BS + pslot(key)) * p.Hkv + g) * D;
-    const auto rs = make_rsrc(cache + off, (uint32_t)nvalid * slot_bytes);
+    const char *src = cache + (uint64_t)(uint32_t)page * page_bytes + (uint64_t)(uint32_t)pslot(key) * slot_bytes;
+    const auto rs = make_rsrc(src, (uint32_t)nvalid * slot_bytes);
 #pragma unroll
     for (int n = 0; n < NI; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (__attribute__((address_space(3))) void *)(smem + lds_off + (kbw + RPI * n) * ROWB), 16, voff[n], 0, 0, 0);
   };
   // The LDS writes of direct loads are tracked by vmcnt only: wait for them
-  // before the barrier that publishes a tile.
-  auto wait_dma = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+  // before the barrier that publishes a tile.  When the 32 bias loads of a
+  // later tile were issued after them, those may stay in flight.
+  auto wait_vm0 = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
+  auto wait_vm8 = [&]() { __builtin_amdgcn_s_waitcnt(0x0F78); };   // vmcnt(8)
+  auto wait_vm32 = [&]() { __builtin_amdgcn_s_waitcnt(0x8F70); };  // vmcnt(32)
+  auto load_bias = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
+    if (bias_fast) tile_bias_load4(sacc, bias_rs, bias_lane_base, kb);
+    else tile_bias_load(sacc, kb, qa, rel_row, p.R, hf);
+  };
 
-  // Tile j (keys t0 + 64 j ..) lives in K and V slot j%2.  While it is
-  // computed, the direct loads of tile j+1 fill the other slots and, when
-  // tile j+1 meets the bias band, this lane's bias values for it are loaded
-  // into registers, so neither latency sits on the critical path.
   auto is_band = [&](int kb) { return p.R > 0 && kb <= band_hi && kb + kTileKeys - 1 >= band_lo; };
+  auto is_plain = [&](int kb) { return kb >= in_lo && kb + kTileKeys - 1 <= in_hi && !is_band(kb); };
+  auto bounds = [&](int kb) {
+    const int off = kb + 4 * hf;
+    return TileBounds{lo_r - off, hi_r - off, qa - p.R + 1 - off, qa - off};
+  };
+  // Lazy max update after the row max mx of a tile: O and l are rescaled
+  // only when some row's max grew by more than kTau.
+  auto update_max = [&](float mx) __attribute__((always_inline)) {
+    if (__any(mx > m_run + kTau)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == neg_inf() ? 1.f : exp2_fast(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+  };
+
   const int nt = t0 < t1 ? (t1 - t0 + kTileKeys - 1) / kTileKeys : 0;
   if (nt > 0) {
-    float bias[2][16];
-    int pg1 = page_of_tile(t0 + kTileKeys);  // page of tile j+1
-    const int pg0 = page_of_tile(t0);
-    dma(p.k, t0, pg0, PrefillLds<D>::kOff(0), voff_k);
-    dma(p.v, t0, pg0, PrefillLds<D>::vOff(0), voff_v);
-    if (is_band(t0)) tile_bias(bias, t0, qa, rel_row, p.R, hf);
-    wait_dma();
-    __syncthreads();
-    for (int j = 0; j < nt; ++j) {
-      const int kb = t0 + j * kTileKeys;
-      const int pg2 = page_of_tile(kb + 2 * kTileKeys);
-      if (j + 1 < nt) {
-        dma(p.k, kb + kTileKeys, pg1, PrefillLds<D>::kOff((j + 1) & 1), voff_k);
-        dma(p.v, kb + kTileKeys, pg1, PrefillLds<D>::vOff((j + 1) & 1), voff_v);
-      }
-      f32x16 sacc[2];
-      qk_tile<D>(smem + PrefillLds<D>::kOff(j & 1), qf, sacc, l32, hf);
-      const bool interior = kb >= in_lo && kb + kTileKeys - 1 <= in_hi;
-      const bool band = is_band(kb);
-      const bool plain = interior && !band;
-      float mx;
-      if (plain) {
-        mx = tile_rowmax<false>(sacc, kb, lo_r, hi_r, qa, bias, c, pos_scale, hf);
-      } else {
-        if (!band) {
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) bias[kb2][jj] = 0.f;
-        }
-        mx = tile_rowmax<true>(sacc, kb, lo_r, hi_r, qa, bias, c, pos_scale, hf);
-      }
-      if (j + 1 < nt && is_band(kb + kTileKeys)) tile_bias(bias, kb + kTileKeys, qa, rel_row, p.R, hf);
-      if (__any(mx > m_run + kTau)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_new == neg_inf() ? 1.f : exp2_fast(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      }
-      const float m_use = m_run == neg_inf() ? 0.f : m_run;
-      const float cc = plain ? c : 1.f;  // general tiles are already in log2 units
-      bf16x8 pb[4];
-      l_run += tile_exp(sacc, cc, m_use, pb);
-      pv_tile<D>(smem + PrefillLds<D>::vOff(j & 1), pb, oacc, lane);
-      wait_dma();
+    // Software pipeline over 64-key tiles.  Tile j's K sits in K slot j%2,
+    // its V in V slot j%2, its scores in register set j%2 (sa or sb).  While
+    // tile j is in flight:
+    //   phase A: exp of tile j on the VALU, QK of tile j+1 on the MFMA pipe;
+    //   phase B: PV of tile j on the MFMA pipe, row max of tile j+1 on the
+    //            VALU;
+    // the direct loads of K(j+2) and V(j+1) and the raw bias of tile j+2
+    // (into the register set tile j just freed) are in flight, and one
+    // barrier ends the iteration.  A general tile's bias and masks are put
+    // into its accumulator before its QK, so every tile's softmax is the same.
+    f32x16 sa[2], sb[2];
+    bf16x8 pb[4];
+    // Page ids: pg_v of tile j+1 and pg_k of tile j+2 at the top of iteration j.
+    int pg_v = page_t(1);
+    int pg_k = page_t(2);
+    // Accumulator start of tile kb in set sacc, in two steps: begin() right
+    // after the set is released (raw bias loads for a band tile, the masks
+    // of an edge tile; a plain tile's set was zeroed), finish() once those
+    // loads have landed (band tiles only).
+    auto begin = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
+      if (is_band(kb)) load_bias(sacc, kb);
+      else if (!is_plain(kb)) tile_init<false>(sacc, bounds(kb), inv_scale, masked);
+    };
+    auto finish = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
+      if (is_band(kb)) tile_init<true>(sacc, bounds(kb), inv_scale, masked);
+    };
+    auto zero = [&](f32x16 *sacc) __attribute__((always_inline)) {
+      sacc[0] = f32x16{};
+      sacc[1] = f32x16{};
+    };
+    {
+      const int pg0 = page_t(0);
+      dma(kcache, t0, pg0, L::kOff(0), voff_k);
+      dma(vcache, t0, pg0, L::vOff(0), voff_v);
+      if (nt > 1) dma(kcache, t0 + kTileKeys, pg_v, L::kOff(1), voff_k);
+      zero(sa);
+      begin(sa, t0);
+      wait_vm0();
       __syncthreads();
-      pg1 = pg2;
+      finish(sa, t0);
+      qk_mfma<D, true>(smem + L::kOff(0), qf, sa, l32, hf);
+      update_max(xor32_max(tile_rowmax(sa) * c));
+      zero(sb);
+      if (nt > 1) begin(sb, t0 + kTileKeys);
+      // Iteration 0 refills K slot 0: every wave must be done reading K(0).
+      __syncthreads();
+    }
+
+    // One pipeline iteration; PAR = j % 2 selects slots and register sets.
+    // Both phases are branch-free; on the last tile the QK (of a K slot the
+    // direct loads zero-filled) and the row max are computed and dropped.
+    // The direct loads are issued on every iteration (past the split they
+    // fill slots already consumed with zeros), so the number of loads in
+    // flight is the same on every path.
+    auto iteration = [&](auto par_tag, int j, f32x16 *cur, f32x16 *nxt) __attribute__((always_inline)) {
+      constexpr int PAR = decltype(par_tag)::value ? 1 : 0;
+      const int kb = t0 + j * kTileKeys;
+      const bool has_next = j + 1 < nt;
+      // Direct loads: K(j+2) into K slot PAR (K(j) was consumed before the
+      // last barrier), V(j+1) into V slot 1-PAR.
+      dma(kcache, kb + 2 * kTileKeys, pg_k, L::kOff(PAR), voff_k);
+      dma(vcache, kb + kTileKeys, pg_v, L::vOff(1 - PAR), voff_v);
+      if (has_next) finish(nxt, kb + kTileKeys);
+      if (j + 3 - pc_base == 64) {
+        pc = pc_next;
+        pc_base += 64;
+        pc_next = load_pages(pc_base + 64);
+      }
+      pg_v = pg_k;
+      pg_k = page_t(j + 3);
+      const float m_use = m_run == neg_inf() ? 0.f : m_run;
+      __builtin_amdgcn_sched_barrier(0);
+      // Phase A: QK of tile j+1 (MFMA) || exp of tile j (VALU).
+      l_run += phase_a<D>(smem + L::kOff(1 - PAR), qf, nxt, cur, c, m_use, pb, l32, hf);
+      // Phase B: PV of tile j (MFMA) || row max of tile j+1, zeroing of the
+      // set tile j released (VALU).
+      const float mx = phase_b<D, L::vOff(PAR)>(smem, pb, oacc, lane, nxt, cur) * c;
+      // Start tile j+2 in the released set, then the barrier that publishes
+      // K(j+2) and V(j+1).  Band tiles' raw bias loads may stay in flight.
+      if (j + 2 < nt && is_band(kb + 2 * kTileKeys)) {
+        load_bias(cur, kb + 2 * kTileKeys);
+        __builtin_amdgcn_sched_barrier(0);
+        if (bias_fast) wait_vm8();
+        else wait_vm32();
+      } else {
+        if (j + 2 < nt) begin(cur, kb + 2 * kTileKeys);
+        wait_vm0();
+      }
+      __syncthreads();
+      if (has_next) update_max(xor32_max(mx));
+    };
+
+    for (int j = 0; j < nt; j += 2) {
+      iteration(BoolTag<false>{}, j, sa, sb);
+      if (j + 1 < nt) iteration(BoolTag<true>{}, j + 1, sb, sa);
     }
   }
 

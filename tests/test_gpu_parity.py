@@ -104,6 +104,20 @@ def test_small_cases(name, S):
     _compare(out, lse, *ref, tag=f"{name} S={S}")
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 1e-35, 0.3])
+@pytest.mark.parametrize("D", [64, 128])
+def test_softmax_scale_signs(scale, D):
+    """Negative, zero and vanishing scales (the prefill path folds the bias
+    into the score accumulator as bias/scale and handles these by negating or
+    zeroing Q) and a large one, on prefill and decode rows with the bias band."""
+    w = wl.build([90, 1, 1], [200, 150, 70], num_heads=8, num_kv_heads=2, head_dim=D, rel_extent=48,
+                 softmax_scale=scale, seed=31, extra_pages=2, poison=True)
+    ref = _oracle(w)
+    for S in (1, 2):
+        out, lse = _gpu_run(w.to("cuda"), S)
+        _compare(out, lse, *ref, tag=f"scale={scale} D={D} S={S}")
+
+
 def test_many_splits_with_short_ranges():
     """More splits than key tiles: most splits are empty and give (0, -inf)
     partials that the combine must ignore."""
