@@ -274,19 +274,28 @@ __device__ __forceinline__ s16x4 lds_read_tr(const char *addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(addr));
 }
 
+// Key offset, within a tile, of accumulator element (kb2, j) of a lane with
+// hf = 0 (lanes with hf = 1 hold keys 4 further on).  K and V rows are staged
+// with the keys of every group of four in reverse order (row r holds key
+// rev4(r)), so element j%4 = m of a group holds key 3 - m of it.
+__device__ __forceinline__ constexpr int rev4(int r) { return (r & ~3) + 3 - (r & 3); }
+__device__ __forceinline__ constexpr int key_of(int kb2, int j) { return 32 * kb2 + 8 * (j >> 2) + 3 - (j & 3); }
+
 // Raw bias values of a 64-key tile for this lane's row, in the S^T
 // accumulator layout: rel_row[qa - t] for the lane's keys t.  Band
 // membership is applied later by tile_init, so nothing waits on these loads
 // here.
 //
 // Fast form: the lane's keys come in eight groups of four consecutive keys,
-// i.e. four consecutive logits in descending order, fetched by one 16-byte
-// load each through a buffer resource over the tile's rel_logits rows plus a
-// margin of 4 values on either side.  A group that runs past its row's band
-// picks up values of the neighbouring row (or zeros past the resource) that
-// the band select discards; lane_base is the byte offset of the group of
-// keys kb - 3 .. kb of this lane, so offsets below the resource wrap and read
-// as zeros.
+// i.e. four consecutive logits, fetched by one 16-byte load each through a
+// buffer resource over the tile's rel_logits rows plus a margin of 4 values
+// on either side.  A group that runs past its row's band picks up values of
+// the neighbouring row (or zeros past the resource) that the band select
+// discards.  lane_base is the byte offset of this lane's logit at distance
+// qa - 4 hf - 3, the lowest distance of its first group when kb = 0; offsets
+// below the resource wrap and read as zeros.  With the reversed key order of
+// a group, memory order is element order, so the loads land in place and
+// nothing waits on them here.
 __device__ __forceinline__ void tile_bias_load4(f32x16 *sacc, __amdgpu_buffer_rsrc_t rs, uint32_t lane_base, int kb) {
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -295,7 +304,7 @@ __device__ __forceinline__ void tile_bias_load4(f32x16 *sacc, __amdgpu_buffer_rs
       const uint32_t voff = lane_base - 4u * (uint32_t)(kb + 32 * kb2 + 8 * g4);
       const u32x4 v = bload16(rs, voff);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) sacc[kb2][4 * g4 + m] = __uint_as_float(v[3 - m]);
+      for (int m = 0; m < 4; ++m) sacc[kb2][4 * g4 + m] = __uint_as_float(v[m]);
     }
   }
 }
@@ -307,15 +316,12 @@ __device__ __forceinline__ void tile_bias_load(f32x16 *sacc, int kb, int qa, con
   for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int d = qa - (kb + 32 * kb2 + 8 * (j >> 2) + 4 * hf + (j & 3));
+      const int d = qa - (kb + key_of(kb2, j) + 4 * hf);
       sacc[kb2][j] = rel_row[min(max(d, 0), R - 1)];
     }
   }
 }
 
-// Key offset, within a tile, of accumulator element (kb2, j) of a lane with
-// hf = 0 (lanes with hf = 1 hold keys 4 further on).
-__device__ __forceinline__ constexpr int key_of(int kb2, int j) { return 32 * kb2 + 8 * (j >> 2) + (j & 3); }
 
 // Per-lane bounds of one tile, relative to the lane's first key kb + 4 hf:
 // element keys k in [vis_lo, vis_hi] are visible, keys in [band_lo, band_hi]
@@ -601,8 +607,8 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   for (int n = 0; n < NI; ++n) {
     const int rr = RPI * n + lane / UNITS;  // row within the wave's block
     const int pu = lane % UNITS;
-    voff_k[n] = (uint32_t)rr * slot_bytes + (uint32_t)((pu ^ swz_k<D>(kbw + rr)) << 4);
-    voff_v[n] = (uint32_t)rr * slot_bytes + (uint32_t)((pu ^ swz_v<D>(kbw + rr)) << 4);
+    voff_k[n] = (uint32_t)rev4(rr) * slot_bytes + (uint32_t)((pu ^ swz_k<D>(kbw + rr)) << 4);
+    voff_v[n] = (uint32_t)rev4(rr) * slot_bytes + (uint32_t)((pu ^ swz_v<D>(kbw + rr)) << 4);
   }
   // Page ids of this wave's 16-key block for a window of 64 tiles, one per
   // lane, read back with readlane (no memory access in the loop); the next
