@@ -335,16 +335,55 @@ struct TileBounds {
 // bias/scale inside the band (sacc holds the raw loaded values when BAND),
 // 0 outside it, and masked (an infinity that the scaled exp2 sends to 0)
 // where the row may not see the key.
-template <bool BAND>
+// Number of a lane's 32 accumulator elements, counted in the order of their
+// key offsets, whose offset (without the 4 hf shift) is below x.  Element
+// (kb2, j) holds offset 32 kb2 + 8 (j/4) + 3 - j%4, so sorted by offset the
+// elements run (kb2, 4 g + 3), (kb2, 4 g + 2), ...
+__device__ __forceinline__ int elems_below(int x) {
+  x = min(max(x, 0), 64);
+  return 16 * (x >> 5) + 4 * ((x >> 3) & 3) + min(x & 7, 4);
+}
+// Bitmap over that order: bit i set iff the i-th element's offset is in [lo, hi].
+__device__ __forceinline__ uint32_t range_bits(int lo, int hi) {
+  const int a = elems_below(lo), b = elems_below(min(hi, 64) + 1);
+  return b > a ? (uint32_t)((1ull << b) - (1ull << a)) : 0u;
+}
+// Bit position, in that order, of element (kb2, j).
+__device__ __forceinline__ constexpr int order_of(int kb2, int j) { return 16 * kb2 + (j & ~3) + 3 - (j & 3); }
+// All-ones if bit pos of bits is set, else 0 (v_bfe_i32), and the bitwise
+// select (m & a) | (~m & b) (v_bfi_b32); as asm so they stay single
+// instructions instead of per-element compares.
+__device__ __forceinline__ uint32_t bit_mask(uint32_t bits, int pos) {
+  uint32_t r;
+  asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(r) : "v"(bits), "i"(pos));
+  return r;
+}
+__device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  return r;
+}
+
+// Accumulator start of a general tile.  FULL: every key of the tile is in
+// every row's band and visible to it, so only the scaling remains.
+template <bool BAND, bool FULL = false>
 __device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv_scale, float masked) {
+  if constexpr (FULL) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) sacc[kb2] *= inv_scale;
+    return;
+  }
+  const uint32_t vis = range_bits(tb.vis_lo, tb.vis_hi);
+  const uint32_t band = BAND ? range_bits(tb.band_lo, tb.band_hi) : 0u;
+  const uint32_t mbits = __float_as_uint(masked);
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int k = key_of(kb2, j);
-      float v = 0.f;
-      if constexpr (BAND) v = (k >= tb.band_lo && k <= tb.band_hi) ? sacc[kb2][j] * inv_scale : 0.f;
-      sacc[kb2][j] = (k < tb.vis_lo || k > tb.vis_hi) ? masked : v;
+      const int pos = order_of(kb2, j);
+      uint32_t v = 0u;
+      if constexpr (BAND) v = __float_as_uint(sacc[kb2][j] * inv_scale) & bit_mask(band, pos);
+      sacc[kb2][j] = __uint_as_float(bit_select(bit_mask(vis, pos), v, mbits));
     }
   }
 }
@@ -610,12 +649,18 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     voff_k[n] = (uint32_t)rev4(rr) * slot_bytes + (uint32_t)((pu ^ swz_k<D>(kbw + rr)) << 4);
     voff_v[n] = (uint32_t)rev4(rr) * slot_bytes + (uint32_t)((pu ^ swz_v<D>(kbw + rr)) << 4);
   }
+  // Tiles are visited from the top of the range down: tile jt starts at key
+  // tile_kb(jt), so the diagonal and the bias band come first.
+  const int nt = t0 < t1 ? (t1 - t0 + kTileKeys - 1) / kTileKeys : 0;
+  const int t_top = t0 + (nt - 1) * kTileKeys;
+  auto tile_kb = [&](int jt) { return t_top - jt * kTileKeys; };
   // Page ids of this wave's 16-key block for a window of 64 tiles, one per
   // lane, read back with readlane (no memory access in the loop); the next
   // window is loaded 64 tiles ahead.
-  auto load_pages = [&](int tile0) {
-    const int key = t0 + (tile0 + lane) * kTileKeys + kbw;
-    return key < kend ? bt[pidx(key)] : 0;
+  auto load_pages = [&](int jt0) {
+    const int jt = jt0 + lane;
+    const int key = tile_kb(jt) + kbw;
+    return jt < nt && key < kend ? bt[pidx(key)] : 0;
   };
   int pc_base = 0;
   int pc = load_pages(0);
@@ -623,9 +668,11 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   auto page_t = [&](int jt) { return __builtin_amdgcn_readlane(pc, jt - pc_base); };
   const char *kcache = reinterpret_cast<const char *>(p.k) + (uint64_t)g * D * 2;
   const char *vcache = reinterpret_cast<const char *>(p.v) + (uint64_t)g * D * 2;
-  auto dma = [&](const char *cache, int kb, int page, int lds_off, const uint32_t *voff) __attribute__((always_inline)) {
-    const int key = kb + kbw;
-    const int nvalid = min(max(kend - key, 0), 16);
+  // Direct loads of tile jt (zeros past the last tile).
+  auto dma = [&](const char *cache, int jt, int page, int lds_off, const uint32_t *voff) __attribute__((always_inline)) {
+    const bool live = jt < nt;
+    const int key = (live ? tile_kb(jt) : t0) + kbw;
+    const int nvalid = live ? min(max(kend - key, 0), 16) : 0;
     const char *src = cache + (uint64_t)(uint32_t)page * page_bytes + (uint64_t)(uint32_t)pslot(key) * slot_bytes;
     const auto rs = make_rsrc(src, (uint32_t)nvalid * slot_bytes);
 #pragma unroll
@@ -646,6 +693,10 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
 
   auto is_band = [&](int kb) { return p.R > 0 && kb <= band_hi && kb + kTileKeys - 1 >= band_lo; };
   auto is_plain = [&](int kb) { return kb >= in_lo && kb + kTileKeys - 1 <= in_hi && !is_band(kb); };
+  // Every key of the tile visible to, and in the band of, every row.
+  const int full_lo = __builtin_amdgcn_readfirstlane(max(in_lo, qa_max - p.R + 1));
+  const int full_hi = __builtin_amdgcn_readfirstlane(min(in_hi, qa_min));
+  auto is_full_band = [&](int kb) { return kb >= full_lo && kb + kTileKeys - 1 <= full_hi; };
   auto bounds = [&](int kb) {
     const int off = kb + 4 * hf;
     return TileBounds{lo_r - off, hi_r - off, qa - p.R + 1 - off, qa - off};
@@ -663,7 +714,6 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     }
   };
 
-  const int nt = t0 < t1 ? (t1 - t0 + kTileKeys - 1) / kTileKeys : 0;
   if (nt > 0) {
     // Software pipeline over 64-key tiles.  Tile j's K sits in K slot j%2,
     // its V in V slot j%2, its scores in register set j%2 (sa or sb).  While
@@ -689,7 +739,10 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       else if (!is_plain(kb)) tile_init<false>(sacc, bounds(kb), inv_scale, masked);
     };
     auto finish = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
-      if (is_band(kb)) tile_init<true>(sacc, bounds(kb), inv_scale, masked);
+      if (is_band(kb)) {
+        if (is_full_band(kb)) tile_init<true, true>(sacc, bounds(kb), inv_scale, masked);
+        else tile_init<true>(sacc, bounds(kb), inv_scale, masked);
+      }
     };
     auto zero = [&](f32x16 *sacc) __attribute__((always_inline)) {
       sacc[0] = f32x16{};
@@ -697,18 +750,36 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     };
     {
       const int pg0 = page_t(0);
-      dma(kcache, t0, pg0, L::kOff(0), voff_k);
-      dma(vcache, t0, pg0, L::vOff(0), voff_v);
-      if (nt > 1) dma(kcache, t0 + kTileKeys, pg_v, L::kOff(1), voff_k);
+      dma(kcache, 0, pg0, L::kOff(0), voff_k);
+      dma(vcache, 0, pg0, L::vOff(0), voff_v);
+      dma(kcache, 1, pg_v, L::kOff(1), voff_k);
       zero(sa);
-      begin(sa, t0);
+      begin(sa, tile_kb(0));
+      // The band tiles come first: pull this wave's rel_logits rows into the
+      // cache now, while the first tiles load, with dword direct loads whose
+      // LDS writes land in V slot 1 (unused until iteration 0).  Line i of
+      // row r is fetched by lane (i + r * LPR) % 64 of load (i + r * LPR) / 64.
+      if (bias_fast && band_hi >= t0 && band_lo < t1) {
+        const int lpr = (p.R * 4 + 127) / 128 + 1;  // 128-byte lines per row
+        const int nload = (32 * lpr + 63) / 64;
+        for (int n = 0; n < nload; ++n) {
+          const int ln = 64 * n + lane;
+          const int rw = ln / lpr;  // row of this wave's 32
+          int rr = min(row0 + 32 * w + rw, row_last);
+          const int tk = tok0 + rr / G, hd = g * G + rr % G;
+          const int64_t off = ((int64_t)tk * p.H + hd) * p.R * 4 - bias_lo * 4 + 128 * (ln - rw * lpr);
+          const uint32_t voff = rw < 32 ? (uint32_t)off : 0xFFFFFFF0u;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              bias_rs, (__attribute__((address_space(3))) void *)(smem + L::vOff(1) + 256 * w), 4, voff, 0, 0, 0);
+        }
+      }
       wait_vm0();
       __syncthreads();
-      finish(sa, t0);
+      finish(sa, tile_kb(0));
       qk_mfma<D, true>(smem + L::kOff(0), qf, sa, l32, hf);
       update_max(xor32_max(tile_rowmax(sa) * c));
       zero(sb);
-      if (nt > 1) begin(sb, t0 + kTileKeys);
+      if (nt > 1) begin(sb, tile_kb(1));
       // Iteration 0 refills K slot 0: every wave must be done reading K(0).
       __syncthreads();
     }
@@ -721,13 +792,13 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     // flight is the same on every path.
     auto iteration = [&](auto par_tag, int j, f32x16 *cur, f32x16 *nxt) __attribute__((always_inline)) {
       constexpr int PAR = decltype(par_tag)::value ? 1 : 0;
-      const int kb = t0 + j * kTileKeys;
+      const int kb = tile_kb(j);
       const bool has_next = j + 1 < nt;
       // Direct loads: K(j+2) into K slot PAR (K(j) was consumed before the
       // last barrier), V(j+1) into V slot 1-PAR.
-      dma(kcache, kb + 2 * kTileKeys, pg_k, L::kOff(PAR), voff_k);
-      dma(vcache, kb + kTileKeys, pg_v, L::vOff(1 - PAR), voff_v);
-      if (has_next) finish(nxt, kb + kTileKeys);
+      dma(kcache, j + 2, pg_k, L::kOff(PAR), voff_k);
+      dma(vcache, j + 1, pg_v, L::vOff(1 - PAR), voff_v);
+      if (has_next) finish(nxt, tile_kb(j + 1));
       if (j + 3 - pc_base == 64) {
         pc = pc_next;
         pc_base += 64;
@@ -744,13 +815,13 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       const float mx = phase_b<D, L::vOff(PAR)>(smem, pb, oacc, lane, nxt, cur) * c;
       // Start tile j+2 in the released set, then the barrier that publishes
       // K(j+2) and V(j+1).  Band tiles' raw bias loads may stay in flight.
-      if (j + 2 < nt && is_band(kb + 2 * kTileKeys)) {
-        load_bias(cur, kb + 2 * kTileKeys);
+      if (j + 2 < nt && is_band(tile_kb(j + 2))) {
+        load_bias(cur, tile_kb(j + 2));
         __builtin_amdgcn_sched_barrier(0);
         if (bias_fast) wait_vm8();
         else wait_vm32();
       } else {
-        if (j + 2 < nt) begin(cur, kb + 2 * kTileKeys);
+        if (j + 2 < nt) begin(cur, tile_kb(j + 2));
         wait_vm0();
       }
       __syncthreads();
