@@ -428,6 +428,10 @@ __device__ __forceinline__ void qk_mfma(const char *Kb, const bf16x8 *qf, f32x16
 // matrix pipe), the LDS read of the operand needed a few MFMAs later, and a
 // slice of the other phase's VALU work; sched_barrier keeps the groups in
 // that order, so the wave issues VALU instructions while its MFMAs run.
+// Values that are only consumed after the phase (partial sums, partial
+// maxima, zeroed registers) are pinned inside their group: otherwise the
+// compiler sinks their arithmetic to the point of use, after the MFMAs.
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 
 // Phase A: S^T(next) = K·Q^T (+ the initial sacc) on the MFMA pipe, and
 // P = exp2(c*s - m) of the current tile as bf16 PV operands (pb[c] covers keys
@@ -446,27 +450,48 @@ __device__ __forceinline__ float phase_a(const char *Kb, const bf16x8 *qf, f32x1
   auto rd = [&](int i) __attribute__((always_inline)) {
     a[i] = *reinterpret_cast<const u32x4 *>(row + (i & 1) * 32 * ROWB + (off0 ^ ((i >> 1) << 5)));
   };
+  // The exp work is skewed over the groups so that no instruction waits on
+  // the one just before it: group i scales the elements of group i+2, takes
+  // exp2 of those of group i+1 and sums those of group i (two partial sums).
+  float pe[32];
+  float psum[2] = {0.f, 0.f};
+  auto fma_g = [&](int gi) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < EPM; ++e) {
+      const int x = gi * EPM + e;
+      pe[x] = __builtin_fmaf(sc[x >> 4][x & 15], c, -m_use);
+    }
+  };
+  auto exp_g = [&](int gi) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < EPM; ++e) pe[gi * EPM + e] = exp2_fast(pe[gi * EPM + e]);
+  };
+  auto sum_g = [&](int gi) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < EPM; ++e) psum[e & 1] += pe[gi * EPM + e];
+    pin(psum[0]);
+    if (EPM > 1) pin(psum[1]);
+    if (((gi + 1) * EPM) % 8 == 0) {
+      const int c4 = (gi + 1) * EPM / 8 - 1;
+      pb[c4] = pack8_bf16(&pe[8 * c4]);
+    }
+  };
 #pragma unroll
   for (int i = 0; i < AHEAD; ++i) rd(i);
-  float pe[32];
-  float psum = 0.f;
+  fma_g(0);
+  fma_g(1);
+  exp_g(0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NM; ++i) {
     sn[i & 1] = mfma32(as_bf16x8(a[i]), qf[i >> 1], sn[i & 1]);
     if (i + AHEAD < NM) rd(i + AHEAD);
-#pragma unroll
-    for (int e = 0; e < EPM; ++e) {
-      const int x = i * EPM + e;
-      pe[x] = exp2_fast(__builtin_fmaf(sc[x >> 4][x & 15], c, -m_use));
-      psum += pe[x];
-    }
-    if (((i + 1) * EPM) % 8 == 0) {
-      const int c4 = (i + 1) * EPM / 8 - 1;
-      pb[c4] = pack8_bf16(&pe[8 * c4]);
-    }
+    if (i + 2 < NM) fma_g(i + 2);
+    if (i + 1 < NM) exp_g(i + 1);
+    sum_g(i);
     __builtin_amdgcn_sched_barrier(0);
   }
-  return psum;
+  return psum[0] + psum[1];
 }
 
 // Phase B: O^T += V^T·P^T on the MFMA pipe (the V^T operand of row
@@ -519,7 +544,8 @@ __device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32
     const u32x2 hi = lds_read_tr_asm<VOFF + (16 * c4 + 8) * ROWB>(base[db]);
     a[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
-  float mx = neg_inf();
+  // Four partial maxima keep the max chain from serialising the groups.
+  float mx[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
   static_for<0, AHEAD>([&](auto i_tag) __attribute__((always_inline)) { rd(i_tag); });
   static_for<0, NM>([&](auto i_tag) __attribute__((always_inline)) {
     constexpr int i = decltype(i_tag)::value;
@@ -530,12 +556,15 @@ __device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32
 #pragma unroll
     for (int e = 0; e < EPM; ++e) {
       const int x = i * EPM + e;
-      mx = fmaxf(mx, sn[x >> 4][x & 15]);
-      sz[x >> 4][x & 15] = 0.f;
+      mx[i & 3] = fmaxf(mx[i & 3], sn[x >> 4][x & 15]);
+      float z = 0.f;
+      pin(z);
+      sz[x >> 4][x & 15] = z;
     }
+    pin(mx[i & 3]);
     __builtin_amdgcn_sched_barrier(0);
   });
-  return mx;
+  return fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
 }
 
 template <int D>
