@@ -160,7 +160,8 @@ def main(argv=None):
     ap.add_argument("--only", default=None, help="run one workload: batched_decode, chunked_prefill, "
                                                   "long_decode, continuous_batch")
     ap.add_argument("--splits", type=int, default=None,
-                    help="override the planner's num_splits for the headline decode batch")
+                    help="override the planner's num_splits for the headline decode batch "
+                         "(or for long_decode with --only long_decode)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -215,6 +216,8 @@ def main(argv=None):
         if a.only in (None, "long_decode"):
             w4 = wl.long_decode(device=dev)
             S4 = bnd.rpa_choose_splits(1, 1, w4.num_heads, w4.num_kv_heads, max(w4.k_lens))
+            if a.splits and a.only == "long_decode":
+                S4 = a.splits
             r4 = Runner(w4, S4)
             ms, ms_c, wk = measure(r4, max(5, a.steps // 2), a.warmup)
             results["long_decode"] = (w4, S4, ms, ms_c, wk)

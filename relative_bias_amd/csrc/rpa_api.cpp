@@ -41,11 +41,14 @@ size_t rpa_workspace_bytes(int32_t num_splits, int32_t num_tokens, int32_t num_h
   return round_up(part_lse_offset(num_splits, num_tokens, num_heads, head_dim) + n * sizeof(float), kAlign);
 }
 
-// Planner: work items are (request, q-tile, kv head); the split count is
-// raised until the grid offers about four workgroups per CU (decode) or two
-// (prefill-shaped batches), never below 512 keys per split and never above
-// RPA_MAX_SPLITS.  A window bounds the keys a row sees, so local attention
-// is not split, as in the walkthrough's inkling_fa4_num_splits.
+// Planner: work items are (request, q-tile, kv head).  A decode batch that
+// already offers a workgroup per CU is not split (a CU streams KV at a
+// bounded rate, so more, shorter workgroups only add per-workgroup start-up
+// and the combine); otherwise the split count is raised until the grid
+// offers about four workgroups per CU (decode) or two (prefill-shaped
+// batches), never below 512 keys per split and never above RPA_MAX_SPLITS.
+// A window bounds the keys a row sees, so local attention is not split, as
+// in the walkthrough's inkling_fa4_num_splits.
 int rpa_choose_splits(int32_t batch, int32_t max_seqlen_q, int32_t num_heads, int32_t num_kv_heads,
                       int64_t max_seqlen_k, int is_local, int32_t num_cus) {
   if (batch < 0 || max_seqlen_q < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_seqlen_k < 0 ||
@@ -57,6 +60,7 @@ int rpa_choose_splits(int32_t batch, int32_t max_seqlen_q, int32_t num_heads, in
   const int64_t items = rpa::items_for_request(max_seqlen_q, G);
   const bool decode = G <= rpa::kDecCols && (int64_t)max_seqlen_q * G <= rpa::kDecCols;
   const int64_t base = (int64_t)batch * num_kv_heads * items;
+  if (decode && base >= num_cus) return 1;
   const int64_t target = (decode ? 4 : 2) * (int64_t)num_cus;
   int64_t s = (target + base - 1) / base;
   const int64_t by_len = max_seqlen_k / 512;

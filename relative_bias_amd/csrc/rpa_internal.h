@@ -13,7 +13,6 @@ constexpr int kTileRows = 128;     // prefill q-tile: (token, head) rows of one 
 constexpr int kTileKeys = 64;      // prefill KV tile
 constexpr int kDecCols = 16;       // decode item: up to 16 (token, head) columns
 constexpr int kDecWaveKeys = 32;   // keys per wave per decode iteration
-constexpr int kDecStep = 4 * kDecWaveKeys;  // keys per workgroup per decode iteration
 
 struct AttnParams {
   const uint16_t *q;            // bf16 [T, H, D]

@@ -41,6 +41,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -899,13 +900,14 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
 
 // ----------------------------------------------------------------- decode
 
-template <int D>
+// NW waves per decode workgroup.
+template <int D, int NW>
 struct DecodeLds {
   static constexpr int VS = kDecWaveKeys + 8;              // V^T row stride (bf16): 80 B
-  static constexpr int vtBytes = 4 * D * VS * 2;           // one V^T tile per wave
-  static constexpr int redOBytes = 4 * D * kDecCols * 4;   // per-wave O^T partials
+  static constexpr int vtBytes = NW * D * VS * 2;          // one V^T tile per wave
+  static constexpr int redOBytes = NW * D * kDecCols * 4;  // per-wave O^T partials
   static constexpr int mainBytes = vtBytes > redOBytes ? vtBytes : redOBytes;
-  static constexpr int redMLBytes = 2 * 4 * kDecCols * 4;  // per-wave m and l
+  static constexpr int redMLBytes = 2 * NW * kDecCols * 4; // per-wave m and l
   static constexpr int pageBytes = kPageCache * 4;
   static constexpr int bytes = mainBytes + redMLBytes + pageBytes;
 };
@@ -926,22 +928,24 @@ struct DecodeRegs {
 // NSET register sets form a ring: while block i is computed, the loads of
 // blocks i+1 .. i+NSET-1 (and, once block i's registers are consumed, of
 // block i+NSET) are in flight.
-template <int D, int NSET>
+template <int D, int NSET, int NW>
 __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, char *smem) {
+  using DL = DecodeLds<D, NW>;
+  constexpr int STEP = NW * kDecWaveKeys;  // keys per workgroup per iteration
   constexpr int QK = D / 32;       // 16x16x32 k-steps over head_dim
   constexpr int DB = D / 16;       // 16-row blocks of O^T
   constexpr int DQ = D / 4;        // head_dim span of one lane group in K operands
   constexpr int CH = D / 8;        // 16-byte chunks per row
   constexpr int NG = 64 / CH;      // lane groups per chunk in V staging
   constexpr int KPL = kDecWaveKeys / NG;  // V keys per lane (8 or 4)
-  constexpr int VS = DecodeLds<D>::VS;
+  constexpr int VS = DL::VS;
   static_assert(KPL == 8 || KPL == 4, "staging layout");
 
   const int b = it.b;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15, q = lane >> 4;
   uint16_t *Vt = reinterpret_cast<uint16_t *>(smem) + w * D * VS;
-  int32_t *pcache = reinterpret_cast<int32_t *>(smem + DecodeLds<D>::mainBytes + DecodeLds<D>::redMLBytes);
+  int32_t *pcache = reinterpret_cast<int32_t *>(smem + DL::mainBytes + DL::redMLBytes);
 
   // Per-request scalars (uniform: kept in SGPRs so the range arithmetic runs
   // on the scalar unit).
@@ -957,7 +961,7 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
   const int qa = qi + lk - lq;
   const int qa_min = lk - lq;
   const int qa_max = (ncols - 1) / G + lk - lq;
-  const Range sr = split_range(visible_range(p, lk, qa_min, qa_max), it.kmax, p.S, s, kDecStep);
+  const Range sr = split_range(visible_range(p, lk, qa_min, qa_max), it.kmax, p.S, s, STEP);
   const int t0 = sr.lo, t1 = sr.hi;
   const int kend = min(lk, t1);
   int lo_c = t0, hi_c = kend - 1;
@@ -1138,27 +1142,27 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
   };
 
   // The split is walked in segments whose block-table entries fit the LDS
-  // page cache.  Inside a segment, wave w takes 32-key blocks w, w + 4, ...
+  // page cache.  Inside a segment, wave w takes 32-key blocks w, w + NW, ...
   // with the loads of its next block in flight while the current one is
   // computed.
-  const int seg_keys = ((kPageCache - 2) * p.BS) / kDecStep * kDecStep;
+  const int seg_keys = ((kPageCache - 2) * p.BS) / STEP * STEP;
   for (int sg0 = t0; sg0 < t1; sg0 += seg_keys) {
     const int sg1 = min(t1, sg0 + seg_keys);
     __syncthreads();  // every wave is done with the previous segment's pages
     if (sg0 < kend) {
       pfirst = sg0 / p.BS;
       const int np = (min(sg1, kend) - 1) / p.BS - pfirst + 1;
-      for (int i = tid; i < np; i += kThreads) pcache[i] = bt[pfirst + i];
+      for (int i = tid; i < np; i += 64 * NW) pcache[i] = bt[pfirst + i];
     }
     __syncthreads();
     const int nblk = (sg1 - sg0 + kDecWaveKeys - 1) / kDecWaveKeys;
-    const int my_n = nblk > w ? (nblk - w + 3) / 4 : 0;
+    const int my_n = nblk > w ? (nblk - w + NW - 1) / NW : 0;
     DecodeRegs<D> Rg[NSET];
 #pragma unroll
     for (int j = 0; j < NSET; ++j) {
       if (j < my_n) {
         BlockRsrc br;
-        rows_of(sg0 + kDecWaveKeys * (w + 4 * j), br);
+        rows_of(sg0 + kDecWaveKeys * (w + NW * j), br);
         issue_k(Rg[j], br);
         issue_v(Rg[j], br);
       }
@@ -1167,19 +1171,19 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
 #pragma unroll
       for (int j = 0; j < NSET; ++j) {
         if (i + j < my_n) {
-          const int base = sg0 + kDecWaveKeys * (w + 4 * (i + j));
-          step(Rg[j], base, base + NSET * kDecStep, i + j + NSET < my_n);
+          const int base = sg0 + kDecWaveKeys * (w + NW * (i + j));
+          step(Rg[j], base, base + NSET * STEP, i + j + NSET < my_n);
         }
       }
     }
   }
 
-  // Merge the four waves' (m, l, O^T) through LDS.
+  // Merge the NW waves' (m, l, O^T) through LDS.
   const float l_col = xor32_sum(xor16_sum(l_run));
   __syncthreads();
-  float *red_o = reinterpret_cast<float *>(smem);  // [4][D][16]
-  float *red_m = reinterpret_cast<float *>(smem + DecodeLds<D>::mainBytes);
-  float *red_l = red_m + 4 * kDecCols;
+  float *red_o = reinterpret_cast<float *>(smem);  // [NW][D][16]
+  float *red_m = reinterpret_cast<float *>(smem + DL::mainBytes);
+  float *red_l = red_m + NW * kDecCols;
   if (q == 0) {
     red_m[w * kDecCols + c16] = m_run;
     red_l[w * kDecCols + c16] = l_col;
@@ -1190,19 +1194,19 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
     for (int j = 0; j < 4; ++j) red_o[(w * D + 16 * db + 4 * q + j) * kDecCols + c16] = oacc[db][j];
   }
   __syncthreads();
-  constexpr int DPG = D / 16;  // head_dim values per thread in the merge
+  constexpr int DPG = D / (4 * NW);  // head_dim values per thread in the merge
   const int fc = tid & 15, fg = tid >> 4;
   if (fc >= ncols) return;
-  float mw[4], sc[4];
+  float mw[NW], sc[NW];
   float M = neg_inf();
 #pragma unroll
-  for (int ww = 0; ww < 4; ++ww) {
+  for (int ww = 0; ww < NW; ++ww) {
     mw[ww] = red_m[ww * kDecCols + fc];
     M = fmaxf(M, mw[ww]);
   }
   float L = 0.f;
 #pragma unroll
-  for (int ww = 0; ww < 4; ++ww) {
+  for (int ww = 0; ww < NW; ++ww) {
     sc[ww] = mw[ww] == neg_inf() ? 0.f : exp2_fast(mw[ww] - M);
     L += sc[ww] * red_l[ww * kDecCols + fc];
   }
@@ -1214,7 +1218,7 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
     const int d = fg * DPG + e;
     float acc = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) acc += sc[ww] * red_o[(ww * D + d) * kDecCols + fc];
+    for (int ww = 0; ww < NW; ++ww) acc += sc[ww] * red_o[(ww * D + d) * kDecCols + fc];
     o[e] = acc * inv;
   }
   const int fqi = fc / G;
@@ -1225,29 +1229,41 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
     if constexpr (DPG == 8) {
       *reinterpret_cast<u32x4 *>(op) = u32x4{pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3]),
                                              pack2_bf16(o[4], o[5]), pack2_bf16(o[6], o[7])};
-    } else {
+    } else if constexpr (DPG == 4) {
       *reinterpret_cast<u32x2 *>(op) = u32x2{pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3])};
+    } else {
+      *reinterpret_cast<uint32_t *>(op) = pack2_bf16(o[0], o[1]);
     }
     if (fg == 0 && p.lse) p.lse[(int64_t)ftok * p.H + fhead] = lse_v;
   } else {
     float *pp = p.part_out + (((int64_t)s * p.num_tokens + ftok) * p.H + fhead) * D + fg * DPG;
+    if constexpr (DPG >= 4) {
 #pragma unroll
-    for (int e = 0; e < DPG; e += 4) *reinterpret_cast<f32x4 *>(pp + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
+      for (int e = 0; e < DPG; e += 4) *reinterpret_cast<f32x4 *>(pp + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
+    } else {
+      *reinterpret_cast<f32x2 *>(pp) = f32x2{o[0], o[1]};
+    }
     if (fg == 0) p.part_lse[((int64_t)s * p.num_tokens + ftok) * p.H + fhead] = lse_v;
   }
 }
 
+// Waves per workgroup (four for both variants: a decode workgroup of eight
+// waves, one per CU, streamed no faster than two of four, since a CU's
+// outstanding misses, not its waves, bound its KV rate).
+template <bool DECODE_ONLY>
+constexpr int attn_waves() { return 4; }
+
 template <int D, bool DECODE_ONLY>
 constexpr int attn_lds_bytes() {
-  return (DECODE_ONLY || PrefillLds<D>::bytes < DecodeLds<D>::bytes) ? DecodeLds<D>::bytes : PrefillLds<D>::bytes;
+  using DL = DecodeLds<D, attn_waves<DECODE_ONLY>()>;
+  return (DECODE_ONLY || PrefillLds<D>::bytes < DL::bytes) ? DL::bytes : PrefillLds<D>::bytes;
 }
 
 // DECODE_ONLY: every request of the batch has Lq*G <= 16 (known on the host
-// from max_seqlen_q), so the prefill path is not compiled in.
-// Two workgroups per CU for both variants (a deeper decode load ring at one
-// workgroup per CU measured slower).
+// from max_seqlen_q), so the prefill path is not compiled in.  Both variants
+// hold two workgroups, i.e. two waves per SIMD, per CU.
 template <int D, bool DECODE_ONLY>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * attn_waves<DECODE_ONLY>(), 2) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char smem[attn_lds_bytes<D, DECODE_ONLY>()];
   const int bid = blockIdx.x;
   const int s = bid % p.S;
@@ -1257,7 +1273,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnParams p) {
   const Item it = resolve_item(p, item, DECODE_ONLY);
   const int kind = __builtin_amdgcn_readfirstlane(it.kind);
   if (kind == 2) {
-    decode_item<D, 1>(p, it, g, s, smem);
+    decode_item<D, 1, attn_waves<DECODE_ONLY>()>(p, it, g, s, smem);
   } else if constexpr (!DECODE_ONLY) {
     if (kind == 1) prefill_item<D>(p, it, g, s, smem);
   }
@@ -1306,7 +1322,7 @@ hipError_t launch_attention(const AttnParams &p, int head_dim, int64_t n_items_u
                             hipStream_t stream) {
   const int64_t blocks = n_items_ub * p.Hkv * p.S;
   if (blocks <= 0) return hipSuccess;
-  const dim3 grid((unsigned)blocks), block(kThreads);
+  const dim3 grid((unsigned)blocks), block(decode_only ? 64 * attn_waves<true>() : 64 * attn_waves<false>());
   if (head_dim == 128) {
     if (decode_only) hipLaunchKernelGGL((attn_kernel<128, true>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((attn_kernel<128, false>), grid, block, 0, stream, p);

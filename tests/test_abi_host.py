@@ -139,3 +139,9 @@ def test_planner_properties(L, B, maxq, H, Hkv, maxk):
 def test_planner_long_context_decode_uses_many_splits(L):
     assert bnd.rpa_choose_splits(1, 1, 64, 8, 1 << 20) >= 16
     assert bnd.rpa_choose_splits(8, 2048, 32, 8, 6144) == 1
+
+
+def test_planner_does_not_split_a_decode_batch_that_fills_the_chip(L):
+    # 32 requests x 8 kv heads = 256 workgroups: one per CU already.
+    assert L.rpa_choose_splits(32, 1, 32, 8, 8192, 0, 256) == 1
+    assert L.rpa_choose_splits(32, 1, 32, 8, 8192, 0, 512) > 1
