@@ -70,7 +70,11 @@ typedef enum {
  *                  cu[batch] = num_tokens.
  *   max_seqlen_q   must be >= every Lq.  It only bounds the launch grid: a
  *                  larger value changes nothing, a smaller one drops work.
- *   softmax_scale  multiplies <q, k>; the bias is added after scaling.
+ *   softmax_scale  multiplies <q, k>; the bias is added after scaling.  Any finite
+ *                  value, including 0 and negative values; a scale below 2^-100 in
+ *                  magnitude is treated as 0 (its q.k term changes no fp32 logit).
+ *                  The prefill kernel carries the bias as bias / scale, so
+ *                  |rel_logits| must stay below 2^27.
  *   causal         nonzero = bottom-right causal mask.
  *   window_left,
  *   window_right   sliding window; -1 leaves that side unbounded.
