@@ -160,7 +160,7 @@ def main(argv=None):
     ap.add_argument("--only", default=None, help="run one workload: batched_decode, chunked_prefill, "
                                                   "long_decode, continuous_batch")
     ap.add_argument("--splits", type=int, default=None,
-                    help="override the planner's num_splits for the headline decode batch "
+                    help="override the planner's num_splits (0 = balanced decode) for the headline decode batch "
                          "(or for long_decode with --only long_decode)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (for scaling the "
@@ -198,7 +198,7 @@ def main(argv=None):
     if run_main:
         w = wl.batched_decode(device="cpu").to(dev)
         S = bnd.rpa_choose_splits(w.batch, 1, w.num_heads, w.num_kv_heads, max(w.k_lens))
-        if a.splits:
+        if a.splits is not None:
             S = a.splits
         r = Runner(w, S, pools=3)
         ms, ms_c, wk = measure(r, a.steps, a.warmup)
@@ -216,7 +216,7 @@ def main(argv=None):
         if a.only in (None, "long_decode"):
             w4 = wl.long_decode(device=dev)
             S4 = bnd.rpa_choose_splits(1, 1, w4.num_heads, w4.num_kv_heads, max(w4.k_lens))
-            if a.splits and a.only == "long_decode":
+            if a.splits is not None and a.only == "long_decode":
                 S4 = a.splits
             r4 = Runner(w4, S4)
             ms, ms_c, wk = measure(r4, max(5, a.steps // 2), a.warmup)
@@ -259,7 +259,12 @@ def main(argv=None):
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
         value, unit = wk["bytes"] / ms / 1e6, "GB/s"
-    roof["kernel"] = "attn_kernel<128>"
+    if S == 0:
+        # Balanced decode: the attention kernel and the combine of the pairs
+        # cut between workgroups; kernel_ms is the whole step (both kernels).
+        roof["kernel"] = "decode_balanced_kernel<128> + combine_balanced_kernel<128>"
+    else:
+        roof["kernel"] = "attn_kernel<128>"
     roof["kernel_ms"] = round(kernel_ms, 5)
     roof["alg_bytes_per_launch"] = wk["bytes"]
     roof["traffic"] = load_traffic(head)

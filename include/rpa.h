@@ -46,7 +46,7 @@ typedef enum {
   RPA_ERR_NULL = -1,        /* a required pointer is NULL                         */
   RPA_ERR_SHAPE = -2,       /* inconsistent or negative sizes                     */
   RPA_ERR_UNSUPPORTED = -3, /* head_dim not 64/128, block_size not a multiple of 16 */
-  RPA_ERR_WORKSPACE = -4,   /* num_splits > 1 and the workspace is missing/small  */
+  RPA_ERR_WORKSPACE = -4,   /* num_splits != 1 and the workspace is missing/small */
   RPA_ERR_HIP = -5          /* a HIP launch failed                                */
 } rpa_status;
 
@@ -80,13 +80,19 @@ typedef enum {
  *   window_right   sliding window; -1 leaves that side unbounded.
  *   rel_extent     R >= 0; 0 means no bias (rel_logits may then be NULL).
  *   rel_logits     fp32 [num_tokens, num_heads, R].
- *   num_splits     S in [1, RPA_MAX_SPLITS]: each work item's visible key
- *                  range is cut into S contiguous chunks whose partial results
- *                  are merged by the log-sum-exp combine.  rpa_choose_splits
- *                  gives a default.  Any S gives the same result up to fp32
- *                  rounding.
+ *   num_splits     S in [0, RPA_MAX_SPLITS].  S >= 1: each work item's
+ *                  visible key range is cut into S contiguous chunks whose
+ *                  partial results are merged by the log-sum-exp combine.
+ *                  S = 0, balanced: when every request has Lq * G <= 16 (known
+ *                  from max_seqlen_q), batch <= 2048 and rel_logits spans
+ *                  less than 2 GiB, the 16-key blocks of the whole batch are
+ *                  dealt out in equal contiguous shares, one per compute unit
+ *                  of the current device, and the pieces of a (request, kv
+ *                  head) cut between shares are merged by the same combine;
+ *                  otherwise S = 0 runs as S = 1.  rpa_choose_splits gives a
+ *                  default.  Any S gives the same result up to fp32 rounding.
  *   workspace      device scratch of at least rpa_workspace_bytes(S, ...)
- *                  bytes when S > 1 (may be NULL when S == 1); holds split
+ *                  bytes when S != 1 (may be NULL when S == 1); holds split
  *                  partials, consumed within this call on `stream`.
  *   out            bf16 [num_tokens, num_heads, head_dim], written.
  *   lse            fp32 [num_tokens, num_heads] natural-log LSE, or NULL.
@@ -111,8 +117,11 @@ int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cach
 /*
  * rpa_workspace_bytes: scratch needed by rpa_attn_varlen for num_splits
  * partials: num_splits * num_tokens * num_heads * (head_dim + 1) * 4 bytes
- * (fp32 partial outputs and LSEs), rounded up to 256; 0 when num_splits <= 1.
- * Returns 0 for negative sizes.
+ * (fp32 partial outputs and LSEs), rounded up to 256; 0 when num_splits == 1.
+ * num_splits = 0 needs a fixed size for head_dim, whatever the batch:
+ * 16 KiB of per-workgroup records plus 1024 * 16 * (head_dim + 1) * 4 bytes
+ * of partials (about 8.5 MB for head_dim 128).  Returns 0 for negative
+ * sizes.
  */
 size_t rpa_workspace_bytes(int32_t num_splits, int32_t num_tokens, int32_t num_heads,
                            int32_t head_dim);
@@ -141,10 +150,11 @@ int rpa_split_combine(const float *partial_out, const float *partial_lse, int32_
  * Same inputs as the walkthrough's inkling_fa4_num_splits (batch,
  * max_seqlen_q, heads, kv heads, max KV length, whether a window is set),
  * re-derived for a gfx950 with num_cus compute units (<= 0 means 256): work
- * items are (request, q-tile, kv head); decode-shaped batches are split until
- * about four workgroups per CU exist, keeping at least 512 keys per split;
- * windowed (local) attention and prefill-heavy batches use 1.
- * Returns a value in [1, RPA_MAX_SPLITS], or RPA_ERR_SHAPE for bad sizes.
+ * items are (request, q-tile, kv head); a decode batch (max_seqlen_q * G <=
+ * 16, at most 2048 requests, no window) gets 0, the balanced decode; other
+ * batches are split until about two workgroups per CU exist, keeping at
+ * least 512 keys per split; windowed (local) attention uses 1.
+ * Returns a value in [0, RPA_MAX_SPLITS], or RPA_ERR_SHAPE for bad sizes.
  */
 int rpa_choose_splits(int32_t batch, int32_t max_seqlen_q, int32_t num_heads,
                       int32_t num_kv_heads, int64_t max_seqlen_k, int is_local, int32_t num_cus);

@@ -150,7 +150,7 @@ def rpa_attn_varlen(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
         lse = torch.empty((T, H), dtype=torch.float32, device=dev)
     if lse is not None:
         _check(lse, "lse", torch.float32, dev, 2)
-    ws_bytes = rpa_workspace_bytes(S, T, H, D) if S > 1 else 0
+    ws_bytes = rpa_workspace_bytes(S, T, H, D) if S != 1 else 0
     if ws_bytes and workspace is None:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
     st = lib().rpa_attn_varlen(

@@ -36,19 +36,19 @@ const char *rpa_status_string(int status) {
 }
 
 size_t rpa_workspace_bytes(int32_t num_splits, int32_t num_tokens, int32_t num_heads, int32_t head_dim) {
-  if (num_splits <= 1 || num_tokens < 0 || num_heads < 0 || head_dim < 0) return 0;
+  if (num_splits < 0 || num_splits == 1 || num_tokens < 0 || num_heads < 0 || head_dim < 0) return 0;
+  if (num_splits == 0) return round_up(rpa::bal_desc_bytes() + rpa::bal_part_bytes(head_dim), kAlign);
   const size_t n = (size_t)num_splits * (size_t)num_tokens * (size_t)num_heads;
   return round_up(part_lse_offset(num_splits, num_tokens, num_heads, head_dim) + n * sizeof(float), kAlign);
 }
 
-// Planner: work items are (request, q-tile, kv head).  A decode batch that
-// already offers a workgroup per CU is not split (a CU streams KV at a
-// bounded rate, so more, shorter workgroups only add per-workgroup start-up
-// and the combine); otherwise the split count is raised until the grid
-// offers about four workgroups per CU (decode) or two (prefill-shaped
-// batches), never below 512 keys per split and never above RPA_MAX_SPLITS.
-// A window bounds the keys a row sees, so local attention is not split, as
-// in the walkthrough's inkling_fa4_num_splits.
+// Planner: work items are (request, q-tile, kv head).  A decode batch gets
+// 0, the balanced decode, which cuts the batch's KV into equal shares per
+// CU whatever the length mix.  Otherwise the split count is raised until
+// the grid offers about two workgroups per CU, never below 512 keys per
+// split and never above RPA_MAX_SPLITS.  A window bounds the keys a row
+// sees, so local attention is not split, as in the walkthrough's
+// inkling_fa4_num_splits.
 int rpa_choose_splits(int32_t batch, int32_t max_seqlen_q, int32_t num_heads, int32_t num_kv_heads,
                       int64_t max_seqlen_k, int is_local, int32_t num_cus) {
   if (batch < 0 || max_seqlen_q < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_seqlen_k < 0 ||
@@ -60,7 +60,7 @@ int rpa_choose_splits(int32_t batch, int32_t max_seqlen_q, int32_t num_heads, in
   const int64_t items = rpa::items_for_request(max_seqlen_q, G);
   const bool decode = G <= rpa::kDecCols && (int64_t)max_seqlen_q * G <= rpa::kDecCols;
   const int64_t base = (int64_t)batch * num_kv_heads * items;
-  if (decode && base >= num_cus) return 1;
+  if (decode && batch <= rpa::kBalMaxBatch) return 0;
   const int64_t target = (decode ? 4 : 2) * (int64_t)num_cus;
   int64_t s = (target + base - 1) / base;
   const int64_t by_len = max_seqlen_k / 512;
@@ -106,7 +106,7 @@ int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cach
       rel_extent < 0 || window_left < -1 || window_right < -1)
     return RPA_ERR_SHAPE;
   if (num_heads % num_kv_heads != 0) return RPA_ERR_SHAPE;
-  if (num_splits < 1 || num_splits > RPA_MAX_SPLITS) return RPA_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > RPA_MAX_SPLITS) return RPA_ERR_SHAPE;
   if (!std::isfinite(softmax_scale)) return RPA_ERR_SHAPE;
   if (batch == 0 && num_tokens > 0) return RPA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return RPA_ERR_UNSUPPORTED;
@@ -118,7 +118,7 @@ int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cach
     return RPA_ERR_NULL;
   if (rel_extent > 0 && !rel_logits) return RPA_ERR_NULL;
   // Workspace for split partials.
-  if (num_splits > 1) {
+  if (num_splits != 1) {
     if (!workspace) return RPA_ERR_WORKSPACE;
     if (workspace_bytes < rpa_workspace_bytes(num_splits, num_tokens, num_heads, head_dim))
       return RPA_ERR_WORKSPACE;
@@ -130,7 +130,19 @@ int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cach
   const int64_t ub_maxq = (int64_t)batch * rpa::items_for_request(max_seqlen_q, G);
   const int64_t n_items_ub = ub_tokens < ub_maxq ? ub_tokens : ub_maxq;
   const bool decode_only = G <= rpa::kDecCols && (int64_t)max_seqlen_q * G <= rpa::kDecCols;
-  if (n_items_ub * num_kv_heads * num_splits > INT32_MAX) return RPA_ERR_SHAPE;
+  // num_splits = 0: the balanced decode where it applies, else one split.
+  const bool balanced = num_splits == 0 && decode_only && batch <= rpa::kBalMaxBatch &&
+                        (int64_t)num_tokens * num_heads * rel_extent * 4 < ((int64_t)1 << 31);
+  if (num_splits == 0 && !balanced) num_splits = 1;
+  if (n_items_ub * num_kv_heads * (int64_t)num_splits > INT32_MAX) return RPA_ERR_SHAPE;
+  int32_t bal_wgs = 0;
+  if (balanced) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return RPA_ERR_HIP;
+    bal_wgs = cus < rpa::kBalMaxWGs ? cus : rpa::kBalMaxWGs;
+  }
 
   rpa::AttnParams p;
   p.q = static_cast<const uint16_t *>(q);
@@ -144,6 +156,13 @@ int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cach
   p.lse = lse;
   p.part_out = nullptr;
   p.part_lse = nullptr;
+  p.bal_part = nullptr;
+  p.bal_desc = nullptr;
+  p.bal_wgs = bal_wgs;
+  if (balanced) {
+    p.bal_desc = static_cast<int32_t *>(workspace);
+    p.bal_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + rpa::bal_desc_bytes());
+  }
   if (num_splits > 1) {
     p.part_out = static_cast<float *>(workspace);
     p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
@@ -168,6 +187,7 @@ int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cach
   p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (balanced) return rpa::launch_balanced_decode(p, head_dim, st) == hipSuccess ? RPA_OK : RPA_ERR_HIP;
   if (rpa::launch_attention(p, head_dim, n_items_ub, decode_only, st) != hipSuccess) return RPA_ERR_HIP;
   if (num_splits > 1) {
     rpa::CombineParams c;

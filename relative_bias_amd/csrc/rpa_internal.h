@@ -14,6 +14,18 @@ constexpr int kTileKeys = 64;      // prefill KV tile
 constexpr int kDecCols = 16;       // decode item: up to 16 (token, head) columns
 constexpr int kDecWaveKeys = 32;   // keys per wave per decode iteration
 
+// Balanced decode (num_splits = 0 on a decode-only batch).
+constexpr int kBalWaves = 8;        // waves per workgroup (one workgroup per CU)
+constexpr int kBalMaxBatch = 2048;  // requests (their unit prefix sums live in LDS)
+constexpr int kBalMaxWGs = 512;     // workgroups at most
+constexpr int kBalDescInts = 8;     // per-workgroup combine record
+// Workspace of the balanced decode: kBalMaxWGs records, then two partial
+// slots per workgroup of kDecCols * (head_dim + 1) fp32 (outputs, then LSEs).
+__host__ __device__ inline size_t bal_desc_bytes() { return (size_t)kBalMaxWGs * kBalDescInts * 4; }
+__host__ __device__ inline size_t bal_part_bytes(int head_dim) {
+  return (size_t)2 * kBalMaxWGs * kDecCols * (size_t)(head_dim + 1) * 4;
+}
+
 struct AttnParams {
   const uint16_t *q;            // bf16 [T, H, D]
   const uint16_t *k;            // bf16 [NB, BS, Hkv, D]
@@ -29,6 +41,9 @@ struct AttnParams {
   int32_t batch, num_tokens, H, Hkv, G, BS, R, S, P;
   int32_t left, right, causal;
   int32_t bs_shift;             // log2(BS) when BS is a power of two, else -1
+  float *bal_part;              // balanced decode: partial slots
+  int32_t *bal_desc;            // balanced decode: per-workgroup combine records
+  int32_t bal_wgs;              // balanced decode: workgroups
   float scale;                  // softmax_scale
   float scale_log2;             // softmax_scale * log2(e)
 };
@@ -53,5 +68,8 @@ __host__ __device__ inline int64_t items_for_request(int64_t lq, int64_t G) {
 hipError_t launch_attention(const AttnParams &p, int head_dim, int64_t n_items_ub, bool decode_only,
                             hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
+// Balanced decode: the attention kernel on p.bal_wgs workgroups, then the
+// combine of the pairs cut between workgroups.
+hipError_t launch_balanced_decode(const AttnParams &p, int head_dim, hipStream_t stream);
 
 }  // namespace rpa

@@ -1279,6 +1279,527 @@ __global__ __launch_bounds__(64 * attn_waves<DECODE_ONLY>(), 2) void attn_kernel
   }
 }
 
+// ------------------------------------------------------ balanced decode
+//
+// Decode-only batches with num_splits = 0.  The work of the batch is the
+// sequence of 16-key units of every (request, kv head) pair, pairs in
+// (request, kv head) order and units in key order; workgroup w of W takes
+// units [w*TU/W, (w+1)*TU/W), so every CU streams the same number of KV
+// bytes whatever the length mix.  A workgroup walks its range piece by piece
+// (a piece is the part of one pair inside the range); its waves take the
+// piece's units round-robin, each with the next unit's loads in flight, and
+// merge their softmax states through LDS at the end of the piece.  A piece
+// that is a whole pair writes the output; a piece of a pair cut between
+// workgroups writes a normalised partial to its slot, and the workgroup that
+// holds the pair's first unit records the pair for the combine.
+//
+// K and V rows reach LDS by direct loads in which 16 lanes cover one key's
+// 256-byte head slice (a load instruction reads whole 128-byte lines), with
+// the 16-byte units of each row XOR-swizzled.  S^T = K·Q^T runs on 16x16x32
+// MFMA (K rows from LDS, Q^T in registers); O^T = V^T·P^T on 16x16x16 MFMA,
+// V^T read with ds_read_b64_tr_b16 and P^T taken straight from the S^T
+// accumulator (lane (col, q) holds keys 4q..4q+3 of its column, which is
+// the B operand layout of the 16x16x16 product).
+
+template <int D>
+struct BalLds {
+  static constexpr int ROWB = D * 2;           // bytes per key row
+  static constexpr int UNITS = D / 8;          // 16-byte units per row
+  static constexpr int RPI = 64 / UNITS;       // rows per direct-load instruction
+  static constexpr int NI = 16 / RPI;          // instructions per 16-key unit (K or V)
+  static constexpr int halfBytes = 16 * ROWB;  // K (or V) of one unit
+  static constexpr int stageBytes = 2 * halfBytes;
+  static constexpr int NST = 2;                // stages per wave
+  static constexpr int biasOff = kBalWaves * NST * stageBytes;  // per wave and stage: 4 x 64 fp32
+  static constexpr int mlOff = biasOff + kBalWaves * NST * 1024;
+  static constexpr int prefixOff = mlOff + 2 * kBalWaves * kDecCols * 4;
+  static constexpr int bytes = prefixOff + (kBalMaxBatch + 1) * 4;
+  // A wave's O^T partial (D x 16 fp32) fits in one of its stages.
+  static_assert(D * kDecCols * 4 <= stageBytes, "merge buffer");
+};
+
+// V rows: unit u sits at u ^ swz_vt(r).  A transposing read touches two
+// adjacent units of 16 consecutive rows; the swizzle moves them in pairs so
+// that each half-wave's eight rows cover all banks.
+template <int D>
+__device__ __forceinline__ int swz_vt(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+
+__device__ __forceinline__ u32x4 lds_read_b128_asm(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+// s_waitcnt lgkmcnt(N) that the listed registers wait for (their values
+// arrive by inline-asm LDS reads the compiler does not track).
+template <int N>
+__device__ __forceinline__ void lgkm_wait_n(u32x4 (&r)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait_n(u32x4 (&r)[2]) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r[0]), "+v"(r[1]) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait_n(u32x2 (&r)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7])
+               : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait_n(u32x2 (&r)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait_n(float (&r)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "n"(N));
+}
+
+// Load through the scalar cache (the data must not be written by the
+// running kernel: the block table).
+__device__ __forceinline__ int scalar_load_i32(const int32_t *p) {
+  return *(const __attribute__((address_space(4))) int32_t *)p;
+}
+__device__ __forceinline__ float lds_read_f32_asm(uint32_t addr) {
+  float v;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ u32x2 lds_read_tr_at(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                   0, 0, 0);
+}
+
+// 16-key units of request b's (request, kv head) pair: the visible range of
+// its rows from its start rounded down to 16; at least one unit, so that a
+// request without visible keys still writes its rows.
+__device__ __forceinline__ int bal_units(const AttnParams &p, int b) {
+  const int lq = p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b];
+  if (lq <= 0) return 0;
+  const int lk = p.cache_seqlens[b];
+  const Range r = visible_range(p, lk, lk - lq, lk - 1);
+  const int lo_a = r.lo & ~15;
+  return r.hi > lo_a ? max((r.hi - lo_a + 15) >> 4, 1) : 1;
+}
+
+// prefix[b] = Hkv * (units of requests before b); prefix[batch] = all units.
+__device__ void bal_prefix(const AttnParams &p, int32_t *prefix, int32_t *tmp) {
+  constexpr int NT = 64 * kBalWaves;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int B = p.batch;
+  const int per = (B + NT - 1) / NT;
+  const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
+  int local = 0;
+  for (int b = b0; b < b1; ++b) local += bal_units(p, b);
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) tmp[w] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int ww = 0; ww < w; ++ww) base += tmp[ww];
+  int run = (base + incl - local) * p.Hkv;
+  for (int b = b0; b < b1; ++b) {
+    prefix[b] = run;
+    run += bal_units(p, b) * p.Hkv;
+  }
+  if (b0 < b1 && b1 == B) prefix[B] = run;
+  __syncthreads();
+}
+
+__device__ __forceinline__ int bal_unit_at(int TU, int x, int nwg) { return (int)((int64_t)TU * x / nwg); }
+
+template <int D, bool BIAS>
+__device__ void decode_balanced(const AttnParams &p, char *smem) {
+  using L = BalLds<D>;
+  constexpr int NW = kBalWaves;
+  constexpr int QK = D / 32, DB = D / 16, NI = L::NI, RPI = L::RPI, UNITS = L::UNITS, ROWB = L::ROWB;
+  constexpr int NPER = 2 * NI;  // vector-memory instructions per unit (plus 4 in the bias band)
+  int32_t *prefix = reinterpret_cast<int32_t *>(smem + L::prefixOff);
+  float *red_m = reinterpret_cast<float *>(smem + L::mlOff);
+  float *red_l = red_m + NW * kDecCols;
+  bal_prefix(p, prefix, reinterpret_cast<int32_t *>(red_m));
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, q = lane >> 4;
+  const int B = p.batch, Hkv = p.Hkv, G = p.G;
+  const int nwg = p.bal_wgs, wg = blockIdx.x;
+  const int TU = __builtin_amdgcn_readfirstlane(prefix[B]);
+  const int u0 = bal_unit_at(TU, wg, nwg), u1 = bal_unit_at(TU, wg + 1, nwg);
+
+  const uint32_t slot_bytes = (uint32_t)Hkv * D * 2;
+  uint32_t gk[NI], gv[NI];
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    const int r = RPI * n + lane / UNITS, pu = lane % UNITS;
+    gk[n] = r * slot_bytes + ((pu ^ swz_k<D>(r)) << 4);
+    gv[n] = r * slot_bytes + ((pu ^ swz_vt<D>(r)) << 4);
+  }
+  uint32_t lk_off[QK], lv_off[DB];
+#pragma unroll
+  for (int ks = 0; ks < QK; ++ks) lk_off[ks] = c16 * ROWB + (((4 * ks + q) ^ swz_k<D>(c16)) << 4);
+  {
+    const int i = (lane & 15) >> 2, t = lane & 3, row = 4 * q + i;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      lv_off[db] = L::halfBytes + row * ROWB + ((((2 * db + (t >> 1)) ^ swz_vt<D>(row)) << 4)) + 8 * (t & 1);
+  }
+  const uint32_t lds_wave = (uint32_t)(uintptr_t)smem + (uint32_t)(w * L::NST * L::stageBytes);
+  const uint32_t lds_bias = (uint32_t)(uintptr_t)smem + (uint32_t)(L::biasOff + w * L::NST * 1024 + 4 * lane);
+  const float c = p.scale_log2;
+  const bool pos_scale = c > 0.f;
+  const auto bias_rs = make_rsrc(p.rel_logits, BIAS ? (uint32_t)p.num_tokens * (uint32_t)p.H * (uint32_t)p.R * 4u : 0u);
+
+  int own_b = -1, own_g = 0, own_last = 0, own_which = 0;
+  int b = 0;
+  {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (prefix[mid] <= u0) lo = mid;
+      else hi = mid - 1;
+    }
+    b = __builtin_amdgcn_readfirstlane(lo);
+  }
+  int cur = u0;
+  while (cur < u1) {
+    while (__builtin_amdgcn_readfirstlane(prefix[b + 1]) <= cur) ++b;
+    const int pb = __builtin_amdgcn_readfirstlane(prefix[b]);
+    const int nu = (__builtin_amdgcn_readfirstlane(prefix[b + 1]) - pb) / Hkv;
+    const int off = cur - pb;
+    const int g = off / nu, j0 = off - g * nu;
+    const int j1 = min(nu, j0 + (u1 - cur));
+    const int which = cur == u0 ? 0 : 1;
+
+    const int tok0 = __builtin_amdgcn_readfirstlane(p.cu_seqlens_q[b]);
+    const int lq = __builtin_amdgcn_readfirstlane(p.cu_seqlens_q[b + 1]) - tok0;
+    const int lk = __builtin_amdgcn_readfirstlane(p.cache_seqlens[b]);
+    const int ncols = lq * G;
+    const int col = c16 < ncols ? c16 : ncols - 1;
+    const int qi = col / G;
+    const int head = g * G + (col - qi * G);
+    const int tok = tok0 + qi;
+    const int qa = qi + lk - lq;
+    const int qa_min = lk - lq, qa_max = lk - 1;
+    const Range vr = visible_range(p, lk, qa_min, qa_max);
+    const int lo_a = vr.lo & ~15;
+    const int kend = min(lk, vr.hi);
+    int lo_c = lo_a, hi_c = kend - 1;
+    if (p.left >= 0) lo_c = max(lo_c, qa - p.left);
+    if (p.causal) hi_c = min(hi_c, qa);
+    if (p.right >= 0) hi_c = min(hi_c, qa + p.right);
+    int in_lo = lo_a, in_hi = kend - 1;
+    if (p.left >= 0) in_lo = max(in_lo, qa_max - p.left);
+    if (p.causal) in_hi = min(in_hi, qa_min);
+    if (p.right >= 0) in_hi = min(in_hi, qa_min + p.right);
+    const int band_lo = qa_min - p.R + 1, band_hi = qa_max;
+    const uint32_t rel_base = BIAS ? (uint32_t)((tok * p.H + head) * p.R) : 0u;
+
+    bf16x8 qf[QK];
+    {
+      const uint16_t *qp = p.q + ((int64_t)tok * p.H + head) * D + 8 * q;
+#pragma unroll
+      for (int ks = 0; ks < QK; ++ks) qf[ks] = as_bf16x8(ld16(qp + 32 * ks));
+    }
+    f32x4 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x4{};
+    float m_run = neg_inf(), l_run = 0.f;
+
+    const int n_units = j1 - j0;
+    const int my_n = n_units > w ? (n_units - w + NW - 1) / NW : 0;
+    // Page ids are read by scalar loads one unit ahead of their use.
+    const int32_t *bt = p.block_table + (int64_t)b * p.P;
+    auto key_of_unit = [&](int k) { return lo_a + 16 * (j0 + w + NW * k); };
+    auto page_of = [&](int k) -> int {
+      const int key = key_of_unit(k);
+      if (k >= my_n || key >= kend) return 0;
+      return scalar_load_i32(bt + (p.bs_shift >= 0 ? (key >> p.bs_shift) : key / p.BS));
+    };
+    auto in_band = [&](int key0) { return BIAS && key0 <= band_hi && key0 + 15 >= band_lo; };
+
+    auto issue = [&](int k, int page, auto s_tag) __attribute__((always_inline)) {
+      constexpr int S = decltype(s_tag)::value;
+      const int key0 = __builtin_amdgcn_readfirstlane(key_of_unit(k));
+      const int nvalid = __builtin_amdgcn_readfirstlane(min(max(kend - key0, 0), 16));
+      const int slot0 = p.bs_shift >= 0 ? (key0 & (p.BS - 1)) : key0 % p.BS;
+      const int64_t eoff = (((int64_t)page * p.BS + slot0) * Hkv + g) * D;
+      const auto rk = make_rsrc(p.k + eoff, (uint32_t)nvalid * slot_bytes);
+      const auto rv = make_rsrc(p.v + eoff, (uint32_t)nvalid * slot_bytes);
+      if (in_band(key0)) {
+        // Raw logits of the lane's four keys (distance clamped into the
+        // row; the band test in compute() discards what lies outside it).
+        char *bst = smem + L::biasOff + (w * L::NST + S) * 1024;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = min(max(qa - (key0 + 4 * q + j), 0), p.R - 1);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(bias_rs, (__attribute__((address_space(3))) void *)(bst + 256 * j),
+                                                   4, (rel_base + (uint32_t)d) * 4u, 0, 0, 0);
+        }
+      }
+      char *st = smem + (w * L::NST + S) * L::stageBytes;
+#pragma unroll
+      for (int n = 0; n < NI; ++n)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void *)(st + n * 1024), 16,
+                                                 gk[n], 0, 0, 0);
+#pragma unroll
+      for (int n = 0; n < NI; ++n)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void *)(st + L::halfBytes + n * 1024), 16, gv[n], 0, 0, 0);
+    };
+
+    auto compute = [&](int k, auto s_tag) __attribute__((always_inline)) {
+      constexpr int S = decltype(s_tag)::value;
+      const int key0 = __builtin_amdgcn_readfirstlane(key_of_unit(k));
+      const uint32_t st = lds_wave + S * L::stageBytes;
+      u32x4 kf[QK];
+#pragma unroll
+      for (int ks = 0; ks < QK; ++ks) kf[ks] = lds_read_b128_asm(st + lk_off[ks]);
+      u32x2 va[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) va[db] = lds_read_tr_at(st + lv_off[db]);
+      // LDS reads complete in order: the K operands are in once at most the
+      // DB V reads issued after them are outstanding.
+      lgkm_wait_n<DB>(kf);
+      f32x4 sacc = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < QK; ++ks) sacc = mfma16(as_bf16x8(kf[ks]), qf[ks], sacc);
+      // Lane (c16, q) holds S[col c16][key key0 + 4q + j].
+      const bool interior = key0 >= in_lo && key0 + 15 <= in_hi;
+      const bool band = in_band(key0);
+      const bool plain = interior && !band;
+      float mx = neg_inf();
+      if (plain) {
+        if (pos_scale) {
+          mx = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3])) * c;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sacc[j] * c);
+        }
+      } else {
+        float bias[4] = {0.f, 0.f, 0.f, 0.f};
+        if (band) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bias[j] = lds_read_f32_asm(lds_bias + S * 1024 + 256 * j);
+          lgkm_wait_n<0>(bias);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = key0 + 4 * q + j;
+          float v = sacc[j] * c;
+          if (band && (unsigned)(qa - t) < (unsigned)p.R) v = __builtin_fmaf(bias[j], kLog2e, v);
+          if (t < lo_c || t > hi_c) v = neg_inf();
+          sacc[j] = v;
+          mx = fmaxf(mx, v);
+        }
+      }
+      mx = xor16_max(mx);
+      mx = xor32_max(mx);
+      if (__any(mx > m_run + kTau)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == neg_inf() ? 1.f : exp2_fast(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      }
+      const float m_use = m_run == neg_inf() ? 0.f : m_run;
+      float pe[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pe[j] = exp2_fast(plain ? __builtin_fmaf(sacc[j], c, -m_use) : sacc[j] - m_use);
+      l_run += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+      const u32x2 pf = u32x2{pack2_bf16(pe[0], pe[1]), pack2_bf16(pe[2], pe[3])};
+      lgkm_wait_n<0>(va);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = mfma16k16(va[db], pf, oacc[db]);
+    };
+
+    // The direct loads write LDS behind the compiler's back: their
+    // completion is awaited explicitly (vmcnt counts this wave's vector
+    // memory instructions in issue order; NPER were issued after the unit
+    // being waited for).
+    int page_nx = 0;
+    auto step = [&](int k, auto s_tag) __attribute__((always_inline)) {
+      constexpr int S = decltype(s_tag)::value;
+      if (k + 1 < my_n) {
+        issue(k + 1, page_nx, IntTag<1 - S>{});
+        page_nx = page_of(k + 2);
+        if (in_band(key_of_unit(k + 1))) __builtin_amdgcn_s_waitcnt(0x0F70 | (NPER + 4));
+        else __builtin_amdgcn_s_waitcnt(0x0F70 | NPER);
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
+      compute(k, s_tag);
+    };
+    // Q is in before the first direct load is issued (nothing of the
+    // previous piece is in flight any more), so that no later wait on the
+    // Q registers can count the unit loads in flight.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (my_n > 0) {
+      issue(0, page_of(0), IntTag<0>{});
+      page_nx = page_of(1);
+    }
+    for (int k = 0; k < my_n; k += 2) {
+      step(k, IntTag<0>{});
+      if (k + 1 < my_n) step(k + 1, IntTag<1>{});
+    }
+
+    // Merge the waves' (m, l, O^T) through LDS: O^T partials go to each
+    // wave's first stage (its loads and reads of this piece are complete).
+    const float l_col = xor32_sum(xor16_sum(l_run));
+    float *red_o = reinterpret_cast<float *>(smem + w * L::NST * L::stageBytes);
+    if (q == 0) {
+      red_m[w * kDecCols + c16] = m_run;
+      red_l[w * kDecCols + c16] = l_col;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red_o[(16 * db + 4 * q + j) * kDecCols + c16] = oacc[db][j];
+    __syncthreads();
+    {
+      constexpr int DPG = D * kDecCols / (64 * NW);
+      const int fc = tid & 15, fg = tid >> 4;
+      if (fc < ncols) {
+        float mw[NW], sc[NW];
+        float M = neg_inf();
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+          mw[ww] = red_m[ww * kDecCols + fc];
+          M = fmaxf(M, mw[ww]);
+        }
+        float Lsum = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+          sc[ww] = mw[ww] == neg_inf() ? 0.f : exp2_fast(mw[ww] - M);
+          Lsum += sc[ww] * red_l[ww * kDecCols + fc];
+        }
+        const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+        const float lse_v = Lsum > 0.f ? (M + log2_fast(Lsum)) * kLn2 : neg_inf();
+        float o[DPG];
+#pragma unroll
+        for (int e = 0; e < DPG; ++e) {
+          const int d = fg * DPG + e;
+          float acc = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < NW; ++ww)
+            acc += sc[ww] * reinterpret_cast<const float *>(smem + ww * L::NST * L::stageBytes)[d * kDecCols + fc];
+          o[e] = acc * inv;
+        }
+        const int fqi = fc / G;
+        const int fhead = g * G + (fc - fqi * G);
+        const int ftok = tok0 + fqi;
+        if (j0 == 0 && j1 == nu) {
+          uint16_t *op = p.out + ((int64_t)ftok * p.H + fhead) * D + fg * DPG;
+          if constexpr (DPG == 4) {
+            *reinterpret_cast<u32x2 *>(op) = u32x2{pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3])};
+          } else {
+            *reinterpret_cast<uint32_t *>(op) = pack2_bf16(o[0], o[1]);
+          }
+          if (fg == 0 && p.lse) p.lse[(int64_t)ftok * p.H + fhead] = lse_v;
+        } else {
+          float *slot = p.bal_part + (size_t)(2 * wg + which) * (kDecCols * (D + 1));
+          float *pp = slot + fc * D + fg * DPG;
+          if constexpr (DPG == 4) {
+            *reinterpret_cast<f32x4 *>(pp) = f32x4{o[0], o[1], o[2], o[3]};
+          } else {
+            *reinterpret_cast<f32x2 *>(pp) = f32x2{o[0], o[1]};
+          }
+          if (fg == 0) slot[kDecCols * D + fc] = lse_v;
+        }
+      }
+    }
+    __syncthreads();  // the stages and red_m / red_l are reused by the next piece
+
+    if (cur + n_units == u1 && j0 == 0 && j1 < nu) {
+      // This workgroup holds the first unit of a pair that continues into
+      // later workgroups: the combine of that pair is its job.
+      const int last_unit = pb + (g + 1) * nu - 1;
+      int wl = (int)(((int64_t)last_unit * nwg) / TU);
+      while (wl + 1 < nwg && bal_unit_at(TU, wl + 1, nwg) <= last_unit) ++wl;
+      while (wl > 0 && bal_unit_at(TU, wl, nwg) > last_unit) --wl;
+      own_b = b;
+      own_g = g;
+      own_last = wl;
+      own_which = which;
+    }
+    cur += n_units;
+  }
+  if (tid == 0) {
+    int32_t *dsc = p.bal_desc + wg * kBalDescInts;
+    dsc[0] = own_b;
+    dsc[1] = own_g;
+    dsc[2] = own_last;
+    dsc[3] = own_which;
+    dsc[4] = TU;
+  }
+}
+
+template <int D, bool BIAS>
+__global__ __launch_bounds__(64 * kBalWaves, 1) void decode_balanced_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[BalLds<D>::bytes];
+  decode_balanced<D, BIAS>(p, smem);
+}
+
+// Merges the pieces of the pair recorded by decode workgroup blockIdx.x: its
+// own piece, then the first piece of every later workgroup up to the one
+// holding the pair's last unit (workgroups with empty ranges hold none).
+template <int D>
+__global__ __launch_bounds__(kThreads) void combine_balanced_kernel(AttnParams p) {
+  const int wg = blockIdx.x;
+  const int32_t *dsc = p.bal_desc + wg * kBalDescInts;
+  const int b = dsc[0];
+  if (b < 0) return;
+  const int g = dsc[1], w_last = dsc[2], which = dsc[3], TU = dsc[4];
+  const int nwg = p.bal_wgs, G = p.G;
+  const int tok0 = p.cu_seqlens_q[b];
+  const int ncols = (p.cu_seqlens_q[b + 1] - tok0) * G;
+  constexpr int DPG = D * kDecCols / kThreads;
+  constexpr int SLOT = kDecCols * (D + 1);
+  const int fc = threadIdx.x & 15, fg = threadIdx.x >> 4;
+  if (fc >= ncols) return;
+  auto for_pieces = [&](auto f) {
+    f(2 * wg + which);
+    for (int w2 = wg + 1; w2 <= w_last; ++w2)
+      if (bal_unit_at(TU, w2, nwg) < bal_unit_at(TU, w2 + 1, nwg)) f(2 * w2);
+  };
+  float M = neg_inf();
+  for_pieces([&](int s) { M = fmaxf(M, p.bal_part[(size_t)s * SLOT + kDecCols * D + fc]); });
+  const int fqi = fc / G;
+  const int fhead = g * G + (fc - fqi * G);
+  const int ftok = tok0 + fqi;
+  uint16_t *op = p.out + ((int64_t)ftok * p.H + fhead) * D + fg * DPG;
+  float o[DPG];
+#pragma unroll
+  for (int e = 0; e < DPG; ++e) o[e] = 0.f;
+  float W = 0.f;
+  if (M != neg_inf()) {
+    for_pieces([&](int s) {
+      const float ls = p.bal_part[(size_t)s * SLOT + kDecCols * D + fc];
+      W += ls == neg_inf() ? 0.f : exp2_fast((ls - M) * kLog2e);
+    });
+    const float invW = 1.f / W;
+    for_pieces([&](int s) {
+      const float ls = p.bal_part[(size_t)s * SLOT + kDecCols * D + fc];
+      const float wt = ls == neg_inf() ? 0.f : exp2_fast((ls - M) * kLog2e) * invW;
+      const float *src = p.bal_part + (size_t)s * SLOT + fc * D + fg * DPG;
+#pragma unroll
+      for (int e = 0; e < DPG; ++e) o[e] += wt * src[e];
+    });
+  }
+#pragma unroll
+  for (int e = 0; e < DPG; e += 2) reinterpret_cast<uint32_t *>(op)[e / 2] = pack2_bf16(o[e], o[e + 1]);
+  if (fg == 0 && p.lse) p.lse[(int64_t)ftok * p.H + fhead] = M == neg_inf() ? neg_inf() : M + log2_fast(W) * kLn2;
+}
+
 // ---------------------------------------------------------------- combine
 
 // One wave per (token, head) row: weights exp(lse_s - LSE) over the splits,
@@ -1329,6 +1850,21 @@ hipError_t launch_attention(const AttnParams &p, int head_dim, int64_t n_items_u
   } else {
     if (decode_only) hipLaunchKernelGGL((attn_kernel<64, true>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((attn_kernel<64, false>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_balanced_decode(const AttnParams &p, int head_dim, hipStream_t stream) {
+  const dim3 grid((unsigned)p.bal_wgs), block(64 * kBalWaves), cgrid((unsigned)p.bal_wgs), cblock(kThreads);
+  const bool bias = p.R > 0;
+  if (head_dim == 128) {
+    if (bias) hipLaunchKernelGGL((decode_balanced_kernel<128, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_balanced_kernel<128, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((combine_balanced_kernel<128>), cgrid, cblock, 0, stream, p);
+  } else {
+    if (bias) hipLaunchKernelGGL((decode_balanced_kernel<64, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_balanced_kernel<64, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((combine_balanced_kernel<64>), cgrid, cblock, 0, stream, p);
   }
   return hipGetLastError();
 }

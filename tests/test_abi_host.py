@@ -50,8 +50,15 @@ def test_status_strings(L):
 
 def test_workspace_bytes(L):
     assert bnd.rpa_workspace_bytes(1, 100, 8, 128) == 0
-    assert bnd.rpa_workspace_bytes(0, 100, 8, 128) == 0
+    assert bnd.rpa_workspace_bytes(-1, 100, 8, 128) == 0
     assert bnd.rpa_workspace_bytes(4, -1, 8, 128) == 0
+    # num_splits = 0 (balanced decode): per-workgroup records plus two
+    # partial slots of 16 columns per workgroup, whatever the batch.
+    for D in (64, 128):
+        n0 = bnd.rpa_workspace_bytes(0, 100, 8, D)
+        assert n0 == bnd.rpa_workspace_bytes(0, 1, 64, D)
+        assert n0 % 256 == 0
+        assert n0 >= 512 * 8 * 4 + 2 * 512 * 16 * (D + 1) * 4
     for S, T, H, D in [(2, 1, 1, 64), (4, 32, 32, 128), (128, 1, 64, 128), (3, 17, 6, 64)]:
         n = bnd.rpa_workspace_bytes(S, T, H, D)
         assert n >= S * T * H * (D + 1) * 4
@@ -79,7 +86,7 @@ def test_rel_logits_required_when_extent_positive(L):
     assert _attn(L, R=8, rel=None) == NULL
 
 
-@pytest.mark.parametrize("kw", [dict(H=6, Hkv=4), dict(S=0), dict(S=129), dict(B=-1), dict(T=-2),
+@pytest.mark.parametrize("kw", [dict(H=6, Hkv=4), dict(S=-1), dict(S=129), dict(B=-1), dict(T=-2),
                                 dict(H=0), dict(Hkv=0), dict(BS=0), dict(left=-2), dict(right=-5),
                                 dict(R=-1), dict(maxq=-1), dict(P=-1), dict(B=0, T=3),
                                 dict(scale=float("nan")), dict(scale=float("inf"))])
@@ -96,6 +103,9 @@ def test_workspace_checks(L):
     assert _attn(L, S=4, ws=None) == WS
     need = bnd.rpa_workspace_bytes(4, 3, 4, 64)
     assert _attn(L, S=4, ws=FAKE, wsb=need - 1) == WS
+    assert _attn(L, S=0, ws=None) == WS
+    need0 = bnd.rpa_workspace_bytes(0, 3, 4, 64)
+    assert _attn(L, S=0, ws=FAKE, wsb=need0 - 1) == WS
 
 
 def test_empty_batch_is_a_no_op(L):
@@ -125,23 +135,31 @@ def test_planner_rejects_bad_sizes(L):
 @pytest.mark.parametrize("B,maxq,H,Hkv,maxk", [(32, 1, 32, 8, 8192), (1, 1, 64, 8, 1 << 20),
                                                (8, 2048, 32, 8, 6144), (68, 1024, 64, 8, 131072),
                                                (3, 16, 4, 2, 312), (1, 1, 8, 1, 100), (256, 1, 32, 8, 4096),
-                                               (1, 4, 64, 8, 1 << 20)])
+                                               (1, 4, 64, 8, 1 << 20), (3000, 1, 32, 8, 4096),
+                                               (4, 3, 32, 4, 5000)])
 def test_planner_properties(L, B, maxq, H, Hkv, maxk):
     s = bnd.rpa_choose_splits(B, maxq, H, Hkv, maxk)
-    assert 1 <= s <= bnd.RPA_MAX_SPLITS
-    if s > 1:
-        assert maxk // s >= 512          # at least 512 keys per split
+    G = H // Hkv
+    if maxq * G <= 16 and B <= 2048:
+        assert s == 0                    # decode batch: the balanced decode
+    else:
+        assert 1 <= s <= bnd.RPA_MAX_SPLITS
+        if s > 1:
+            assert maxk // s >= 512      # at least 512 keys per split
+        # more requests never ask for more splits
+        assert bnd.rpa_choose_splits(2 * B, maxq, H, Hkv, maxk) <= s
     assert bnd.rpa_choose_splits(B, maxq, H, Hkv, maxk, is_local=True) == 1
-    # more requests never ask for more splits
-    assert bnd.rpa_choose_splits(2 * B, maxq, H, Hkv, maxk) <= s
 
 
-def test_planner_long_context_decode_uses_many_splits(L):
-    assert bnd.rpa_choose_splits(1, 1, 64, 8, 1 << 20) >= 16
+def test_planner_splits_long_context_prefill_rows(L):
+    # A query longer than one decode column group cannot take the balanced
+    # decode: split by length.
+    assert bnd.rpa_choose_splits(1, 32, 64, 8, 1 << 20) >= 16
     assert bnd.rpa_choose_splits(8, 2048, 32, 8, 6144) == 1
 
 
-def test_planner_does_not_split_a_decode_batch_that_fills_the_chip(L):
-    # 32 requests x 8 kv heads = 256 workgroups: one per CU already.
-    assert L.rpa_choose_splits(32, 1, 32, 8, 8192, 0, 256) == 1
-    assert L.rpa_choose_splits(32, 1, 32, 8, 8192, 0, 512) > 1
+def test_planner_balances_decode_batches(L):
+    assert L.rpa_choose_splits(32, 1, 32, 8, 8192, 0, 256) == 0
+    assert L.rpa_choose_splits(1, 1, 64, 8, 1 << 20, 0, 256) == 0
+    # More requests than the balanced decode takes: one split each.
+    assert L.rpa_choose_splits(3000, 1, 32, 8, 8192, 0, 256) == 1

@@ -93,7 +93,7 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("S", [1, 3])
+@pytest.mark.parametrize("S", [1, 3, 0])
 @pytest.mark.parametrize("name", list(CASES))
 def test_small_cases(name, S):
     ql, kl, H, Hkv, D, BS, R, causal, win = CASES[name]
@@ -116,6 +116,74 @@ def test_softmax_scale_signs(scale, D):
     for S in (1, 2):
         out, lse = _gpu_run(w.to("cuda"), S)
         _compare(out, lse, *ref, tag=f"scale={scale} D={D} S={S}")
+
+
+# Decode-only batches for the balanced decode (num_splits = 0): work cut
+# into equal per-CU shares of 16-key units, pairs split across workgroups.
+BAL_CASES = {
+    # name: (q_lens, k_lens, H, Hkv, D, BS, R, causal, window, scale)
+    "fewer_units_than_cus": ([1], [20], 4, 1, 128, 16, 8, True, (-1, -1), None),
+    "one_key": ([1, 1], [1, 2], 8, 2, 64, 16, 4, True, (-1, -1), None),
+    "long_and_short": ([1, 1, 1], [20000, 3, 900], 16, 2, 128, 16, 128, True, (-1, -1), None),
+    "zero_q_and_empty_kv": ([1, 0, 1, 2, 1], [0, 5, 1, 1, 40], 8, 2, 128, 16, 16, True, (-1, -1), None),
+    "sixteen_columns": ([4, 2, 1], [300, 57, 1000], 16, 4, 128, 16, 64, True, (-1, -1), None),
+    "window_left": ([1, 1, 3], [5000, 200, 2000], 8, 2, 128, 16, 64, True, (255, 0), None),
+    "window_both_noncausal": ([2, 1], [300, 120], 4, 2, 64, 16, 10, False, (20, 7), None),
+    "bs48_d64": ([1, 1], [1000, 333], 8, 1, 64, 48, 100, True, (-1, -1), None),
+    "bs32_no_bias": ([1, 1, 1], [2049, 31, 64], 8, 2, 128, 32, 0, True, (-1, -1), None),
+    "gqa16_d64": ([1, 1], [4000, 77], 16, 1, 64, 16, 8, True, (-1, -1), None),
+    "bias_wider_than_kv": ([1, 1], [25, 300], 4, 2, 128, 16, 512, True, (-1, -1), None),
+    "negative_scale": ([1, 2], [700, 90], 8, 2, 128, 16, 48, True, (-1, -1), -0.09),
+    "zero_scale": ([1, 1], [300, 1500], 8, 2, 64, 16, 48, True, (-1, -1), 0.0),
+}
+
+
+@pytest.mark.parametrize("name", list(BAL_CASES))
+def test_balanced_decode_cases(name):
+    ql, kl, H, Hkv, D, BS, R, causal, win, scale = BAL_CASES[name]
+    kw = {} if scale is None else {"softmax_scale": scale}
+    w = wl.build(ql, kl, num_heads=H, num_kv_heads=Hkv, head_dim=D, block_size=BS, rel_extent=R,
+                 causal=causal, window_size=win, seed=sum(map(ord, name)), extra_pages=3, poison=True, **kw)
+    ref = _oracle(w)
+    out, lse = _gpu_run(w.to("cuda"), 0)
+    _compare(out, lse, *ref, tag=f"{name} balanced")
+
+
+def test_balanced_decode_many_requests():
+    """More requests than CUs, ragged lengths 0..1500: pieces of many pairs
+    per workgroup, and pairs cut across workgroup boundaries."""
+    g = torch.Generator().manual_seed(77)
+    B = 300
+    kl = [int(x) for x in torch.randint(0, 1500, (B,), generator=g)]
+    w = wl.build([1] * B, kl, num_heads=8, num_kv_heads=2, head_dim=128, rel_extent=64, seed=78,
+                 extra_pages=2, poison=True)
+    ref = _oracle(w)
+    out, lse = _gpu_run(w.to("cuda"), 0)
+    _compare(out, lse, *ref, tag="many requests balanced")
+
+
+def test_balanced_decode_repeatable_and_page_permutation_exact():
+    w = wl.build([1, 1, 2], [5000, 300, 2000], num_heads=8, num_kv_heads=2, head_dim=128,
+                 rel_extent=64, seed=41, extra_pages=4)
+    wg = w.to("cuda")
+    a = bnd.attn_workload(wg, num_splits=0)
+    b = bnd.attn_workload(wg, num_splits=0)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    nb = w.key_cache.shape[0]
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(10))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(nb)
+    w2 = w.to("cpu")
+    w2.key_cache = w.key_cache[perm].contiguous()
+    w2.value_cache = w.value_cache[perm].contiguous()
+    bt = w.block_table.clone()
+    m = bt >= 0
+    bt[m] = inv[bt[m].long()].int()
+    w2.block_table = bt
+    c = bnd.attn_workload(w2.to("cuda"), num_splits=0)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
 
 
 def test_many_splits_with_short_ranges():
@@ -185,7 +253,7 @@ def test_split_count_invariance():
     w = wl.build([1, 1, 30], [3000, 1500, 2048], num_heads=16, num_kv_heads=2, head_dim=128,
                  rel_extent=128, seed=23).to("cuda")
     base = _gpu_run(w, 1)
-    for S in (2, 7, 16, 64):
+    for S in (2, 7, 16, 64, 0):
         o, l = _gpu_run(w, S)
         assert (o - base[0]).abs().max().item() <= 1e-2
         fin = torch.isfinite(base[1])
