@@ -1301,6 +1301,8 @@ __global__ __launch_bounds__(64 * attn_waves<DECODE_ONLY>(), 2) void attn_kernel
 // accumulator (lane (col, q) holds keys 4q..4q+3 of its column, which is
 // the B operand layout of the 16x16x16 product).
 
+constexpr int kBalStages = 2;  // 16-key units in flight or in use per wave
+
 template <int D>
 struct BalLds {
   static constexpr int ROWB = D * 2;           // bytes per key row
@@ -1309,7 +1311,7 @@ struct BalLds {
   static constexpr int NI = 16 / RPI;          // instructions per 16-key unit (K or V)
   static constexpr int halfBytes = 16 * ROWB;  // K (or V) of one unit
   static constexpr int stageBytes = 2 * halfBytes;
-  static constexpr int NST = 2;                // stages per wave
+  static constexpr int NST = kBalStages;       // stages per wave
   static constexpr int biasOff = kBalWaves * NST * stageBytes;  // per wave and stage: 4 x 64 fp32
   static constexpr int mlOff = biasOff + kBalWaves * NST * 1024;
   static constexpr int prefixOff = mlOff + 2 * kBalWaves * kDecCols * 4;
@@ -1352,6 +1354,14 @@ __device__ __forceinline__ void lgkm_wait_n(u32x2 (&r)[4]) {
 template <int N>
 __device__ __forceinline__ void lgkm_wait_n(float (&r)[4]) {
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "n"(N));
+}
+
+// s_waitcnt vmcnt(N): at most N vector-memory instructions of this wave
+// still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Load through the scalar cache (the data must not be written by the
@@ -1421,7 +1431,9 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
   using L = BalLds<D>;
   constexpr int NW = kBalWaves;
   constexpr int QK = D / 32, DB = D / 16, NI = L::NI, RPI = L::RPI, UNITS = L::UNITS, ROWB = L::ROWB;
-  constexpr int NPER = 2 * NI;  // vector-memory instructions per unit (plus 4 in the bias band)
+  constexpr int NST = L::NST;
+  constexpr int NPER = 2 * NI + (BIAS ? 4 : 0);  // vector-memory instructions per unit
+  static_assert(NPER * (NST - 1) < 64, "vmcnt range");
   int32_t *prefix = reinterpret_cast<int32_t *>(smem + L::prefixOff);
   float *red_m = reinterpret_cast<float *>(smem + L::mlOff);
   float *red_l = red_m + NW * kDecCols;
@@ -1456,7 +1468,7 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
   const uint32_t lds_bias = (uint32_t)(uintptr_t)smem + (uint32_t)(L::biasOff + w * L::NST * 1024 + 4 * lane);
   const float c = p.scale_log2;
   const bool pos_scale = c > 0.f;
-  const auto bias_rs = make_rsrc(p.rel_logits, BIAS ? (uint32_t)p.num_tokens * (uint32_t)p.H * (uint32_t)p.R * 4u : 0u);
+  const uint32_t bias_bytes = BIAS ? (uint32_t)p.num_tokens * (uint32_t)p.H * (uint32_t)p.R * 4u : 0u;
 
   int own_b = -1, own_g = 0, own_last = 0, own_which = 0;
   int b = 0;
@@ -1534,15 +1546,18 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
       const int64_t eoff = (((int64_t)page * p.BS + slot0) * Hkv + g) * D;
       const auto rk = make_rsrc(p.k + eoff, (uint32_t)nvalid * slot_bytes);
       const auto rv = make_rsrc(p.v + eoff, (uint32_t)nvalid * slot_bytes);
-      if (in_band(key0)) {
+      if constexpr (BIAS) {
         // Raw logits of the lane's four keys (distance clamped into the
         // row; the band test in compute() discards what lies outside it).
+        // Issued for every unit, through an empty resource outside the
+        // band, so that every unit counts the same vector-memory ops.
+        const auto brs = make_rsrc(p.rel_logits, in_band(key0) ? bias_bytes : 0u);
         char *bst = smem + L::biasOff + (w * L::NST + S) * 1024;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = min(max(qa - (key0 + 4 * q + j), 0), p.R - 1);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(bias_rs, (__attribute__((address_space(3))) void *)(bst + 256 * j),
-                                                   4, (rel_base + (uint32_t)d) * 4u, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (__attribute__((address_space(3))) void *)(bst + 256 * j), 4,
+                                                   (rel_base + (uint32_t)d) * 4u, 0, 0, 0);
         }
       }
       char *st = smem + (w * L::NST + S) * L::stageBytes;
@@ -1624,32 +1639,39 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
 
     // The direct loads write LDS behind the compiler's back: their
     // completion is awaited explicitly (vmcnt counts this wave's vector
-    // memory instructions in issue order; NPER were issued after the unit
-    // being waited for).
+    // memory instructions in issue order, NPER per unit).  Unit k uses
+    // stage k % NST; units k+1 .. k+NST-1 are in flight while it is
+    // computed.
     int page_nx = 0;
     auto step = [&](int k, auto s_tag) __attribute__((always_inline)) {
       constexpr int S = decltype(s_tag)::value;
-      if (k + 1 < my_n) {
-        issue(k + 1, page_nx, IntTag<1 - S>{});
-        page_nx = page_of(k + 2);
-        if (in_band(key_of_unit(k + 1))) __builtin_amdgcn_s_waitcnt(0x0F70 | (NPER + 4));
-        else __builtin_amdgcn_s_waitcnt(0x0F70 | NPER);
+      if (k + NST - 1 < my_n) {
+        issue(k + NST - 1, page_nx, IntTag<(S + NST - 1) % NST>{});
+        page_nx = page_of(k + NST);
+        wait_vm<NPER * (NST - 1)>();
       } else {
-        __builtin_amdgcn_s_waitcnt(0x0F70);
+        const int after = my_n - 1 - k;  // units issued after k
+        static_for<0, NST - 1>([&](auto i_tag) __attribute__((always_inline)) {
+          constexpr int i = decltype(i_tag)::value;
+          if (after == i) wait_vm<NPER * i>();
+        });
       }
       compute(k, s_tag);
     };
     // Q is in before the first direct load is issued (nothing of the
     // previous piece is in flight any more), so that no later wait on the
     // Q registers can count the unit loads in flight.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    if (my_n > 0) {
-      issue(0, page_of(0), IntTag<0>{});
-      page_nx = page_of(1);
-    }
-    for (int k = 0; k < my_n; k += 2) {
-      step(k, IntTag<0>{});
-      if (k + 1 < my_n) step(k + 1, IntTag<1>{});
+    wait_vm<0>();
+    static_for<0, NST - 1>([&](auto i_tag) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_tag)::value;
+      if (i < my_n) issue(i, page_of(i), IntTag<i>{});
+    });
+    page_nx = page_of(NST - 1);
+    for (int k = 0; k < my_n; k += NST) {
+      static_for<0, NST>([&](auto i_tag) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_tag)::value;
+        if (k + i < my_n) step(k + i, IntTag<i>{});
+      });
     }
 
     // Merge the waves' (m, l, O^T) through LDS: O^T partials go to each
@@ -1733,6 +1755,10 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
     }
     cur += n_units;
   }
+  if (u0 == u1 && tid < kDecCols) {
+    // Empty range: a pair cut around it finds an empty piece in its slot.
+    p.bal_part[(size_t)(2 * wg) * (kDecCols * (D + 1)) + kDecCols * D + tid] = neg_inf();
+  }
   if (tid == 0) {
     int32_t *dsc = p.bal_desc + wg * kBalDescInts;
     dsc[0] = own_b;
@@ -1751,53 +1777,83 @@ __global__ __launch_bounds__(64 * kBalWaves, 1) void decode_balanced_kernel(Attn
 
 // Merges the pieces of the pair recorded by decode workgroup blockIdx.x: its
 // own piece, then the first piece of every later workgroup up to the one
-// holding the pair's last unit (workgroups with empty ranges hold none).
+// holding the pair's last unit (a workgroup with an empty range marks its
+// slot empty).  The pieces' LSEs are gathered and turned into weights in
+// LDS first, so that the partial loads of all pieces can be in flight
+// together.
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_balanced_kernel(AttnParams p) {
+  __shared__ float wts[kBalMaxWGs][kDecCols];
+  __shared__ float red[2][kThreads / 64][kDecCols];
   const int wg = blockIdx.x;
   const int32_t *dsc = p.bal_desc + wg * kBalDescInts;
   const int b = dsc[0];
   if (b < 0) return;
-  const int g = dsc[1], w_last = dsc[2], which = dsc[3], TU = dsc[4];
-  const int nwg = p.bal_wgs, G = p.G;
+  const int g = dsc[1], w_last = dsc[2], which = dsc[3];
+  const int np = w_last - wg + 1;
+  const int G = p.G;
   const int tok0 = p.cu_seqlens_q[b];
   const int ncols = (p.cu_seqlens_q[b + 1] - tok0) * G;
-  constexpr int DPG = D * kDecCols / kThreads;
   constexpr int SLOT = kDecCols * (D + 1);
-  const int fc = threadIdx.x & 15, fg = threadIdx.x >> 4;
-  if (fc >= ncols) return;
-  auto for_pieces = [&](auto f) {
-    f(2 * wg + which);
-    for (int w2 = wg + 1; w2 <= w_last; ++w2)
-      if (bal_unit_at(TU, w2, nwg) < bal_unit_at(TU, w2 + 1, nwg)) f(2 * w2);
-  };
+  constexpr int DPG = D * kDecCols / kThreads;
+  auto slot_of = [&](int i) { return (size_t)(i == 0 ? 2 * wg + which : 2 * (wg + i)) * SLOT; };
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int x = tid; x < np * kDecCols; x += kThreads)
+    wts[x / kDecCols][x % kDecCols] = p.bal_part[slot_of(x / kDecCols) + kDecCols * D + x % kDecCols];
+  __syncthreads();
+  // Column c = tid % 16 is reduced by the 16 threads tid / 16.
+  const int c = tid & 15, sub = tid >> 4;
   float M = neg_inf();
-  for_pieces([&](int s) { M = fmaxf(M, p.bal_part[(size_t)s * SLOT + kDecCols * D + fc]); });
-  const int fqi = fc / G;
-  const int fhead = g * G + (fc - fqi * G);
-  const int ftok = tok0 + fqi;
-  uint16_t *op = p.out + ((int64_t)ftok * p.H + fhead) * D + fg * DPG;
+  for (int i = sub; i < np; i += kThreads / kDecCols) M = fmaxf(M, wts[i][c]);
+  M = fmaxf(M, __shfl_xor(M, 16));
+  M = fmaxf(M, __shfl_xor(M, 32));
+  if (lane < 16) red[0][wv][c] = M;
+  __syncthreads();
+#pragma unroll
+  for (int ww = 0; ww < kThreads / 64; ++ww) M = fmaxf(M, red[0][ww][c]);
+  float W = 0.f;
+  if (M != neg_inf()) {
+    for (int i = sub; i < np; i += kThreads / kDecCols) {
+      const float ls = wts[i][c];
+      W += ls == neg_inf() ? 0.f : exp2_fast((ls - M) * kLog2e);
+    }
+  }
+  W += __shfl_xor(W, 16);
+  W += __shfl_xor(W, 32);
+  if (lane < 16) red[1][wv][c] = W;
+  __syncthreads();
+  W = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < kThreads / 64; ++ww) W += red[1][ww][c];
+  const float invW = W > 0.f ? 1.f / W : 0.f;
+  for (int i = sub; i < np; i += kThreads / kDecCols) {
+    const float ls = wts[i][c];
+    wts[i][c] = ls == neg_inf() ? 0.f : exp2_fast((ls - M) * kLog2e) * invW;
+  }
+  __syncthreads();
+  if (c >= ncols) return;
+  // Thread (c, sub) owns head_dim values [sub * DPG, sub * DPG + DPG).
   float o[DPG];
 #pragma unroll
   for (int e = 0; e < DPG; ++e) o[e] = 0.f;
-  float W = 0.f;
-  if (M != neg_inf()) {
-    for_pieces([&](int s) {
-      const float ls = p.bal_part[(size_t)s * SLOT + kDecCols * D + fc];
-      W += ls == neg_inf() ? 0.f : exp2_fast((ls - M) * kLog2e);
-    });
-    const float invW = 1.f / W;
-    for_pieces([&](int s) {
-      const float ls = p.bal_part[(size_t)s * SLOT + kDecCols * D + fc];
-      const float wt = ls == neg_inf() ? 0.f : exp2_fast((ls - M) * kLog2e) * invW;
-      const float *src = p.bal_part + (size_t)s * SLOT + fc * D + fg * DPG;
+#pragma unroll 4
+  for (int i = 0; i < np; ++i) {
+    const float wt = wts[i][c];
+    const float *src = p.bal_part + slot_of(i) + c * D + sub * DPG;
+    f32x4 v[DPG / 4];
 #pragma unroll
-      for (int e = 0; e < DPG; ++e) o[e] += wt * src[e];
-    });
+    for (int e = 0; e < DPG / 4; ++e) v[e] = reinterpret_cast<const f32x4 *>(src)[e];
+    // An empty piece has weight 0 and may hold anything: select, not scale.
+#pragma unroll
+    for (int e = 0; e < DPG; ++e) o[e] += wt != 0.f ? wt * v[e / 4][e % 4] : 0.f;
   }
+  const int fqi = c / G;
+  const int fhead = g * G + (c - fqi * G);
+  const int ftok = tok0 + fqi;
+  uint16_t *op = p.out + ((int64_t)ftok * p.H + fhead) * D + sub * DPG;
 #pragma unroll
   for (int e = 0; e < DPG; e += 2) reinterpret_cast<uint32_t *>(op)[e / 2] = pack2_bf16(o[e], o[e + 1]);
-  if (fg == 0 && p.lse) p.lse[(int64_t)ftok * p.H + fhead] = M == neg_inf() ? neg_inf() : M + log2_fast(W) * kLn2;
+  if (sub == 0 && p.lse) p.lse[(int64_t)ftok * p.H + fhead] = M == neg_inf() ? neg_inf() : M + log2_fast(W) * kLn2;
 }
 
 // ---------------------------------------------------------------- combine
