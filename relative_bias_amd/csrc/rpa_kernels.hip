@@ -1313,8 +1313,9 @@ struct BalLds {
   static constexpr int stageBytes = 2 * halfBytes;
   static constexpr int NST = kBalStages;       // stages per wave
   static constexpr int biasOff = kBalWaves * NST * stageBytes;  // per wave and stage: 4 x 64 fp32
-  static constexpr int mlOff = biasOff + kBalWaves * NST * 1024;
-  static constexpr int prefixOff = mlOff + 2 * kBalWaves * kDecCols * 4;
+  static constexpr int mlOff = biasOff + kBalWaves * NST * 1024;     // merge: m, then l [waves][16]
+  static constexpr int slotOff = mlOff + 2 * kBalWaves * kDecCols * 4;  // merge: each wave's stage
+  static constexpr int prefixOff = slotOff + 64;
   static constexpr int bytes = prefixOff + (kBalMaxBatch + 1) * 4;
   // A wave's O^T partial (D x 16 fp32) fits in one of its stages.
   static_assert(D * kDecCols * 4 <= stageBytes, "merge buffer");
@@ -1374,6 +1375,45 @@ __device__ __forceinline__ float lds_read_f32_asm(uint32_t addr) {
   asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");
   return v;
 }
+__device__ __forceinline__ int lds_read_i32_now(uint32_t addr) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+// LDS writes in inline asm complete before the asm ends: the compiler's
+// hazard checks do not see inside asm, and the data registers may be
+// overwritten by the next instruction.
+__device__ __forceinline__ void lds_write_b32_now(uint32_t addr, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_write4_b128_now(const uint32_t (&a)[4], const f32x4 (&v)[4]) {
+  asm volatile(
+      "ds_write_b128 %0, %4\n\tds_write_b128 %1, %5\n\tds_write_b128 %2, %6\n\tds_write_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      :
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3])
+      : "memory");
+}
+__device__ __forceinline__ void lgkm_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
+// Eight LDS reads in flight together, then one wait that the results depend on.
+__device__ __forceinline__ void lds_read8_b32(uint32_t a0, uint32_t stride, uint32_t (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("ds_read_b32 %0, %1" : "=v"(v[i]) : "v"(a0 + i * stride) : "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
+}
+__device__ __forceinline__ void lds_read8_b128(const uint32_t (&a)[8], u32x4 (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("ds_read_b128 %0, %1" : "=v"(v[i]) : "v"(a[i]) : "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
+}
+__device__ __forceinline__ void lds_read8_b64(const uint32_t (&a)[8], u32x2 (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("ds_read_b64 %0, %1" : "=v"(v[i]) : "v"(a[i]) : "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
+}
 __device__ __forceinline__ u32x2 lds_read_tr_at(uint32_t addr) {
   u32x2 v;
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr) : "memory");
@@ -1431,13 +1471,10 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
   using L = BalLds<D>;
   constexpr int NW = kBalWaves;
   constexpr int QK = D / 32, DB = D / 16, NI = L::NI, RPI = L::RPI, UNITS = L::UNITS, ROWB = L::ROWB;
-  constexpr int NST = L::NST;
+  static_assert(L::NST == 2, "two stages per wave: one computed, one in flight");
   constexpr int NPER = 2 * NI + (BIAS ? 4 : 0);  // vector-memory instructions per unit
-  static_assert(NPER * (NST - 1) < 64, "vmcnt range");
   int32_t *prefix = reinterpret_cast<int32_t *>(smem + L::prefixOff);
-  float *red_m = reinterpret_cast<float *>(smem + L::mlOff);
-  float *red_l = red_m + NW * kDecCols;
-  bal_prefix(p, prefix, reinterpret_cast<int32_t *>(red_m));
+  bal_prefix(p, prefix, reinterpret_cast<int32_t *>(smem + L::mlOff));
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1446,6 +1483,16 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
   const int nwg = p.bal_wgs, wg = blockIdx.x;
   const int TU = __builtin_amdgcn_readfirstlane(prefix[B]);
   const int u0 = bal_unit_at(TU, wg, nwg), u1 = bal_unit_at(TU, wg + 1, nwg);
+  int b_it = 0;
+  {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (prefix[mid] <= u0) lo = mid;
+      else hi = mid - 1;
+    }
+    b_it = __builtin_amdgcn_readfirstlane(lo);
+  }
 
   const uint32_t slot_bytes = (uint32_t)Hkv * D * 2;
   uint32_t gk[NI], gv[NI];
@@ -1464,296 +1511,358 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
     for (int db = 0; db < DB; ++db)
       lv_off[db] = L::halfBytes + row * ROWB + ((((2 * db + (t >> 1)) ^ swz_vt<D>(row)) << 4)) + 8 * (t & 1);
   }
-  const uint32_t lds_wave = (uint32_t)(uintptr_t)smem + (uint32_t)(w * L::NST * L::stageBytes);
-  const uint32_t lds_bias = (uint32_t)(uintptr_t)smem + (uint32_t)(L::biasOff + w * L::NST * 1024 + 4 * lane);
+  const uint32_t smem_u = (uint32_t)(uintptr_t)smem;
+  const uint32_t lds_wave = smem_u + (uint32_t)(w * 2 * L::stageBytes);
+  const uint32_t lds_bias = smem_u + (uint32_t)(L::biasOff + w * 2 * 1024 + 4 * lane);
+  const uint32_t lds_m = smem_u + L::mlOff, lds_l = lds_m + NW * kDecCols * 4;
+  const uint32_t lds_slot = smem_u + L::slotOff;
+  const uint32_t lds_prefix = smem_u + L::prefixOff;
   const float c = p.scale_log2;
   const bool pos_scale = c > 0.f;
   const uint32_t bias_bytes = BIAS ? (uint32_t)p.num_tokens * (uint32_t)p.H * (uint32_t)p.R * 4u : 0u;
 
-  int own_b = -1, own_g = 0, own_last = 0, own_which = 0;
-  int b = 0;
-  {
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (prefix[mid] <= u0) lo = mid;
-      else hi = mid - 1;
-    }
-    b = __builtin_amdgcn_readfirstlane(lo);
-  }
-  int cur = u0;
-  while (cur < u1) {
-    while (__builtin_amdgcn_readfirstlane(prefix[b + 1]) <= cur) ++b;
-    const int pb = __builtin_amdgcn_readfirstlane(prefix[b]);
-    const int nu = (__builtin_amdgcn_readfirstlane(prefix[b + 1]) - pb) / Hkv;
+  // A piece: units [j0, j1) of pair (b, g) inside this workgroup's range,
+  // with what its rows need (uniform fields, then the lane's column).
+  struct Piece {
+    int b, g, j0, j1, nu, which, pair_start;
+    int tok0, lq, ncols, lo_a, kend, in_lo, in_hi, band_lo, band_hi, my_n;
+    int qa, lo_c, hi_c, tok, head;
+    uint32_t rel_base;
+  };
+  // LDS reads while direct loads are in flight go through inline asm (the
+  // compiler would wait for the loads first).
+  auto prefix_at = [&](int i) { return __builtin_amdgcn_readfirstlane(lds_read_i32_now(lds_prefix + 4u * i)); };
+  auto make_piece = [&](int cur) __attribute__((always_inline)) {
+    Piece P;
+    while (prefix_at(b_it + 1) <= cur) ++b_it;
+    P.b = b_it;
+    const int pb = prefix_at(b_it);
+    P.nu = (prefix_at(b_it + 1) - pb) / Hkv;
     const int off = cur - pb;
-    const int g = off / nu, j0 = off - g * nu;
-    const int j1 = min(nu, j0 + (u1 - cur));
-    const int which = cur == u0 ? 0 : 1;
-
-    const int tok0 = __builtin_amdgcn_readfirstlane(p.cu_seqlens_q[b]);
-    const int lq = __builtin_amdgcn_readfirstlane(p.cu_seqlens_q[b + 1]) - tok0;
-    const int lk = __builtin_amdgcn_readfirstlane(p.cache_seqlens[b]);
-    const int ncols = lq * G;
-    const int col = c16 < ncols ? c16 : ncols - 1;
+    P.g = off / P.nu;
+    P.j0 = off - P.g * P.nu;
+    P.j1 = min(P.nu, P.j0 + (u1 - cur));
+    P.which = cur == u0 ? 0 : 1;
+    P.pair_start = pb + P.g * P.nu;
+    P.tok0 = scalar_load_i32(p.cu_seqlens_q + P.b);
+    P.lq = scalar_load_i32(p.cu_seqlens_q + P.b + 1) - P.tok0;
+    const int lk = scalar_load_i32(p.cache_seqlens + P.b);
+    P.ncols = P.lq * G;
+    const int col = c16 < P.ncols ? c16 : P.ncols - 1;
     const int qi = col / G;
-    const int head = g * G + (col - qi * G);
-    const int tok = tok0 + qi;
-    const int qa = qi + lk - lq;
-    const int qa_min = lk - lq, qa_max = lk - 1;
+    P.head = P.g * G + (col - qi * G);
+    P.tok = P.tok0 + qi;
+    P.qa = qi + lk - P.lq;
+    const int qa_min = lk - P.lq, qa_max = lk - 1;
     const Range vr = visible_range(p, lk, qa_min, qa_max);
-    const int lo_a = vr.lo & ~15;
-    const int kend = min(lk, vr.hi);
-    int lo_c = lo_a, hi_c = kend - 1;
-    if (p.left >= 0) lo_c = max(lo_c, qa - p.left);
-    if (p.causal) hi_c = min(hi_c, qa);
-    if (p.right >= 0) hi_c = min(hi_c, qa + p.right);
-    int in_lo = lo_a, in_hi = kend - 1;
-    if (p.left >= 0) in_lo = max(in_lo, qa_max - p.left);
-    if (p.causal) in_hi = min(in_hi, qa_min);
-    if (p.right >= 0) in_hi = min(in_hi, qa_min + p.right);
-    const int band_lo = qa_min - p.R + 1, band_hi = qa_max;
-    const uint32_t rel_base = BIAS ? (uint32_t)((tok * p.H + head) * p.R) : 0u;
+    P.lo_a = vr.lo & ~15;
+    P.kend = min(lk, vr.hi);
+    P.lo_c = P.lo_a;
+    P.hi_c = P.kend - 1;
+    if (p.left >= 0) P.lo_c = max(P.lo_c, P.qa - p.left);
+    if (p.causal) P.hi_c = min(P.hi_c, P.qa);
+    if (p.right >= 0) P.hi_c = min(P.hi_c, P.qa + p.right);
+    P.in_lo = P.lo_a;
+    P.in_hi = P.kend - 1;
+    if (p.left >= 0) P.in_lo = max(P.in_lo, qa_max - p.left);
+    if (p.causal) P.in_hi = min(P.in_hi, qa_min);
+    if (p.right >= 0) P.in_hi = min(P.in_hi, qa_min + p.right);
+    P.band_lo = qa_min - p.R + 1;
+    P.band_hi = qa_max;
+    P.rel_base = BIAS ? (uint32_t)((P.tok * p.H + P.head) * p.R) : 0u;
+    const int n_units = P.j1 - P.j0;
+    P.my_n = n_units > w ? (n_units - w + NW - 1) / NW : 0;
+    return P;
+  };
+  auto key_of = [&](const Piece &P, int k) { return P.lo_a + 16 * (P.j0 + w + NW * k); };
+  auto in_band = [&](const Piece &P, int key0) { return BIAS && key0 <= P.band_hi && key0 + 15 >= P.band_lo; };
+  // Page ids come from scalar loads one unit ahead of their use.
+  auto page_of = [&](const Piece &P, int k) -> int {
+    const int key = key_of(P, k);
+    if (k >= P.my_n || key >= P.kend) return 0;
+    return scalar_load_i32(p.block_table + (int64_t)P.b * p.P + (p.bs_shift >= 0 ? (key >> p.bs_shift) : key / p.BS));
+  };
+  auto load_q = [&](const Piece &P, bf16x8 (&qf)[QK]) __attribute__((always_inline)) {
+    const uint16_t *qp = p.q + ((int64_t)P.tok * p.H + P.head) * D + 8 * q;
+#pragma unroll
+    for (int ks = 0; ks < QK; ++ks) qf[ks] = as_bf16x8(ld16(qp + 32 * ks));
+  };
 
+  auto issue = [&](const Piece &P, int k, int page, int slot) __attribute__((always_inline)) {
+    const int key0 = __builtin_amdgcn_readfirstlane(key_of(P, k));
+    const int nvalid = __builtin_amdgcn_readfirstlane(min(max(P.kend - key0, 0), 16));
+    const int slot0 = p.bs_shift >= 0 ? (key0 & (p.BS - 1)) : key0 % p.BS;
+    const int64_t eoff = (((int64_t)page * p.BS + slot0) * Hkv + P.g) * D;
+    const auto rk = make_rsrc(p.k + eoff, (uint32_t)nvalid * slot_bytes);
+    const auto rv = make_rsrc(p.v + eoff, (uint32_t)nvalid * slot_bytes);
+    if constexpr (BIAS) {
+      // Raw logits of the lane's four keys (distance clamped into the row;
+      // the band test in compute() discards what lies outside it), through
+      // an empty resource outside the band, so that every unit counts the
+      // same vector-memory instructions.
+      const auto brs = make_rsrc(p.rel_logits, in_band(P, key0) ? bias_bytes : 0u);
+      char *bst = smem + L::biasOff + (w * 2 + slot) * 1024;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = min(max(P.qa - (key0 + 4 * q + j), 0), p.R - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (__attribute__((address_space(3))) void *)(bst + 256 * j), 4,
+                                                 (P.rel_base + (uint32_t)d) * 4u, 0, 0, 0);
+      }
+    }
+    char *st = smem + (w * 2 + slot) * L::stageBytes;
+#pragma unroll
+    for (int n = 0; n < NI; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void *)(st + n * 1024), 16,
+                                               gk[n], 0, 0, 0);
+#pragma unroll
+    for (int n = 0; n < NI; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void *)(st + L::halfBytes + n * 1024), 16, gv[n], 0, 0, 0);
+  };
+
+  f32x4 oacc[DB];
+  float m_run, l_run;
+  auto compute = [&](const Piece &P, int k, int slot, const bf16x8 (&qf)[QK]) __attribute__((always_inline)) {
+    const int key0 = __builtin_amdgcn_readfirstlane(key_of(P, k));
+    const uint32_t st = lds_wave + slot * L::stageBytes;
+    u32x4 kf[QK];
+#pragma unroll
+    for (int ks = 0; ks < QK; ++ks) kf[ks] = lds_read_b128_asm(st + lk_off[ks]);
+    u32x2 va[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) va[db] = lds_read_tr_at(st + lv_off[db]);
+    // LDS reads complete in order: the K operands are in once at most the
+    // DB V reads issued after them are outstanding.
+    lgkm_wait_n<DB>(kf);
+    f32x4 sacc = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < QK; ++ks) sacc = mfma16(as_bf16x8(kf[ks]), qf[ks], sacc);
+    // Lane (c16, q) holds S[col c16][key key0 + 4q + j].
+    const bool interior = key0 >= P.in_lo && key0 + 15 <= P.in_hi;
+    const bool band = in_band(P, key0);
+    const bool plain = interior && !band;
+    float mx = neg_inf();
+    if (plain) {
+      if (pos_scale) {
+        mx = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3])) * c;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sacc[j] * c);
+      }
+    } else {
+      float bias[4] = {0.f, 0.f, 0.f, 0.f};
+      if (band) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bias[j] = lds_read_f32_asm(lds_bias + slot * 1024 + 256 * j);
+        lgkm_wait_n<0>(bias);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = key0 + 4 * q + j;
+        float v = sacc[j] * c;
+        if (band && (unsigned)(P.qa - t) < (unsigned)p.R) v = __builtin_fmaf(bias[j], kLog2e, v);
+        if (t < P.lo_c || t > P.hi_c) v = neg_inf();
+        sacc[j] = v;
+        mx = fmaxf(mx, v);
+      }
+    }
+    mx = xor16_max(mx);
+    mx = xor32_max(mx);
+    if (__any(mx > m_run + kTau)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == neg_inf() ? 1.f : exp2_fast(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+    const float m_use = m_run == neg_inf() ? 0.f : m_run;
+    float pe[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pe[j] = exp2_fast(plain ? __builtin_fmaf(sacc[j], c, -m_use) : sacc[j] - m_use);
+    l_run += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+    const u32x2 pf = u32x2{pack2_bf16(pe[0], pe[1]), pack2_bf16(pe[2], pe[3])};
+    lgkm_wait_n<0>(va);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = mfma16k16(va[db], pf, oacc[db]);
+  };
+
+  int own_b = -1, own_g = 0, own_last = 0, own_which = 0;
+  int cur = u0;
+  if (cur < u1) {
+    Piece P = make_piece(cur);
     bf16x8 qf[QK];
-    {
-      const uint16_t *qp = p.q + ((int64_t)tok * p.H + head) * D + 8 * q;
-#pragma unroll
-      for (int ks = 0; ks < QK; ++ks) qf[ks] = as_bf16x8(ld16(qp + 32 * ks));
-    }
-    f32x4 oacc[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] = f32x4{};
-    float m_run = neg_inf(), l_run = 0.f;
-
-    const int n_units = j1 - j0;
-    const int my_n = n_units > w ? (n_units - w + NW - 1) / NW : 0;
-    // Page ids are read by scalar loads one unit ahead of their use.
-    const int32_t *bt = p.block_table + (int64_t)b * p.P;
-    auto key_of_unit = [&](int k) { return lo_a + 16 * (j0 + w + NW * k); };
-    auto page_of = [&](int k) -> int {
-      const int key = key_of_unit(k);
-      if (k >= my_n || key >= kend) return 0;
-      return scalar_load_i32(bt + (p.bs_shift >= 0 ? (key >> p.bs_shift) : key / p.BS));
-    };
-    auto in_band = [&](int key0) { return BIAS && key0 <= band_hi && key0 + 15 >= band_lo; };
-
-    auto issue = [&](int k, int page, auto s_tag) __attribute__((always_inline)) {
-      constexpr int S = decltype(s_tag)::value;
-      const int key0 = __builtin_amdgcn_readfirstlane(key_of_unit(k));
-      const int nvalid = __builtin_amdgcn_readfirstlane(min(max(kend - key0, 0), 16));
-      const int slot0 = p.bs_shift >= 0 ? (key0 & (p.BS - 1)) : key0 % p.BS;
-      const int64_t eoff = (((int64_t)page * p.BS + slot0) * Hkv + g) * D;
-      const auto rk = make_rsrc(p.k + eoff, (uint32_t)nvalid * slot_bytes);
-      const auto rv = make_rsrc(p.v + eoff, (uint32_t)nvalid * slot_bytes);
-      if constexpr (BIAS) {
-        // Raw logits of the lane's four keys (distance clamped into the
-        // row; the band test in compute() discards what lies outside it).
-        // Issued for every unit, through an empty resource outside the
-        // band, so that every unit counts the same vector-memory ops.
-        const auto brs = make_rsrc(p.rel_logits, in_band(key0) ? bias_bytes : 0u);
-        char *bst = smem + L::biasOff + (w * L::NST + S) * 1024;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = min(max(qa - (key0 + 4 * q + j), 0), p.R - 1);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (__attribute__((address_space(3))) void *)(bst + 256 * j), 4,
-                                                   (rel_base + (uint32_t)d) * 4u, 0, 0, 0);
-        }
-      }
-      char *st = smem + (w * L::NST + S) * L::stageBytes;
-#pragma unroll
-      for (int n = 0; n < NI; ++n)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void *)(st + n * 1024), 16,
-                                                 gk[n], 0, 0, 0);
-#pragma unroll
-      for (int n = 0; n < NI; ++n)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, (__attribute__((address_space(3))) void *)(st + L::halfBytes + n * 1024), 16, gv[n], 0, 0, 0);
-    };
-
-    auto compute = [&](int k, auto s_tag) __attribute__((always_inline)) {
-      constexpr int S = decltype(s_tag)::value;
-      const int key0 = __builtin_amdgcn_readfirstlane(key_of_unit(k));
-      const uint32_t st = lds_wave + S * L::stageBytes;
-      u32x4 kf[QK];
-#pragma unroll
-      for (int ks = 0; ks < QK; ++ks) kf[ks] = lds_read_b128_asm(st + lk_off[ks]);
-      u32x2 va[DB];
-#pragma unroll
-      for (int db = 0; db < DB; ++db) va[db] = lds_read_tr_at(st + lv_off[db]);
-      // LDS reads complete in order: the K operands are in once at most the
-      // DB V reads issued after them are outstanding.
-      lgkm_wait_n<DB>(kf);
-      f32x4 sacc = f32x4{};
-#pragma unroll
-      for (int ks = 0; ks < QK; ++ks) sacc = mfma16(as_bf16x8(kf[ks]), qf[ks], sacc);
-      // Lane (c16, q) holds S[col c16][key key0 + 4q + j].
-      const bool interior = key0 >= in_lo && key0 + 15 <= in_hi;
-      const bool band = in_band(key0);
-      const bool plain = interior && !band;
-      float mx = neg_inf();
-      if (plain) {
-        if (pos_scale) {
-          mx = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3])) * c;
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sacc[j] * c);
-        }
-      } else {
-        float bias[4] = {0.f, 0.f, 0.f, 0.f};
-        if (band) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) bias[j] = lds_read_f32_asm(lds_bias + S * 1024 + 256 * j);
-          lgkm_wait_n<0>(bias);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = key0 + 4 * q + j;
-          float v = sacc[j] * c;
-          if (band && (unsigned)(qa - t) < (unsigned)p.R) v = __builtin_fmaf(bias[j], kLog2e, v);
-          if (t < lo_c || t > hi_c) v = neg_inf();
-          sacc[j] = v;
-          mx = fmaxf(mx, v);
-        }
-      }
-      mx = xor16_max(mx);
-      mx = xor32_max(mx);
-      if (__any(mx > m_run + kTau)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_new == neg_inf() ? 1.f : exp2_fast(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      }
-      const float m_use = m_run == neg_inf() ? 0.f : m_run;
-      float pe[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pe[j] = exp2_fast(plain ? __builtin_fmaf(sacc[j], c, -m_use) : sacc[j] - m_use);
-      l_run += (pe[0] + pe[1]) + (pe[2] + pe[3]);
-      const u32x2 pf = u32x2{pack2_bf16(pe[0], pe[1]), pack2_bf16(pe[2], pe[3])};
-      lgkm_wait_n<0>(va);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] = mfma16k16(va[db], pf, oacc[db]);
-    };
-
-    // The direct loads write LDS behind the compiler's back: their
-    // completion is awaited explicitly (vmcnt counts this wave's vector
-    // memory instructions in issue order, NPER per unit).  Unit k uses
-    // stage k % NST; units k+1 .. k+NST-1 are in flight while it is
-    // computed.
-    int page_nx = 0;
-    auto step = [&](int k, auto s_tag) __attribute__((always_inline)) {
-      constexpr int S = decltype(s_tag)::value;
-      if (k + NST - 1 < my_n) {
-        issue(k + NST - 1, page_nx, IntTag<(S + NST - 1) % NST>{});
-        page_nx = page_of(k + NST);
-        wait_vm<NPER * (NST - 1)>();
-      } else {
-        const int after = my_n - 1 - k;  // units issued after k
-        static_for<0, NST - 1>([&](auto i_tag) __attribute__((always_inline)) {
-          constexpr int i = decltype(i_tag)::value;
-          if (after == i) wait_vm<NPER * i>();
-        });
-      }
-      compute(k, s_tag);
-    };
-    // Q is in before the first direct load is issued (nothing of the
-    // previous piece is in flight any more), so that no later wait on the
-    // Q registers can count the unit loads in flight.
+    load_q(P, qf);
+    // Q is in before the first direct load is issued, so that no later
+    // wait on the Q registers can count the unit loads in flight.
     wait_vm<0>();
-    static_for<0, NST - 1>([&](auto i_tag) __attribute__((always_inline)) {
-      constexpr int i = decltype(i_tag)::value;
-      if (i < my_n) issue(i, page_of(i), IntTag<i>{});
-    });
-    page_nx = page_of(NST - 1);
-    for (int k = 0; k < my_n; k += NST) {
-      static_for<0, NST>([&](auto i_tag) __attribute__((always_inline)) {
-        constexpr int i = decltype(i_tag)::value;
-        if (k + i < my_n) step(k + i, IntTag<i>{});
-      });
-    }
+    int slot0 = 0;        // stage of this wave's first unit of P
+    if (P.my_n > 0) issue(P, 0, page_of(P, 0), 0);
+    while (true) {
+      const int cur_next = cur + (P.j1 - P.j0);
+      const bool has_next = cur_next < u1;
+      Piece N;
+      int page_n0 = 0;
+      if (has_next) {
+        N = make_piece(cur_next);
+        page_n0 = page_of(N, 0);
+      }
+      const bool pre_n = has_next && N.my_n > 0;  // this wave prefetches N's first unit
+      int page_nx = page_of(P, 1);
+      bf16x8 qn[QK];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = f32x4{};
+      m_run = neg_inf();
+      l_run = 0.f;
+      // The direct loads write LDS behind the compiler's back: their
+      // completion is awaited explicitly (vmcnt counts this wave's
+      // vector-memory instructions in issue order).  While unit k is
+      // computed the next unit of this wave's stream is in flight: unit
+      // k+1 of P or, after P's last, unit 0 of the next piece.
+      int pslot = -1;  // stage holding the next piece's first unit
+      for (int k = 0; k < P.my_n; ++k) {
+        const int sk = (slot0 + k) & 1;
+        if (k + 1 < P.my_n) {
+          issue(P, k + 1, page_nx, sk ^ 1);
+          page_nx = page_of(P, k + 2);
+          wait_vm<NPER>();
+        } else if (pre_n) {
+          load_q(N, qn);
+          issue(N, 0, page_n0, sk ^ 1);
+          pslot = sk ^ 1;
+          wait_vm<NPER>();
+        } else {
+          wait_vm<0>();
+        }
+        compute(P, k, sk, qf);
+      }
+      if (P.my_n == 0 && pre_n) {
+        load_q(N, qn);
+        issue(N, 0, page_n0, 0);
+        pslot = 0;
+      }
 
-    // Merge the waves' (m, l, O^T) through LDS: O^T partials go to each
-    // wave's first stage (its loads and reads of this piece are complete).
-    const float l_col = xor32_sum(xor16_sum(l_run));
-    float *red_o = reinterpret_cast<float *>(smem + w * L::NST * L::stageBytes);
-    if (q == 0) {
-      red_m[w * kDecCols + c16] = m_run;
-      red_l[w * kDecCols + c16] = l_col;
-    }
+      // Merge the waves' (m, l, O^T) through LDS: each wave's O^T goes to
+      // its stage that holds no load in flight.  Raw barriers (no memory
+      // fence) keep the next piece's loads in flight across the merge.
+      const float l_col = xor32_sum(xor16_sum(l_run));
+      const int rs = pslot == 0 ? 1 : 0;
+      {
+        const uint32_t red = lds_wave + rs * L::stageBytes;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+        for (int d4 = 0; d4 < DB; d4 += 4) {
+          uint32_t a[4];
+          f32x4 v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) red_o[(16 * db + 4 * q + j) * kDecCols + c16] = oacc[db][j];
-    __syncthreads();
-    {
-      constexpr int DPG = D * kDecCols / (64 * NW);
-      const int fc = tid & 15, fg = tid >> 4;
-      if (fc < ncols) {
-        float mw[NW], sc[NW];
-        float M = neg_inf();
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-          mw[ww] = red_m[ww * kDecCols + fc];
-          M = fmaxf(M, mw[ww]);
+          for (int i = 0; i < 4; ++i) {
+            a[i] = red + ((4 * (d4 + i) + q) * kDecCols + c16) * 16;
+            v[i] = oacc[d4 + i];
+          }
+          lds_write4_b128_now(a, v);
         }
-        float Lsum = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-          sc[ww] = mw[ww] == neg_inf() ? 0.f : exp2_fast(mw[ww] - M);
-          Lsum += sc[ww] * red_l[ww * kDecCols + fc];
+        if (q == 0) {
+          lds_write_b32_now(lds_m + (w * kDecCols + c16) * 4, __builtin_bit_cast(uint32_t, m_run));
+          lds_write_b32_now(lds_l + (w * kDecCols + c16) * 4, __builtin_bit_cast(uint32_t, l_col));
         }
-        const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-        const float lse_v = Lsum > 0.f ? (M + log2_fast(Lsum)) * kLn2 : neg_inf();
-        float o[DPG];
+        if (lane == 0) lds_write_b32_now(lds_slot + 4 * w, (uint32_t)rs);
+      }
+      lgkm_wait_all();
+      __builtin_amdgcn_s_barrier();
+      {
+        constexpr int DPG = D * kDecCols / (64 * NW);
+        const int fc = tid & 15, fg = tid >> 4;
+        if (fc < P.ncols) {
+          uint32_t sl[NW], mw[NW], lw[NW];
+          lds_read8_b32(lds_slot, 4, sl);
+          lds_read8_b32(lds_m + fc * 4, kDecCols * 4, mw);
+          lds_read8_b32(lds_l + fc * 4, kDecCols * 4, lw);
+          float M = neg_inf();
 #pragma unroll
-        for (int e = 0; e < DPG; ++e) {
-          const int d = fg * DPG + e;
-          float acc = 0.f;
+          for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, __builtin_bit_cast(float, mw[ww]));
+          float sc[NW];
+          float Lsum = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < NW; ++ww) {
+            const float m_w = __builtin_bit_cast(float, mw[ww]);
+            sc[ww] = m_w == neg_inf() ? 0.f : exp2_fast(m_w - M);
+            Lsum += sc[ww] * __builtin_bit_cast(float, lw[ww]);
+          }
+          const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+          const float lse_v = Lsum > 0.f ? (M + log2_fast(Lsum)) * kLn2 : neg_inf();
+          // O^T of wave ww, head_dim d, column fc sits at float
+          // ((d / 4) * 16 + fc) * 4 + d % 4 of its merge stage.
+          uint32_t oaddr[NW];
 #pragma unroll
           for (int ww = 0; ww < NW; ++ww)
-            acc += sc[ww] * reinterpret_cast<const float *>(smem + ww * L::NST * L::stageBytes)[d * kDecCols + fc];
-          o[e] = acc * inv;
-        }
-        const int fqi = fc / G;
-        const int fhead = g * G + (fc - fqi * G);
-        const int ftok = tok0 + fqi;
-        if (j0 == 0 && j1 == nu) {
-          uint16_t *op = p.out + ((int64_t)ftok * p.H + fhead) * D + fg * DPG;
+            oaddr[ww] = smem_u + (uint32_t)((ww * 2 + (int)sl[ww]) * L::stageBytes) +
+                        ((((fg * DPG) >> 2) * kDecCols + fc) * 4 + ((fg * DPG) & 3)) * 4;
+          float o[DPG];
           if constexpr (DPG == 4) {
-            *reinterpret_cast<u32x2 *>(op) = u32x2{pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3])};
+            u32x4 part[NW];
+            lds_read8_b128(oaddr, part);
+            // Whole vectors are bit-cast: a bit_cast of one ext-vector
+            // element is not reliable with this compiler.
+            f32x4 acc = f32x4{};
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) acc += sc[ww] * __builtin_bit_cast(f32x4, part[ww]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = acc[e] * inv;
           } else {
-            *reinterpret_cast<uint32_t *>(op) = pack2_bf16(o[0], o[1]);
+            u32x2 part[NW];
+            lds_read8_b64(oaddr, part);
+            f32x2 acc = f32x2{};
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) acc += sc[ww] * __builtin_bit_cast(f32x2, part[ww]);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) o[e] = acc[e] * inv;
           }
-          if (fg == 0 && p.lse) p.lse[(int64_t)ftok * p.H + fhead] = lse_v;
-        } else {
-          float *slot = p.bal_part + (size_t)(2 * wg + which) * (kDecCols * (D + 1));
-          float *pp = slot + fc * D + fg * DPG;
-          if constexpr (DPG == 4) {
-            *reinterpret_cast<f32x4 *>(pp) = f32x4{o[0], o[1], o[2], o[3]};
+          const int fqi = fc / G;
+          const int fhead = P.g * G + (fc - fqi * G);
+          const int ftok = P.tok0 + fqi;
+          if (P.j0 == 0 && P.j1 == P.nu) {
+            uint16_t *op = p.out + ((int64_t)ftok * p.H + fhead) * D + fg * DPG;
+            if constexpr (DPG == 4) {
+              *reinterpret_cast<u32x2 *>(op) = u32x2{pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3])};
+            } else {
+              *reinterpret_cast<uint32_t *>(op) = pack2_bf16(o[0], o[1]);
+            }
+            if (fg == 0 && p.lse) p.lse[(int64_t)ftok * p.H + fhead] = lse_v;
           } else {
-            *reinterpret_cast<f32x2 *>(pp) = f32x2{o[0], o[1]};
+            float *slot = p.bal_part + (size_t)(2 * wg + P.which) * (kDecCols * (D + 1));
+            float *pp = slot + fc * D + fg * DPG;
+            if constexpr (DPG == 4) {
+              *reinterpret_cast<f32x4 *>(pp) = f32x4{o[0], o[1], o[2], o[3]};
+            } else {
+              *reinterpret_cast<f32x2 *>(pp) = f32x2{o[0], o[1]};
+            }
+            if (fg == 0) slot[kDecCols * D + fc] = lse_v;
           }
-          if (fg == 0) slot[kDecCols * D + fc] = lse_v;
         }
       }
-    }
-    __syncthreads();  // the stages and red_m / red_l are reused by the next piece
+      lgkm_wait_all();
+      __builtin_amdgcn_s_barrier();  // merge stages and m / l / slot entries are free again
 
-    if (cur + n_units == u1 && j0 == 0 && j1 < nu) {
-      // This workgroup holds the first unit of a pair that continues into
-      // later workgroups: the combine of that pair is its job.
-      const int last_unit = pb + (g + 1) * nu - 1;
-      int wl = (int)(((int64_t)last_unit * nwg) / TU);
-      while (wl + 1 < nwg && bal_unit_at(TU, wl + 1, nwg) <= last_unit) ++wl;
-      while (wl > 0 && bal_unit_at(TU, wl, nwg) > last_unit) --wl;
-      own_b = b;
-      own_g = g;
-      own_last = wl;
-      own_which = which;
+      if (!has_next && P.j0 == 0 && P.j1 < P.nu) {
+        // This workgroup holds the first unit of a pair that continues into
+        // later workgroups: the combine of that pair is its job.
+        const int last_unit = P.pair_start + P.nu - 1;
+        int wl = (int)(((int64_t)last_unit * nwg) / TU);
+        while (wl + 1 < nwg && bal_unit_at(TU, wl + 1, nwg) <= last_unit) ++wl;
+        while (wl > 0 && bal_unit_at(TU, wl, nwg) > last_unit) --wl;
+        own_b = P.b;
+        own_g = P.g;
+        own_last = wl;
+        own_which = P.which;
+      }
+      if (!has_next) break;
+      cur = cur_next;
+      P = N;
+      if (pre_n) {
+#pragma unroll
+        for (int ks = 0; ks < QK; ++ks) qf[ks] = qn[ks];
+      }
+      slot0 = pslot < 0 ? 0 : pslot;
     }
-    cur += n_units;
   }
   if (u0 == u1 && tid < kDecCols) {
     // Empty range: a pair cut around it finds an empty piece in its slot.
