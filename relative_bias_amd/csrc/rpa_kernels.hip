@@ -1884,17 +1884,20 @@ __global__ __launch_bounds__(64 * kBalWaves, 1) void decode_balanced_kernel(Attn
   decode_balanced<D, BIAS>(p, smem);
 }
 
-// Merges the pieces of the pair recorded by decode workgroup blockIdx.x: its
-// own piece, then the first piece of every later workgroup up to the one
-// holding the pair's last unit (a workgroup with an empty range marks its
-// slot empty).  The pieces' LSEs are gathered and turned into weights in
-// LDS first, so that the partial loads of all pieces can be in flight
-// together.
+// Merges the pieces of the pair recorded by decode workgroup blockIdx.x /
+// kBalCombineParts: its own piece, then the first piece of every later
+// workgroup up to the one holding the pair's last unit (a workgroup with an
+// empty range marks its slot empty).  The pair's outputs are shared by
+// kBalCombineParts workgroups, one output per thread; the pieces' weights
+// are gathered in LDS first, then each thread has the loads of 16 pieces in
+// flight together.  Sums run in piece order, so the result is repeatable.
+constexpr int kBalCombineParts = 4;
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_balanced_kernel(AttnParams p) {
   __shared__ float wts[kBalMaxWGs][kDecCols];
   __shared__ float red[2][kThreads / 64][kDecCols];
-  const int wg = blockIdx.x;
+  __shared__ float colM[kDecCols], colW[kDecCols];
+  const int wg = blockIdx.x / kBalCombineParts, part = blockIdx.x % kBalCombineParts;
   const int32_t *dsc = p.bal_desc + wg * kBalDescInts;
   const int b = dsc[0];
   if (b < 0) return;
@@ -1904,7 +1907,6 @@ __global__ __launch_bounds__(kThreads) void combine_balanced_kernel(AttnParams p
   const int tok0 = p.cu_seqlens_q[b];
   const int ncols = (p.cu_seqlens_q[b + 1] - tok0) * G;
   constexpr int SLOT = kDecCols * (D + 1);
-  constexpr int DPG = D * kDecCols / kThreads;
   auto slot_of = [&](int i) { return (size_t)(i == 0 ? 2 * wg + which : 2 * (wg + i)) * SLOT; };
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int x = tid; x < np * kDecCols; x += kThreads)
@@ -1939,30 +1941,38 @@ __global__ __launch_bounds__(kThreads) void combine_balanced_kernel(AttnParams p
     const float ls = wts[i][c];
     wts[i][c] = ls == neg_inf() ? 0.f : exp2_fast((ls - M) * kLog2e) * invW;
   }
-  __syncthreads();
-  if (c >= ncols) return;
-  // Thread (c, sub) owns head_dim values [sub * DPG, sub * DPG + DPG).
-  float o[DPG];
-#pragma unroll
-  for (int e = 0; e < DPG; ++e) o[e] = 0.f;
-#pragma unroll 4
-  for (int i = 0; i < np; ++i) {
-    const float wt = wts[i][c];
-    const float *src = p.bal_part + slot_of(i) + c * D + sub * DPG;
-    f32x4 v[DPG / 4];
-#pragma unroll
-    for (int e = 0; e < DPG / 4; ++e) v[e] = reinterpret_cast<const f32x4 *>(src)[e];
-    // An empty piece has weight 0 and may hold anything: select, not scale.
-#pragma unroll
-    for (int e = 0; e < DPG; ++e) o[e] += wt != 0.f ? wt * v[e / 4][e % 4] : 0.f;
+  if (sub == 0) {
+    colM[c] = M;
+    colW[c] = W;
   }
-  const int fqi = c / G;
-  const int fhead = g * G + (c - fqi * G);
-  const int ftok = tok0 + fqi;
-  uint16_t *op = p.out + ((int64_t)ftok * p.H + fhead) * D + sub * DPG;
+  __syncthreads();
+  // Outputs of this part: one (column, d) per thread.
+  const int n_out = ncols * D;
+  const int per = (n_out + kBalCombineParts - 1) / kBalCombineParts;
+  for (int oi = part * per + tid; oi < min(n_out, (part + 1) * per); oi += kThreads) {
+    const int cc = oi / D, d = oi - cc * D;
+    float acc = 0.f;
+    for (int i0 = 0; i0 < np; i0 += 16) {
+      float v[16], wt[16];
 #pragma unroll
-  for (int e = 0; e < DPG; e += 2) reinterpret_cast<uint32_t *>(op)[e / 2] = pack2_bf16(o[e], o[e + 1]);
-  if (sub == 0 && p.lse) p.lse[(int64_t)ftok * p.H + fhead] = M == neg_inf() ? neg_inf() : M + log2_fast(W) * kLn2;
+      for (int u = 0; u < 16; ++u) {
+        const int i = min(i0 + u, np - 1);
+        wt[u] = i0 + u < np ? wts[i][cc] : 0.f;
+        v[u] = p.bal_part[slot_of(i) + cc * D + d];
+      }
+      // An empty piece has weight 0 and may hold anything: select, not scale.
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc += wt[u] != 0.f ? wt[u] * v[u] : 0.f;
+    }
+    const int fqi = cc / G;
+    const int fhead = g * G + (cc - fqi * G);
+    const int ftok = tok0 + fqi;
+    p.out[((int64_t)ftok * p.H + fhead) * D + d] = __builtin_bit_cast(uint16_t, (__bf16)acc);
+    if (d == 0 && p.lse) {
+      const float Mc = colM[cc], Wc = colW[cc];
+      p.lse[(int64_t)ftok * p.H + fhead] = Mc == neg_inf() ? neg_inf() : Mc + log2_fast(Wc) * kLn2;
+    }
+  }
 }
 
 // ---------------------------------------------------------------- combine
@@ -2020,7 +2030,8 @@ hipError_t launch_attention(const AttnParams &p, int head_dim, int64_t n_items_u
 }
 
 hipError_t launch_balanced_decode(const AttnParams &p, int head_dim, hipStream_t stream) {
-  const dim3 grid((unsigned)p.bal_wgs), block(64 * kBalWaves), cgrid((unsigned)p.bal_wgs), cblock(kThreads);
+  const dim3 grid((unsigned)p.bal_wgs), block(64 * kBalWaves), cgrid((unsigned)(p.bal_wgs * kBalCombineParts)),
+      cblock(kThreads);
   const bool bias = p.R > 0;
   if (head_dim == 128) {
     if (bias) hipLaunchKernelGGL((decode_balanced_kernel<128, true>), grid, block, 0, stream, p);
