@@ -365,17 +365,28 @@ __device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t a, uint32_t 
   return r;
 }
 
-// Accumulator start of a general tile.  FULL: every key of the tile is in
-// every row's band and visible to it, so only the scaling remains.
-template <bool BAND, bool FULL = false>
+// Accumulator start of a general tile, by what the tile needs:
+//   kInitEdge:     no bias; 0 where visible, masked elsewhere;
+//   kInitBand:     bias/scale where in the band and visible, 0 where visible
+//                  only, masked elsewhere;
+//   kInitBandVis:  every visible key of the tile is in every row's band:
+//                  bias/scale where visible, masked elsewhere;
+//   kInitBandOnly: every key of the tile is visible to every row:
+//                  bias/scale in the band, 0 elsewhere;
+//   kInitFull:     every key visible and in the band: bias/scale.
+// sacc holds the raw loaded bias values for the band modes.
+enum { kInitEdge, kInitBand, kInitBandVis, kInitBandOnly, kInitFull };
+template <int MODE>
 __device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv_scale, float masked) {
-  if constexpr (FULL) {
+  if constexpr (MODE == kInitFull) {
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) sacc[kb2] *= inv_scale;
     return;
   }
-  const uint32_t vis = range_bits(tb.vis_lo, tb.vis_hi);
-  const uint32_t band = BAND ? range_bits(tb.band_lo, tb.band_hi) : 0u;
+  constexpr bool USE_VIS = MODE != kInitBandOnly;
+  constexpr bool USE_BAND = MODE == kInitBand || MODE == kInitBandOnly;
+  const uint32_t vis = USE_VIS ? range_bits(tb.vis_lo, tb.vis_hi) : 0u;
+  const uint32_t band = USE_BAND ? range_bits(tb.band_lo, tb.band_hi) : 0u;
   const uint32_t mbits = __float_as_uint(masked);
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -383,8 +394,10 @@ __device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv
     for (int j = 0; j < 16; ++j) {
       const int pos = order_of(kb2, j);
       uint32_t v = 0u;
-      if constexpr (BAND) v = __float_as_uint(sacc[kb2][j] * inv_scale) & bit_mask(band, pos);
-      sacc[kb2][j] = __uint_as_float(bit_select(bit_mask(vis, pos), v, mbits));
+      if constexpr (MODE != kInitEdge) v = __float_as_uint(sacc[kb2][j] * inv_scale);
+      if constexpr (USE_BAND) v &= bit_mask(band, pos);
+      if constexpr (USE_VIS) v = bit_select(bit_mask(vis, pos), v, mbits);
+      sacc[kb2][j] = __uint_as_float(v);
     }
   }
 }
@@ -434,12 +447,14 @@ __device__ __forceinline__ void qk_mfma(const char *Kb, const bf16x8 *qf, f32x16
 // compiler sinks their arithmetic to the point of use, after the MFMAs.
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 
-// Phase A: S^T(next) = K·Q^T (+ the initial sacc) on the MFMA pipe, and
-// P = exp2(c*s - m) of the current tile as bf16 PV operands (pb[c] covers keys
-// 16c .. 16c+15 in V^T slot order); returns this lane's part of the row sum.
+// Phase A: S^T(next) = K·Q^T on the MFMA pipe, starting from the initial
+// sacc, or from zero when zc (a plain tile: the first MFMA of each chain
+// takes a zero accumulator), and P = exp2(c*s - m) of the current tile as
+// bf16 PV operands (pb[c] covers keys 16c .. 16c+15 in V^T slot order);
+// returns this lane's part of the row sum (of the fp32 P).
 template <int D>
 __device__ __forceinline__ float phase_a(const char *Kb, const bf16x8 *qf, f32x16 *sn, const f32x16 *sc,
-                                         float c, float m_use, bf16x8 *pb, int l32, int hf) {
+                                         float c, float m_use, bf16x8 *pb, int l32, int hf, bool zc) {
   constexpr int KSTEPS = D / 16;
   constexpr int NM = 2 * KSTEPS;     // MFMAs
   constexpr int EPM = 32 / NM;       // exp elements per MFMA group
@@ -453,7 +468,8 @@ __device__ __forceinline__ float phase_a(const char *Kb, const bf16x8 *qf, f32x1
   };
   // The exp work is skewed over the groups so that no instruction waits on
   // the one just before it: group i scales the elements of group i+2, takes
-  // exp2 of those of group i+1 and sums those of group i (two partial sums).
+  // exp2 of those of group i+1 and sums and packs those of group i (two
+  // partial sums).
   float pe[32];
   float psum[2] = {0.f, 0.f};
   auto fma_g = [&](int gi) __attribute__((always_inline)) {
@@ -485,7 +501,12 @@ __device__ __forceinline__ float phase_a(const char *Kb, const bf16x8 *qf, f32x1
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NM; ++i) {
-    sn[i & 1] = mfma32(as_bf16x8(a[i]), qf[i >> 1], sn[i & 1]);
+    if (i < 2) {
+      if (zc) sn[i & 1] = mfma32(as_bf16x8(a[i]), qf[i >> 1], f32x16{});
+      else sn[i & 1] = mfma32(as_bf16x8(a[i]), qf[i >> 1], sn[i & 1]);
+    } else {
+      sn[i & 1] = mfma32(as_bf16x8(a[i]), qf[i >> 1], sn[i & 1]);
+    }
     if (i + AHEAD < NM) rd(i + AHEAD);
     if (i + 2 < NM) fma_g(i + 2);
     if (i + 1 < NM) exp_g(i + 1);
@@ -497,8 +518,8 @@ __device__ __forceinline__ float phase_a(const char *Kb, const bf16x8 *qf, f32x1
 
 // Phase B: O^T += V^T·P^T on the MFMA pipe (the V^T operand of row
 // d = lane%32 and eight slot-order keys comes from two transposing reads of
-// the row-major V tile), and the row max (raw units) of the next tile plus
-// the zeroing of the released register set sz on the VALU.
+// the row-major V tile), and the row max (raw units) of the next tile on the
+// VALU.
 //
 // The transposing reads are issued as inline asm: the compiler cannot tell
 // them apart from the direct loads in flight into the other V slot and would
@@ -519,7 +540,7 @@ __device__ __forceinline__ void lgkm_wait_for(u32x4 &a) {
 
 template <int D, int VOFF>
 __device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32x16 *oacc, int lane,
-                                         const f32x16 *sn, f32x16 *sz) {
+                                         const f32x16 *sn) {
   constexpr int DB = D / 32;
   constexpr int NM = 4 * DB;
   constexpr int EPM = 32 / NM;
@@ -558,9 +579,6 @@ __device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32
     for (int e = 0; e < EPM; ++e) {
       const int x = i * EPM + e;
       mx[i & 3] = fmaxf(mx[i & 3], sn[x >> 4][x & 15]);
-      float z = 0.f;
-      pin(z);
-      sz[x >> 4][x & 15] = z;
     }
     pin(mx[i & 3]);
     __builtin_amdgcn_sched_barrier(0);
@@ -727,6 +745,13 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   const int full_lo = __builtin_amdgcn_readfirstlane(max(in_lo, qa_max - p.R + 1));
   const int full_hi = __builtin_amdgcn_readfirstlane(min(in_hi, qa_min));
   auto is_full_band = [&](int kb) { return kb >= full_lo && kb + kTileKeys - 1 <= full_hi; };
+  // Every key of the tile visible to every row; every visible key of the
+  // tile inside every row's band (no visible key past qa, none below
+  // qa_max - R + 1).
+  auto is_all_vis = [&](int kb) { return kb >= in_lo && kb + kTileKeys - 1 <= in_hi; };
+  const bool vis_below_qa = p.causal || p.right == 0;
+  const int band_all_lo = __builtin_amdgcn_readfirstlane(qa_max - p.R + 1);
+  auto band_covers_vis = [&](int kb) { return vis_below_qa && kb >= band_all_lo; };
   auto bounds = [&](int kb) {
     const int off = kb + 4 * hf;
     return TileBounds{lo_r - off, hi_r - off, qa - p.R + 1 - off, qa - off};
@@ -762,16 +787,18 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     int pg_k = page_t(2);
     // Accumulator start of tile kb in set sacc, in two steps: begin() right
     // after the set is released (raw bias loads for a band tile, the masks
-    // of an edge tile; a plain tile's set was zeroed), finish() once those
-    // loads have landed (band tiles only).
+    // of an edge tile; a plain tile's set is zeroed first), finish() once
+    // those loads have landed (band tiles only).
     auto begin = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
       if (is_band(kb)) load_bias(sacc, kb);
-      else if (!is_plain(kb)) tile_init<false>(sacc, bounds(kb), inv_scale, masked);
+      else if (!is_plain(kb)) tile_init<kInitEdge>(sacc, bounds(kb), inv_scale, masked);
     };
     auto finish = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
       if (is_band(kb)) {
-        if (is_full_band(kb)) tile_init<true, true>(sacc, bounds(kb), inv_scale, masked);
-        else tile_init<true>(sacc, bounds(kb), inv_scale, masked);
+        if (is_full_band(kb)) tile_init<kInitFull>(sacc, bounds(kb), inv_scale, masked);
+        else if (is_all_vis(kb)) tile_init<kInitBandOnly>(sacc, bounds(kb), inv_scale, masked);
+        else if (band_covers_vis(kb)) tile_init<kInitBandVis>(sacc, bounds(kb), inv_scale, masked);
+        else tile_init<kInitBand>(sacc, bounds(kb), inv_scale, masked);
       }
     };
     auto zero = [&](f32x16 *sacc) __attribute__((always_inline)) {
@@ -820,15 +847,24 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     // The direct loads are issued on every iteration (past the split they
     // fill slots already consumed with zeros), so the number of loads in
     // flight is the same on every path.
+    //
+    // A plain tile's set is never set up: its QK starts from a zero
+    // accumulator.  A general tile's set was started one iteration earlier
+    // and is finished here before the direct loads are issued (the raw bias
+    // of a band tile, loaded into it while the previous PV ran, has landed by
+    // then); the raw bias of a band tile j+2 is loaded into the set tile j
+    // releases between the two phases, so it has phase B and the barrier to
+    // arrive.
     auto iteration = [&](auto par_tag, int j, f32x16 *cur, f32x16 *nxt) __attribute__((always_inline)) {
       constexpr int PAR = decltype(par_tag)::value ? 1 : 0;
-      const int kb = tile_kb(j);
       const bool has_next = j + 1 < nt;
+      const bool zc = !has_next || is_plain(tile_kb(j + 1));
+      if (!zc) finish(nxt, tile_kb(j + 1));
+      __builtin_amdgcn_sched_barrier(0);
       // Direct loads: K(j+2) into K slot PAR (K(j) was consumed before the
       // last barrier), V(j+1) into V slot 1-PAR.
       dma(kcache, j + 2, pg_k, L::kOff(PAR), voff_k);
       dma(vcache, j + 1, pg_v, L::vOff(1 - PAR), voff_v);
-      if (has_next) finish(nxt, tile_kb(j + 1));
       if (j + 3 - pc_base == 64) {
         pc = pc_next;
         pc_base += 64;
@@ -839,21 +875,20 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       const float m_use = m_run == neg_inf() ? 0.f : m_run;
       __builtin_amdgcn_sched_barrier(0);
       // Phase A: QK of tile j+1 (MFMA) || exp of tile j (VALU).
-      l_run += phase_a<D>(smem + L::kOff(1 - PAR), qf, nxt, cur, c, m_use, pb, l32, hf);
-      // Phase B: PV of tile j (MFMA) || row max of tile j+1, zeroing of the
-      // set tile j released (VALU).
-      const float mx = phase_b<D, L::vOff(PAR)>(smem, pb, oacc, lane, nxt, cur) * c;
-      // Start tile j+2 in the released set, then the barrier that publishes
-      // K(j+2) and V(j+1).  Band tiles' raw bias loads may stay in flight.
-      if (j + 2 < nt && is_band(tile_kb(j + 2))) {
-        load_bias(cur, tile_kb(j + 2));
-        __builtin_amdgcn_sched_barrier(0);
-        if (bias_fast) wait_vm8();
-        else wait_vm32();
-      } else {
-        if (j + 2 < nt) begin(cur, tile_kb(j + 2));
-        wait_vm0();
-      }
+      l_run += phase_a<D>(smem + L::kOff(1 - PAR), qf, nxt, cur, c, m_use, pb, l32, hf, zc);
+      const bool band2 = j + 2 < nt && is_band(tile_kb(j + 2));
+      if (band2) load_bias(cur, tile_kb(j + 2));
+      __builtin_amdgcn_sched_barrier(0);
+      // Phase B: PV of tile j (MFMA) || row max of tile j+1 (VALU).
+      const float mx = phase_b<D, L::vOff(PAR)>(smem, pb, oacc, lane, nxt) * c;
+      // Masks of an edge tile j+2 in the released set, then the barrier that
+      // publishes K(j+2) and V(j+1).  Raw bias loads may stay in flight.
+      if (!band2 && j + 2 < nt && !is_plain(tile_kb(j + 2)))
+        tile_init<kInitEdge>(cur, bounds(tile_kb(j + 2)), inv_scale, masked);
+      __builtin_amdgcn_sched_barrier(0);
+      if (!band2) wait_vm0();
+      else if (bias_fast) wait_vm8();
+      else wait_vm32();
       __syncthreads();
       if (has_next) update_max(xor32_max(mx));
     };

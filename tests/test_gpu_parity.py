@@ -90,6 +90,11 @@ CASES = {
     "bias_wider_than_kv": ([20, 1], [25, 40], 4, 2, 64, 16, 512, True, (-1, -1)),
     "empty_rows": ([5, 0, 3, 1], [2, 10, 0, 0], 4, 2, 64, 16, 4, True, (-1, -1)),
     "block_size_64": ([9, 1], [300, 170], 8, 2, 128, 64, 32, True, (-1, -1)),
+    # Bias bands wider than a key tile: full-band tiles, band-only tiles
+    # below the diagonal and band-covers-visible tiles at the diagonal.
+    "prefill_wide_band": ([300, 97], [700, 500], 8, 2, 128, 16, 130, True, (-1, -1)),
+    # Keys past qa visible (right window): band tiles that need both masks.
+    "prefill_band_right_window": ([150, 40], [400, 260], 8, 2, 128, 16, 100, False, (-1, 40)),
 }
 
 
