@@ -118,6 +118,18 @@ __device__ __forceinline__ float xor16_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Workgroup barrier without the fences of __syncthreads(): those make the
+// compiler wait for every outstanding global load (vmcnt(0)) first, which
+// would also wait for loads meant to stay in flight across the barrier.
+// Callers wait explicitly for what the barrier publishes (the LDS writes of
+// direct loads: vmcnt; ds_write: lgkmcnt).  The empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void barrier_raw() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Orders this wave's LDS writes before its later LDS reads (and vice versa).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -154,8 +166,8 @@ __device__ __forceinline__ int wave_max_i(int v) {
 }
 
 __device__ __forceinline__ bool is_decode(int lq, int G) { return lq > 0 && G <= kDecCols && lq * G <= kDecCols; }
-__device__ __forceinline__ int prefill_tiles(int lq, int G) {
-  return (lq <= 0 || is_decode(lq, G)) ? 0 : (int)(((int64_t)lq * G + kTileRows - 1) / kTileRows);
+__device__ __forceinline__ int prefill_tiles(int lq, int G, int rows) {
+  return (lq <= 0 || is_decode(lq, G)) ? 0 : (int)(((int64_t)lq * G + rows - 1) / rows);
 }
 
 struct Item {
@@ -169,14 +181,14 @@ struct Item {
 // prefill q-tiles in request order, the heaviest (last) tile of a request
 // first; items [NP, NP + ND) are the decode items in request order.  Every
 // wave scans independently (the reads hit cache), so no barrier is needed.
-__device__ Item resolve_item(const AttnParams &p, int item, bool decode_only) {
+__device__ Item resolve_item(const AttnParams &p, int item, bool decode_only, int rows) {
   const int lane = threadIdx.x & 63;
   int np = 0, kmax = 0;
   for (int c = 0; c < p.batch; c += 64) {
     const int b = c + lane;
     if (b < p.batch) {
       kmax = max(kmax, p.cache_seqlens[b]);
-      if (!decode_only) np += prefill_tiles(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b], p.G);
+      if (!decode_only) np += prefill_tiles(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b], p.G, rows);
     }
   }
   kmax = wave_max_i(kmax);
@@ -189,7 +201,7 @@ __device__ Item resolve_item(const AttnParams &p, int item, bool decode_only) {
     int n = 0;
     if (b < p.batch) {
       const int lq = p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b];
-      n = pre ? prefill_tiles(lq, p.G) : (is_decode(lq, p.G) ? 1 : 0);
+      n = pre ? prefill_tiles(lq, p.G, rows) : (is_decode(lq, p.G) ? 1 : 0);
     }
     int incl = n;
 #pragma unroll
@@ -590,6 +602,7 @@ template <int D>
 __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, char *smem) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
+  constexpr int ROWS = kTileRows;
   using L = PrefillLds<D>;
 
   const int b = it.b;
@@ -602,8 +615,8 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   const int lk = __builtin_amdgcn_readfirstlane(p.cache_seqlens[b]);
   const int G = p.G;
   const int nrows = lq * G;
-  const int row0 = it.tile * kTileRows;
-  const int row_last = min(row0 + kTileRows, nrows) - 1;
+  const int row0 = it.tile * ROWS;
+  const int row_last = min(row0 + ROWS, nrows) - 1;
   int r = row0 + 32 * w + l32;
   const bool row_valid = r <= row_last;
   if (!row_valid) r = row_last;  // idle lanes shadow the last row; never stored
@@ -769,6 +782,49 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     }
   };
 
+  // Accumulator start of tile kb in set sacc, in two steps: begin() right
+  // after the set is released (raw bias loads for a band tile, the masks
+  // of an edge tile; a plain tile's set is zeroed first), finish() once
+  // those loads have landed (band tiles only).
+  auto begin = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
+    if (is_band(kb)) load_bias(sacc, kb);
+    else if (!is_plain(kb)) tile_init<kInitEdge>(sacc, bounds(kb), inv_scale, masked);
+  };
+  auto finish = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
+    if (is_band(kb)) {
+      if (is_full_band(kb)) tile_init<kInitFull>(sacc, bounds(kb), inv_scale, masked);
+      else if (is_all_vis(kb)) tile_init<kInitBandOnly>(sacc, bounds(kb), inv_scale, masked);
+      else if (band_covers_vis(kb)) tile_init<kInitBandVis>(sacc, bounds(kb), inv_scale, masked);
+      else tile_init<kInitBand>(sacc, bounds(kb), inv_scale, masked);
+    }
+  };
+  auto zero = [&](f32x16 *sacc) __attribute__((always_inline)) {
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
+  };
+
+  // Prologue prefetch: the band tiles come first, so pull this wave's
+  // rel_logits rows into the cache while the first tiles load, with dword
+  // direct loads whose LDS writes land in V slot 1 (unused until iteration
+  // 0).  Line i of row r is fetched by lane (i + r * LPR) % 64
+  // of load (i + r * LPR) / 64.
+  auto prefetch_band_rows = [&]() __attribute__((always_inline)) {
+    if (bias_fast && band_hi >= t0 && band_lo < t1) {
+      const int lpr = (p.R * 4 + 127) / 128 + 1;  // 128-byte lines per row
+      const int nload = (32 * lpr + 63) / 64;
+      for (int n = 0; n < nload; ++n) {
+        const int ln = 64 * n + lane;
+        const int rw = ln / lpr;  // row of this wave's 32
+        int rr = min(row0 + 32 * w + rw, row_last);
+        const int tk = tok0 + rr / G, hd = g * G + rr % G;
+        const int64_t off = ((int64_t)tk * p.H + hd) * p.R * 4 - bias_lo * 4 + 128 * (ln - rw * lpr);
+        const uint32_t voff = rw < 32 ? (uint32_t)off : 0xFFFFFFF0u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            bias_rs, (__attribute__((address_space(3))) void *)(smem + L::vOff(1) + 256 * w), 4, voff, 0, 0, 0);
+      }
+    }
+  };
+
   if (nt > 0) {
     // Software pipeline over 64-key tiles.  Tile j's K sits in K slot j%2,
     // its V in V slot j%2, its scores in register set j%2 (sa or sb).  While
@@ -785,26 +841,6 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     // Page ids: pg_v of tile j+1 and pg_k of tile j+2 at the top of iteration j.
     int pg_v = page_t(1);
     int pg_k = page_t(2);
-    // Accumulator start of tile kb in set sacc, in two steps: begin() right
-    // after the set is released (raw bias loads for a band tile, the masks
-    // of an edge tile; a plain tile's set is zeroed first), finish() once
-    // those loads have landed (band tiles only).
-    auto begin = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
-      if (is_band(kb)) load_bias(sacc, kb);
-      else if (!is_plain(kb)) tile_init<kInitEdge>(sacc, bounds(kb), inv_scale, masked);
-    };
-    auto finish = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
-      if (is_band(kb)) {
-        if (is_full_band(kb)) tile_init<kInitFull>(sacc, bounds(kb), inv_scale, masked);
-        else if (is_all_vis(kb)) tile_init<kInitBandOnly>(sacc, bounds(kb), inv_scale, masked);
-        else if (band_covers_vis(kb)) tile_init<kInitBandVis>(sacc, bounds(kb), inv_scale, masked);
-        else tile_init<kInitBand>(sacc, bounds(kb), inv_scale, masked);
-      }
-    };
-    auto zero = [&](f32x16 *sacc) __attribute__((always_inline)) {
-      sacc[0] = f32x16{};
-      sacc[1] = f32x16{};
-    };
     {
       const int pg0 = page_t(0);
       dma(kcache, 0, pg0, L::kOff(0), voff_k);
@@ -812,24 +848,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       dma(kcache, 1, pg_v, L::kOff(1), voff_k);
       zero(sa);
       begin(sa, tile_kb(0));
-      // The band tiles come first: pull this wave's rel_logits rows into the
-      // cache now, while the first tiles load, with dword direct loads whose
-      // LDS writes land in V slot 1 (unused until iteration 0).  Line i of
-      // row r is fetched by lane (i + r * LPR) % 64 of load (i + r * LPR) / 64.
-      if (bias_fast && band_hi >= t0 && band_lo < t1) {
-        const int lpr = (p.R * 4 + 127) / 128 + 1;  // 128-byte lines per row
-        const int nload = (32 * lpr + 63) / 64;
-        for (int n = 0; n < nload; ++n) {
-          const int ln = 64 * n + lane;
-          const int rw = ln / lpr;  // row of this wave's 32
-          int rr = min(row0 + 32 * w + rw, row_last);
-          const int tk = tok0 + rr / G, hd = g * G + rr % G;
-          const int64_t off = ((int64_t)tk * p.H + hd) * p.R * 4 - bias_lo * 4 + 128 * (ln - rw * lpr);
-          const uint32_t voff = rw < 32 ? (uint32_t)off : 0xFFFFFFF0u;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              bias_rs, (__attribute__((address_space(3))) void *)(smem + L::vOff(1) + 256 * w), 4, voff, 0, 0, 0);
-        }
-      }
+      prefetch_band_rows();
       wait_vm0();
       __syncthreads();
       finish(sa, tile_kb(0));
@@ -889,7 +908,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       if (!band2) wait_vm0();
       else if (bias_fast) wait_vm8();
       else wait_vm32();
-      __syncthreads();
+      barrier_raw();
       if (has_next) update_max(xor32_max(mx));
     };
 
@@ -1305,7 +1324,7 @@ __global__ __launch_bounds__(64 * attn_waves<DECODE_ONLY>(), 2) void attn_kernel
   const int rest = bid / p.S;
   const int g = rest % p.Hkv;
   const int item = rest / p.Hkv;
-  const Item it = resolve_item(p, item, DECODE_ONLY);
+  const Item it = resolve_item(p, item, DECODE_ONLY, kTileRows);
   const int kind = __builtin_amdgcn_readfirstlane(it.kind);
   if (kind == 2) {
     decode_item<D, 1, attn_waves<DECODE_ONLY>()>(p, it, g, s, smem);
@@ -2053,12 +2072,14 @@ hipError_t launch_attention(const AttnParams &p, int head_dim, int64_t n_items_u
                             hipStream_t stream) {
   const int64_t blocks = n_items_ub * p.Hkv * p.S;
   if (blocks <= 0) return hipSuccess;
-  const dim3 grid((unsigned)blocks), block(decode_only ? 64 * attn_waves<true>() : 64 * attn_waves<false>());
-  if (head_dim == 128) {
-    if (decode_only) hipLaunchKernelGGL((attn_kernel<128, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((attn_kernel<128, false>), grid, block, 0, stream, p);
+  const dim3 grid((unsigned)blocks);
+  if (decode_only) {
+    const dim3 block(64 * attn_waves<true>());
+    if (head_dim == 128) hipLaunchKernelGGL((attn_kernel<128, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((attn_kernel<64, true>), grid, block, 0, stream, p);
   } else {
-    if (decode_only) hipLaunchKernelGGL((attn_kernel<64, true>), grid, block, 0, stream, p);
+    const dim3 block(64 * attn_waves<false>());
+    if (head_dim == 128) hipLaunchKernelGGL((attn_kernel<128, false>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((attn_kernel<64, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
