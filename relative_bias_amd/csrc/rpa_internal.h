@@ -19,11 +19,14 @@ constexpr int kBalWaves = 8;        // waves per workgroup (one workgroup per CU
 constexpr int kBalMaxBatch = 2048;  // requests (their unit prefix sums live in LDS)
 constexpr int kBalMaxWGs = 512;     // workgroups at most
 constexpr int kBalDescInts = 8;     // per-workgroup combine record
+constexpr int kBalHeads = 8;        // kv heads streamed side by side (one per wave)
 // Workspace of the balanced decode: kBalMaxWGs records, then two partial
-// slots per workgroup of kDecCols * (head_dim + 1) fp32 (outputs, then LSEs).
+// slots per workgroup, each with kBalHeads entries of kDecCols *
+// (head_dim + 1) fp32 (outputs, then LSEs).  The one-head-per-workgroup
+// form uses the first entry of each slot.
 __host__ __device__ inline size_t bal_desc_bytes() { return (size_t)kBalMaxWGs * kBalDescInts * 4; }
 __host__ __device__ inline size_t bal_part_bytes(int head_dim) {
-  return (size_t)2 * kBalMaxWGs * kDecCols * (size_t)(head_dim + 1) * 4;
+  return (size_t)2 * kBalMaxWGs * kBalHeads * kDecCols * (size_t)(head_dim + 1) * 4;
 }
 
 struct AttnParams {

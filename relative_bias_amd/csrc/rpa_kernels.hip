@@ -1490,8 +1490,8 @@ __device__ __forceinline__ int bal_units(const AttnParams &p, int b) {
   return r.hi > lo_a ? max((r.hi - lo_a + 15) >> 4, 1) : 1;
 }
 
-// prefix[b] = Hkv * (units of requests before b); prefix[batch] = all units.
-__device__ void bal_prefix(const AttnParams &p, int32_t *prefix, int32_t *tmp) {
+// prefix[b] = mult * (units of requests before b); prefix[batch] = all.
+__device__ void bal_prefix(const AttnParams &p, int32_t *prefix, int32_t *tmp, int mult) {
   constexpr int NT = 64 * kBalWaves;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int B = p.batch;
@@ -1509,10 +1509,10 @@ __device__ void bal_prefix(const AttnParams &p, int32_t *prefix, int32_t *tmp) {
   __syncthreads();
   int base = 0;
   for (int ww = 0; ww < w; ++ww) base += tmp[ww];
-  int run = (base + incl - local) * p.Hkv;
+  int run = (base + incl - local) * mult;
   for (int b = b0; b < b1; ++b) {
     prefix[b] = run;
-    run += bal_units(p, b) * p.Hkv;
+    run += bal_units(p, b) * mult;
   }
   if (b0 < b1 && b1 == B) prefix[B] = run;
   __syncthreads();
@@ -1528,7 +1528,7 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
   static_assert(L::NST == 2, "two stages per wave: one computed, one in flight");
   constexpr int NPER = 2 * NI + (BIAS ? 4 : 0);  // vector-memory instructions per unit
   int32_t *prefix = reinterpret_cast<int32_t *>(smem + L::prefixOff);
-  bal_prefix(p, prefix, reinterpret_cast<int32_t *>(smem + L::mlOff));
+  bal_prefix(p, prefix, reinterpret_cast<int32_t *>(smem + L::mlOff), p.Hkv);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2029,6 +2029,468 @@ __global__ __launch_bounds__(kThreads) void combine_balanced_kernel(AttnParams p
   }
 }
 
+// ------------------------------------- balanced decode, kv heads in parallel
+//
+// The same balance for batches with eight kv heads, but a unit is a 16-key
+// block of a request over all eight heads: units run in (request, key)
+// order, workgroup x of W takes units [x*TU/W, (x+1)*TU/W), and wave w
+// streams kv head w over them.  The waves of a workgroup read the same
+// tokens, so together they fetch whole token rows of the cache (all heads,
+// 2 KB for head_dim 128) instead of one head's 256-byte slice.  Waves never
+// merge: each finishes its head of a piece (the part of one request inside
+// the range) on its own, with the output when the piece is the whole
+// request, else with a normalised partial in its head's entry of the
+// piece's slot; the workgroup holding a cut request's first unit records it
+// for combine_heads_kernel.  Per unit and wave the loads, LDS layout and
+// arithmetic are those of decode_balanced.
+
+template <int D, bool BIAS>
+__device__ void decode_heads(const AttnParams &p, char *smem) {
+  using L = BalLds<D>;
+  constexpr int QK = D / 32, DB = D / 16, NI = L::NI, RPI = L::RPI, UNITS = L::UNITS, ROWB = L::ROWB;
+  static_assert(L::NST == 2, "two stages per wave: one computed, one in flight");
+  static_assert(kBalWaves == kBalHeads, "one wave per kv head");
+  constexpr int NPER = 2 * NI + (BIAS ? 4 : 0);  // vector-memory instructions per unit
+  constexpr int SLOT = kDecCols * (D + 1);
+  int32_t *prefix = reinterpret_cast<int32_t *>(smem + L::prefixOff);
+  bal_prefix(p, prefix, reinterpret_cast<int32_t *>(smem + L::mlOff), 1);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = w;  // this wave's kv head
+  const int c16 = lane & 15, q = lane >> 4;
+  const int B = p.batch, G = p.G;
+  const int nwg = p.bal_wgs, wg = blockIdx.x;
+  const int TU = __builtin_amdgcn_readfirstlane(prefix[B]);
+  const int u0 = bal_unit_at(TU, wg, nwg), u1 = bal_unit_at(TU, wg + 1, nwg);
+  int b_it = 0;
+  {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (prefix[mid] <= u0) lo = mid;
+      else hi = mid - 1;
+    }
+    b_it = __builtin_amdgcn_readfirstlane(lo);
+  }
+
+  const uint32_t slot_bytes = (uint32_t)kBalHeads * D * 2;
+  uint32_t gk[NI], gv[NI];
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    const int r = RPI * n + lane / UNITS, pu = lane % UNITS;
+    gk[n] = r * slot_bytes + ((pu ^ swz_k<D>(r)) << 4);
+    gv[n] = r * slot_bytes + ((pu ^ swz_vt<D>(r)) << 4);
+  }
+  uint32_t lk_off[QK], lv_off[DB];
+#pragma unroll
+  for (int ks = 0; ks < QK; ++ks) lk_off[ks] = c16 * ROWB + (((4 * ks + q) ^ swz_k<D>(c16)) << 4);
+  {
+    const int i = (lane & 15) >> 2, t = lane & 3, row = 4 * q + i;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      lv_off[db] = L::halfBytes + row * ROWB + ((((2 * db + (t >> 1)) ^ swz_vt<D>(row)) << 4)) + 8 * (t & 1);
+  }
+  const uint32_t smem_u = (uint32_t)(uintptr_t)smem;
+  const uint32_t lds_wave = smem_u + (uint32_t)(w * 2 * L::stageBytes);
+  const uint32_t lds_bias = smem_u + (uint32_t)(L::biasOff + w * 2 * 1024 + 4 * lane);
+  const uint32_t lds_prefix = smem_u + L::prefixOff;
+  const float c = p.scale_log2;
+  const bool pos_scale = c > 0.f;
+  const uint32_t bias_bytes = BIAS ? (uint32_t)p.num_tokens * (uint32_t)p.H * (uint32_t)p.R * 4u : 0u;
+
+  // A piece: units [j0, j1) of request b inside this workgroup's range,
+  // with what its rows need (uniform fields, then the lane's column).
+  struct Piece {
+    int b, j0, j1, nu, which, pair_start;
+    int tok0, lq, ncols, lo_a, kend, in_lo, in_hi, band_lo, band_hi, n;
+    int qa, lo_c, hi_c, tok, head;
+    uint32_t rel_base;
+  };
+  auto prefix_at = [&](int i) { return __builtin_amdgcn_readfirstlane(lds_read_i32_now(lds_prefix + 4u * i)); };
+  auto make_piece = [&](int cur) __attribute__((always_inline)) {
+    Piece P;
+    while (prefix_at(b_it + 1) <= cur) ++b_it;
+    P.b = b_it;
+    P.pair_start = prefix_at(b_it);
+    P.nu = prefix_at(b_it + 1) - P.pair_start;
+    P.j0 = cur - P.pair_start;
+    P.j1 = min(P.nu, P.j0 + (u1 - cur));
+    P.n = P.j1 - P.j0;
+    P.which = cur == u0 ? 0 : 1;
+    P.tok0 = scalar_load_i32(p.cu_seqlens_q + P.b);
+    P.lq = scalar_load_i32(p.cu_seqlens_q + P.b + 1) - P.tok0;
+    const int lk = scalar_load_i32(p.cache_seqlens + P.b);
+    P.ncols = P.lq * G;
+    const int col = c16 < P.ncols ? c16 : P.ncols - 1;
+    const int qi = col / G;
+    P.head = g * G + (col - qi * G);
+    P.tok = P.tok0 + qi;
+    P.qa = qi + lk - P.lq;
+    const int qa_min = lk - P.lq, qa_max = lk - 1;
+    const Range vr = visible_range(p, lk, qa_min, qa_max);
+    P.lo_a = vr.lo & ~15;
+    P.kend = min(lk, vr.hi);
+    P.lo_c = P.lo_a;
+    P.hi_c = P.kend - 1;
+    if (p.left >= 0) P.lo_c = max(P.lo_c, P.qa - p.left);
+    if (p.causal) P.hi_c = min(P.hi_c, P.qa);
+    if (p.right >= 0) P.hi_c = min(P.hi_c, P.qa + p.right);
+    P.in_lo = P.lo_a;
+    P.in_hi = P.kend - 1;
+    if (p.left >= 0) P.in_lo = max(P.in_lo, qa_max - p.left);
+    if (p.causal) P.in_hi = min(P.in_hi, qa_min);
+    if (p.right >= 0) P.in_hi = min(P.in_hi, qa_min + p.right);
+    P.band_lo = qa_min - p.R + 1;
+    P.band_hi = qa_max;
+    P.rel_base = BIAS ? (uint32_t)((P.tok * p.H + P.head) * p.R) : 0u;
+    return P;
+  };
+  auto key_of = [&](const Piece &P, int k) { return P.lo_a + 16 * (P.j0 + k); };
+  auto in_band = [&](const Piece &P, int key0) { return BIAS && key0 <= P.band_hi && key0 + 15 >= P.band_lo; };
+  auto page_of = [&](const Piece &P, int k) -> int {
+    const int key = key_of(P, k);
+    if (k >= P.n || key >= P.kend) return 0;
+    return scalar_load_i32(p.block_table + (int64_t)P.b * p.P + (p.bs_shift >= 0 ? (key >> p.bs_shift) : key / p.BS));
+  };
+  auto load_q = [&](const Piece &P, bf16x8 (&qf)[QK]) __attribute__((always_inline)) {
+    const uint16_t *qp = p.q + ((int64_t)P.tok * p.H + P.head) * D + 8 * q;
+#pragma unroll
+    for (int ks = 0; ks < QK; ++ks) qf[ks] = as_bf16x8(ld16(qp + 32 * ks));
+  };
+  auto issue = [&](const Piece &P, int k, int page, int slot) __attribute__((always_inline)) {
+    const int key0 = __builtin_amdgcn_readfirstlane(key_of(P, k));
+    const int nvalid = __builtin_amdgcn_readfirstlane(min(max(P.kend - key0, 0), 16));
+    const int slot0 = p.bs_shift >= 0 ? (key0 & (p.BS - 1)) : key0 % p.BS;
+    const int64_t eoff = (((int64_t)page * p.BS + slot0) * kBalHeads + g) * D;
+    const auto rk = make_rsrc(p.k + eoff, (uint32_t)nvalid * slot_bytes);
+    const auto rv = make_rsrc(p.v + eoff, (uint32_t)nvalid * slot_bytes);
+    if constexpr (BIAS) {
+      const auto brs = make_rsrc(p.rel_logits, in_band(P, key0) ? bias_bytes : 0u);
+      char *bst = smem + L::biasOff + (w * 2 + slot) * 1024;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = min(max(P.qa - (key0 + 4 * q + j), 0), p.R - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (__attribute__((address_space(3))) void *)(bst + 256 * j), 4,
+                                                 (P.rel_base + (uint32_t)d) * 4u, 0, 0, 0);
+      }
+    }
+    char *st = smem + (w * 2 + slot) * L::stageBytes;
+#pragma unroll
+    for (int n = 0; n < NI; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void *)(st + n * 1024), 16,
+                                               gk[n], 0, 0, 0);
+#pragma unroll
+    for (int n = 0; n < NI; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void *)(st + L::halfBytes + n * 1024), 16, gv[n], 0, 0, 0);
+  };
+
+  f32x4 oacc[DB];
+  float m_run, l_run;
+  auto compute = [&](const Piece &P, int k, int slot, const bf16x8 (&qf)[QK]) __attribute__((always_inline)) {
+    const int key0 = __builtin_amdgcn_readfirstlane(key_of(P, k));
+    const uint32_t st = lds_wave + slot * L::stageBytes;
+    u32x4 kf[QK];
+#pragma unroll
+    for (int ks = 0; ks < QK; ++ks) kf[ks] = lds_read_b128_asm(st + lk_off[ks]);
+    u32x2 va[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) va[db] = lds_read_tr_at(st + lv_off[db]);
+    lgkm_wait_n<DB>(kf);
+    f32x4 sacc = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < QK; ++ks) sacc = mfma16(as_bf16x8(kf[ks]), qf[ks], sacc);
+    const bool interior = key0 >= P.in_lo && key0 + 15 <= P.in_hi;
+    const bool band = in_band(P, key0);
+    const bool plain = interior && !band;
+    float mx = neg_inf();
+    if (plain) {
+      if (pos_scale) {
+        mx = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3])) * c;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sacc[j] * c);
+      }
+    } else {
+      float bias[4] = {0.f, 0.f, 0.f, 0.f};
+      if (band) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bias[j] = lds_read_f32_asm(lds_bias + slot * 1024 + 256 * j);
+        lgkm_wait_n<0>(bias);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = key0 + 4 * q + j;
+        float v = sacc[j] * c;
+        if (band && (unsigned)(P.qa - t) < (unsigned)p.R) v = __builtin_fmaf(bias[j], kLog2e, v);
+        if (t < P.lo_c || t > P.hi_c) v = neg_inf();
+        sacc[j] = v;
+        mx = fmaxf(mx, v);
+      }
+    }
+    mx = xor16_max(mx);
+    mx = xor32_max(mx);
+    if (__any(mx > m_run + kTau)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == neg_inf() ? 1.f : exp2_fast(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+    const float m_use = m_run == neg_inf() ? 0.f : m_run;
+    float pe[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pe[j] = exp2_fast(plain ? __builtin_fmaf(sacc[j], c, -m_use) : sacc[j] - m_use);
+    l_run += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+    const u32x2 pf = u32x2{pack2_bf16(pe[0], pe[1]), pack2_bf16(pe[2], pe[3])};
+    lgkm_wait_n<0>(va);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = mfma16k16(va[db], pf, oacc[db]);
+  };
+  // Lane (c16, q) holds O^T[16 db + 4 q + e][column c16] in oacc[db][e];
+  // the column's l is spread over its four q lanes.
+  auto finish_piece = [&](const Piece &P) __attribute__((always_inline)) {
+    const float l_col = xor32_sum(xor16_sum(l_run));
+    const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
+    const float lse_v = l_col > 0.f ? (m_run + log2_fast(l_col)) * kLn2 : neg_inf();
+    if (c16 >= P.ncols) return;
+    if (P.j0 == 0 && P.j1 == P.nu) {
+      uint16_t *op = p.out + ((int64_t)P.tok * p.H + P.head) * D + 4 * q;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<u32x2 *>(op + 16 * db) =
+            u32x2{pack2_bf16(oacc[db][0] * inv, oacc[db][1] * inv), pack2_bf16(oacc[db][2] * inv, oacc[db][3] * inv)};
+      if (q == 0 && p.lse) p.lse[(int64_t)P.tok * p.H + P.head] = lse_v;
+    } else {
+      float *slot = p.bal_part + ((size_t)(2 * wg + P.which) * kBalHeads + g) * SLOT;
+      float *pp = slot + c16 * D + 4 * q;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4 *>(pp + 16 * db) = oacc[db] * inv;
+      if (q == 0) slot[kDecCols * D + c16] = lse_v;
+    }
+  };
+
+  int own_b = -1, own_ncols = 0, own_last = 0, own_which = 0;
+  int cur = u0;
+  if (cur < u1) {
+    Piece P = make_piece(cur);
+    bf16x8 qf[QK];
+    load_q(P, qf);
+    // Q is in before the first direct load is issued, so that no later
+    // wait on the Q registers can count the unit loads in flight.
+    wait_vm<0>();
+    int slot = 0;  // stage of the next unit to compute
+    issue(P, 0, page_of(P, 0), 0);
+    while (true) {
+      const int cur_next = cur + P.n;
+      const bool has_next = cur_next < u1;
+      Piece N;
+      int page_n0 = 0;
+      if (has_next) {
+        N = make_piece(cur_next);
+        page_n0 = page_of(N, 0);
+      }
+      int page_nx = page_of(P, 1);
+      bf16x8 qn[QK];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = f32x4{};
+      m_run = neg_inf();
+      l_run = 0.f;
+      // While unit k is computed the next unit of the wave's stream is in
+      // flight: unit k+1 of P or, after P's last, unit 0 of the next piece
+      // (this wave's head of the next request).
+      for (int k = 0; k < P.n; ++k) {
+        if (k + 1 < P.n) {
+          issue(P, k + 1, page_nx, slot ^ 1);
+          page_nx = page_of(P, k + 2);
+          wait_vm<NPER>();
+        } else if (has_next) {
+          load_q(N, qn);
+          issue(N, 0, page_n0, slot ^ 1);
+          wait_vm<NPER>();
+        } else {
+          wait_vm<0>();
+        }
+        compute(P, k, slot, qf);
+        slot ^= 1;
+      }
+      finish_piece(P);
+      if (!has_next && P.j0 == 0 && P.j1 < P.nu) {
+        // This workgroup holds the first unit of a request that continues
+        // into later workgroups: the combine of its heads is its job.
+        const int last_unit = P.pair_start + P.nu - 1;
+        int wl = (int)(((int64_t)last_unit * nwg) / TU);
+        while (wl + 1 < nwg && bal_unit_at(TU, wl + 1, nwg) <= last_unit) ++wl;
+        while (wl > 0 && bal_unit_at(TU, wl, nwg) > last_unit) --wl;
+        own_b = P.b;
+        own_ncols = P.ncols;
+        own_last = wl;
+        own_which = P.which;
+      }
+      if (!has_next) break;
+      cur = cur_next;
+      P = N;
+#pragma unroll
+      for (int ks = 0; ks < QK; ++ks) qf[ks] = qn[ks];
+    }
+  }
+  if (u0 == u1 && tid < kBalHeads * kDecCols) {
+    // Empty range: a request cut around it finds empty pieces in its slot.
+    p.bal_part[((size_t)(2 * wg) * kBalHeads + tid / kDecCols) * SLOT + kDecCols * D + tid % kDecCols] = neg_inf();
+  }
+  if (tid == 0) {
+    int32_t *dsc = p.bal_desc + wg * kBalDescInts;
+    dsc[0] = own_b;
+    dsc[1] = own_ncols;
+    dsc[2] = own_last;
+    dsc[3] = own_which;
+    dsc[4] = TU;
+  }
+}
+
+template <int D, bool BIAS>
+__global__ __launch_bounds__(64 * kBalWaves, 1) void decode_heads_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[BalLds<D>::bytes];
+  decode_heads<D, BIAS>(p, smem);
+}
+
+// Combine of the requests cut by decode_heads.  A task is (recording
+// workgroup x, kv head, column, block of head_dim values) and takes one
+// wave: the pieces' LSEs and the first 16 pieces of each lane's group are
+// loaded together, the weights exp(lse_i - LSE) go to LDS, and lane
+// (piece group, d) sums every PG-th piece for one d; the piece groups are
+// added by shuffles.  PG grows with the piece count (1 up to 16 pieces,
+// then up to 16 groups) so that long requests spread over many waves.
+// Tasks are numbered over the recording workgroups in order; every
+// workgroup scans the records (request, column count, last workgroup).
+template <int D>
+__global__ __launch_bounds__(kThreads) void combine_heads_kernel(AttnParams p) {
+  constexpr int SLOT = kDecCols * (D + 1);
+  constexpr int NWV = kThreads / 64;
+  __shared__ int tpre[kBalMaxWGs + 1];
+  __shared__ int wpart[NWV];
+  __shared__ float wts[NWV][kBalMaxWGs];
+  const int nwg = p.bal_wgs, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // Piece groups of a record: log2 PG with PG = pow2ceil(np / 16) in [1, 16].
+  auto lg_pg = [&](int np) {
+    int lg = 0;
+    while (lg < 4 && (16 << lg) < np) ++lg;
+    return lg;
+  };
+  auto tasks_of = [&](int x) {
+    if (x >= nwg) return 0;
+    const int32_t *dsc = p.bal_desc + x * kBalDescInts;
+    if (dsc[0] < 0) return 0;
+    const int dl_bits = 6 - lg_pg(dsc[2] - x + 1);
+    return kBalHeads * dsc[1] * max(D >> dl_bits, 1);
+  };
+  // Exclusive prefix of the task counts over records (two per thread).
+  const int n0 = tasks_of(2 * tid), n1 = tasks_of(2 * tid + 1);
+  int incl = n0 + n1;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wpart[wv] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int ww = 0; ww < wv; ++ww) base += wpart[ww];
+  const int ex = base + incl - n0 - n1;
+  if (2 * tid < kBalMaxWGs) tpre[2 * tid] = ex;
+  if (2 * tid + 1 < kBalMaxWGs) tpre[2 * tid + 1] = ex + n0;
+  if (tid == kThreads - 1) tpre[kBalMaxWGs] = ex + n0 + n1;
+  __syncthreads();
+  const int total = tpre[kBalMaxWGs];
+  for (int task = blockIdx.x * NWV + wv; task < total; task += gridDim.x * NWV) {
+    int lo = 0, hi = kBalMaxWGs - 1;  // the last record x with tpre[x] <= task
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tpre[mid] <= task) lo = mid;
+      else hi = mid - 1;
+    }
+    const int x = __builtin_amdgcn_readfirstlane(lo);
+    const int32_t *dsc = p.bal_desc + x * kBalDescInts;
+    const int b = dsc[0], ncols = dsc[1], w_last = dsc[2], which = dsc[3];
+    const int np = w_last - x + 1;
+    const int tok0 = p.cu_seqlens_q[b];
+    const int lg = lg_pg(np), dl_bits = 6 - lg;
+    const int nch = max(D >> dl_bits, 1);
+    const int rem = task - tpre[x];
+    const int g = rem / (ncols * nch);
+    const int rem2 = rem - g * ncols * nch;
+    const int cc = rem2 / nch, ch = rem2 - cc * nch;
+    auto slot_of = [&](int i) {
+      return ((size_t)(i == 0 ? 2 * x + which : 2 * (x + i)) * kBalHeads + g) * SLOT;
+    };
+    const int pg = lane >> dl_bits, dl = lane & ((1 << dl_bits) - 1);
+    const int d = (ch << dl_bits) + dl;
+    const int PG = 1 << lg;
+    // The pieces' LSEs (lane i holds pieces i, i + 64, ...) and the first
+    // 16 pieces of this lane's group are loaded together.
+    float ls[kBalMaxWGs / 64], v[16];
+#pragma unroll
+    for (int u = 0; u < kBalMaxWGs / 64; ++u) {
+      const int i = lane + 64 * u;
+      ls[u] = i < np ? p.bal_part[slot_of(i) + kDecCols * D + cc] : neg_inf();
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = pg + u * PG;
+      v[u] = i < np && d < D ? p.bal_part[slot_of(i) + cc * D + d] : 0.f;
+    }
+    float M = neg_inf();
+#pragma unroll
+    for (int u = 0; u < kBalMaxWGs / 64; ++u) M = fmaxf(M, ls[u]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float W = 0.f;
+#pragma unroll
+    for (int u = 0; u < kBalMaxWGs / 64; ++u) {
+      const int i = lane + 64 * u;
+      const float e = (M == neg_inf() || ls[u] == neg_inf()) ? 0.f : exp2_fast((ls[u] - M) * kLog2e);
+      if (i < np) wts[wv][i] = e;
+      W += e;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) W += __shfl_xor(W, o);
+    wave_lds_sync();
+    // An empty piece has weight 0 and may hold anything: select, not scale.
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = pg + u * PG;
+      const float wt = i < np ? wts[wv][i] : 0.f;
+      acc += wt != 0.f ? wt * v[u] : 0.f;
+    }
+    if (d < D) {
+      for (int i0 = pg + 16 * PG; i0 < np; i0 += 8 * PG) {
+        float wt[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * PG;
+          wt[u] = i < np ? wts[wv][i] : 0.f;
+          v[u] = i < np ? p.bal_part[slot_of(i) + cc * D + d] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += wt[u] != 0.f ? wt[u] * v[u] : 0.f;
+      }
+    }
+    for (int bit = dl_bits; bit < 6; ++bit) acc += __shfl_xor(acc, 1 << bit);
+    wave_lds_sync();  // wts[wv] is rewritten by the next task
+    if (pg == 0 && d < D) {
+      const int fqi = cc / p.G;
+      const int fhead = g * p.G + (cc - fqi * p.G);
+      const int ftok = tok0 + fqi;
+      const float invW = W > 0.f ? 1.f / W : 0.f;
+      p.out[((int64_t)ftok * p.H + fhead) * D + d] = __builtin_bit_cast(uint16_t, (__bf16)(acc * invW));
+      if (d == 0 && p.lse) p.lse[(int64_t)ftok * p.H + fhead] = M == neg_inf() ? neg_inf() : M + log2_fast(W) * kLn2;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- combine
 
 // One wave per (token, head) row: weights exp(lse_s - LSE) over the splits,
@@ -2089,6 +2551,19 @@ hipError_t launch_balanced_decode(const AttnParams &p, int head_dim, hipStream_t
   const dim3 grid((unsigned)p.bal_wgs), block(64 * kBalWaves), cgrid((unsigned)(p.bal_wgs * kBalCombineParts)),
       cblock(kThreads);
   const bool bias = p.R > 0;
+  if (p.Hkv == kBalHeads) {
+    const dim3 hgrid((unsigned)(p.bal_wgs * 2));
+    if (head_dim == 128) {
+      if (bias) hipLaunchKernelGGL((decode_heads_kernel<128, true>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((decode_heads_kernel<128, false>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((combine_heads_kernel<128>), hgrid, cblock, 0, stream, p);
+    } else {
+      if (bias) hipLaunchKernelGGL((decode_heads_kernel<64, true>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((decode_heads_kernel<64, false>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((combine_heads_kernel<64>), hgrid, cblock, 0, stream, p);
+    }
+    return hipGetLastError();
+  }
   if (head_dim == 128) {
     if (bias) hipLaunchKernelGGL((decode_balanced_kernel<128, true>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((decode_balanced_kernel<128, false>), grid, block, 0, stream, p);

@@ -143,9 +143,14 @@ BAL_CASES = {
 }
 
 
+@pytest.mark.parametrize("heads8", [False, True], ids=["kv_heads_as_listed", "kv_heads_8"])
 @pytest.mark.parametrize("name", list(BAL_CASES))
-def test_balanced_decode_cases(name):
+def test_balanced_decode_cases(name, heads8):
+    """heads8 runs the case with eight kv heads (same GQA group size), the
+    form where every wave of a workgroup streams its own kv head."""
     ql, kl, H, Hkv, D, BS, R, causal, win, scale = BAL_CASES[name]
+    if heads8:
+        H, Hkv = H * 8 // Hkv, 8
     kw = {} if scale is None else {"softmax_scale": scale}
     w = wl.build(ql, kl, num_heads=H, num_kv_heads=Hkv, head_dim=D, block_size=BS, rel_extent=R,
                  causal=causal, window_size=win, seed=sum(map(ord, name)), extra_pages=3, poison=True, **kw)
@@ -154,21 +159,23 @@ def test_balanced_decode_cases(name):
     _compare(out, lse, *ref, tag=f"{name} balanced")
 
 
-def test_balanced_decode_many_requests():
+@pytest.mark.parametrize("Hkv", [2, 8])
+def test_balanced_decode_many_requests(Hkv):
     """More requests than CUs, ragged lengths 0..1500: pieces of many pairs
     per workgroup, and pairs cut across workgroup boundaries."""
     g = torch.Generator().manual_seed(77)
     B = 300
     kl = [int(x) for x in torch.randint(0, 1500, (B,), generator=g)]
-    w = wl.build([1] * B, kl, num_heads=8, num_kv_heads=2, head_dim=128, rel_extent=64, seed=78,
+    w = wl.build([1] * B, kl, num_heads=4 * Hkv, num_kv_heads=Hkv, head_dim=128, rel_extent=64, seed=78,
                  extra_pages=2, poison=True)
     ref = _oracle(w)
     out, lse = _gpu_run(w.to("cuda"), 0)
     _compare(out, lse, *ref, tag="many requests balanced")
 
 
-def test_balanced_decode_repeatable_and_page_permutation_exact():
-    w = wl.build([1, 1, 2], [5000, 300, 2000], num_heads=8, num_kv_heads=2, head_dim=128,
+@pytest.mark.parametrize("Hkv", [2, 8])
+def test_balanced_decode_repeatable_and_page_permutation_exact(Hkv):
+    w = wl.build([1, 1, 2], [5000, 300, 2000], num_heads=4 * Hkv, num_kv_heads=Hkv, head_dim=128,
                  rel_extent=64, seed=41, extra_pages=4)
     wg = w.to("cuda")
     a = bnd.attn_workload(wg, num_splits=0)
