@@ -279,9 +279,13 @@ def main(argv=None):
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
         value, unit = wk["bytes"] / ms / 1e6, "GB/s"
     if S == 0:
-        # Balanced decode: the attention kernel and the combine of the pairs
-        # cut between workgroups; kernel_ms is the whole step (both kernels).
-        roof["kernel"] = "decode_balanced_kernel<128> + combine_balanced_kernel<128>"
+        # Balanced decode: the attention kernel and the combine of the
+        # requests cut between workgroups; kernel_ms is the whole step (both
+        # kernels).  Eight kv heads take the form with one kv head per wave.
+        if w.num_kv_heads == 8:
+            roof["kernel"] = "decode_heads_kernel<128> + combine_heads_kernel<128>"
+        else:
+            roof["kernel"] = "decode_balanced_kernel<128> + combine_balanced_kernel<128>"
     else:
         roof["kernel"] = "attn_kernel<128>"
     roof["kernel_ms"] = round(kernel_ms, 5)

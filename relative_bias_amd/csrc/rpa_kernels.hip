@@ -378,16 +378,15 @@ __device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t a, uint32_t 
 }
 
 // Accumulator start of a general tile, by what the tile needs:
-//   kInitEdge:     no bias; 0 where visible, masked elsewhere;
-//   kInitBand:     bias/scale where in the band and visible, 0 where visible
-//                  only, masked elsewhere;
-//   kInitBandVis:  every visible key of the tile is in every row's band:
-//                  bias/scale where visible, masked elsewhere;
-//   kInitBandOnly: every key of the tile is visible to every row:
-//                  bias/scale in the band, 0 elsewhere;
-//   kInitFull:     every key visible and in the band: bias/scale.
-// sacc holds the raw loaded bias values for the band modes.
-enum { kInitEdge, kInitBand, kInitBandVis, kInitBandOnly, kInitFull };
+//   kInitEdge: no bias; 0 where visible, masked elsewhere;
+//   kInitBand: bias/scale where in the band and visible, 0 where visible
+//              only, masked elsewhere;
+//   kInitFull: every key of the tile visible to, and in the band of, every
+//              row: bias/scale.
+// sacc holds the raw loaded bias values for the band modes.  (Tiles that
+// need only one of the two masks measured no faster with a form of their
+// own, which costs registers.)
+enum { kInitEdge, kInitBand, kInitFull };
 template <int MODE>
 __device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv_scale, float masked) {
   if constexpr (MODE == kInitFull) {
@@ -395,8 +394,8 @@ __device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv
     for (int kb2 = 0; kb2 < 2; ++kb2) sacc[kb2] *= inv_scale;
     return;
   }
-  constexpr bool USE_VIS = MODE != kInitBandOnly;
-  constexpr bool USE_BAND = MODE == kInitBand || MODE == kInitBandOnly;
+  constexpr bool USE_VIS = true;
+  constexpr bool USE_BAND = MODE == kInitBand;
   const uint32_t vis = USE_VIS ? range_bits(tb.vis_lo, tb.vis_hi) : 0u;
   const uint32_t band = USE_BAND ? range_bits(tb.band_lo, tb.band_hi) : 0u;
   const uint32_t mbits = __float_as_uint(masked);
@@ -758,13 +757,6 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   const int full_lo = __builtin_amdgcn_readfirstlane(max(in_lo, qa_max - p.R + 1));
   const int full_hi = __builtin_amdgcn_readfirstlane(min(in_hi, qa_min));
   auto is_full_band = [&](int kb) { return kb >= full_lo && kb + kTileKeys - 1 <= full_hi; };
-  // Every key of the tile visible to every row; every visible key of the
-  // tile inside every row's band (no visible key past qa, none below
-  // qa_max - R + 1).
-  auto is_all_vis = [&](int kb) { return kb >= in_lo && kb + kTileKeys - 1 <= in_hi; };
-  const bool vis_below_qa = p.causal || p.right == 0;
-  const int band_all_lo = __builtin_amdgcn_readfirstlane(qa_max - p.R + 1);
-  auto band_covers_vis = [&](int kb) { return vis_below_qa && kb >= band_all_lo; };
   auto bounds = [&](int kb) {
     const int off = kb + 4 * hf;
     return TileBounds{lo_r - off, hi_r - off, qa - p.R + 1 - off, qa - off};
@@ -793,8 +785,6 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   auto finish = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
     if (is_band(kb)) {
       if (is_full_band(kb)) tile_init<kInitFull>(sacc, bounds(kb), inv_scale, masked);
-      else if (is_all_vis(kb)) tile_init<kInitBandOnly>(sacc, bounds(kb), inv_scale, masked);
-      else if (band_covers_vis(kb)) tile_init<kInitBandVis>(sacc, bounds(kb), inv_scale, masked);
       else tile_init<kInitBand>(sacc, bounds(kb), inv_scale, masked);
     }
   };
