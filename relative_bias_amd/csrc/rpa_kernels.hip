@@ -11,8 +11,8 @@
 //
 // One launch serves a whole mixed batch.  Workgroup id = (item, kv head,
 // split); each workgroup finds its item by scanning cu_seqlens_q on the
-// device (no host metadata, no device->host copy).  Prefill q-tiles are
-// numbered first, heaviest tile of each request first, then decode items.
+// device (no host metadata, no device->host copy).  Decode items are
+// numbered first, then prefill q-tiles, heaviest tile of each request first.
 //   * prefill item: 128 (token, q-head) rows of one kv head.  Four waves,
 //     32 rows each.  S^T = K·Q^T and O^T = V^T·P^T on 32x32x16 bf16 MFMA so
 //     that each lane owns one query row: softmax statistics stay lane-local
@@ -177,24 +177,29 @@ struct Item {
   int kmax;  // longest cache_seqlens in the batch (sets the split chunk)
 };
 
-// Maps a linear work-item index to (request, tile).  Items [0, NP) are the
-// prefill q-tiles in request order, the heaviest (last) tile of a request
-// first; items [NP, NP + ND) are the decode items in request order.  Every
+// Maps a linear work-item index to (request, tile).  Items [0, ND) are the
+// decode items in request order, items [ND, ND + NP) the prefill q-tiles in
+// request order, the heaviest (last) tile of a request first.  Decode items
+// go first so that their streaming overlaps the prefill tiles' compute
+// (about 1 % on a mixed batch) instead of running in the tail.  Every
 // wave scans independently (the reads hit cache), so no barrier is needed.
 __device__ Item resolve_item(const AttnParams &p, int item, bool decode_only, int rows) {
   const int lane = threadIdx.x & 63;
-  int np = 0, kmax = 0;
+  int np = 0, kmax = 0, nd = 0;
   for (int c = 0; c < p.batch; c += 64) {
     const int b = c + lane;
     if (b < p.batch) {
       kmax = max(kmax, p.cache_seqlens[b]);
-      if (!decode_only) np += prefill_tiles(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b], p.G, rows);
+      const int lqb = p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b];
+      if (!decode_only) np += prefill_tiles(lqb, p.G, rows);
+      nd += is_decode(lqb, p.G) ? 1 : 0;
     }
   }
   kmax = wave_max_i(kmax);
   np = wave_sum_i(np);
-  const bool pre = item < np;
-  const int target = pre ? item : item - np;
+  nd = wave_sum_i(nd);
+  const bool pre = item >= nd;
+  const int target = pre ? item - nd : item;
   int base = 0;
   for (int c = 0; c < p.batch; c += 64) {
     const int b = c + lane;
