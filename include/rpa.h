@@ -87,9 +87,10 @@ typedef enum {
  *                  from max_seqlen_q), batch <= 2048 and rel_logits spans
  *                  less than 2 GiB, the 16-key blocks of the whole batch are
  *                  dealt out in equal contiguous shares, one per compute unit
- *                  of the current device, and the pieces of a (request, kv
- *                  head) cut between shares are merged by the same combine;
- *                  otherwise S = 0 runs as S = 1.  rpa_choose_splits gives a
+ *                  of the current device (with 8 kv heads a block covers all
+ *                  heads, else one (request, kv head) pair), and the pieces of
+ *                  a request cut between shares are merged by the same
+ *                  combine; otherwise S = 0 runs as S = 1.  rpa_choose_splits gives a
  *                  default.  Any S gives the same result up to fp32 rounding.
  *   workspace      device scratch of at least rpa_workspace_bytes(S, ...)
  *                  bytes when S != 1 (may be NULL when S == 1); holds split
@@ -119,9 +120,9 @@ int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cach
  * partials: num_splits * num_tokens * num_heads * (head_dim + 1) * 4 bytes
  * (fp32 partial outputs and LSEs), rounded up to 256; 0 when num_splits == 1.
  * num_splits = 0 needs a fixed size for head_dim, whatever the batch:
- * 16 KiB of per-workgroup records plus 1024 * 16 * (head_dim + 1) * 4 bytes
- * of partials (about 8.5 MB for head_dim 128).  Returns 0 for negative
- * sizes.
+ * 16 KiB of per-workgroup records plus 8192 * 16 * (head_dim + 1) * 4 bytes
+ * of partials (two slots of eight kv heads for each of up to 512
+ * workgroups; about 68 MB for head_dim 128).  Returns 0 for negative sizes.
  */
 size_t rpa_workspace_bytes(int32_t num_splits, int32_t num_tokens, int32_t num_heads,
                            int32_t head_dim);
