@@ -344,3 +344,48 @@ def test_long_decode_sampled_heads():
     for S in (bnd.rpa_choose_splits(1, 1, 64, 8, 1 << 20), 16):
         out, lse = _gpu_run(wg, S)
         _compare(out, lse, *ref, heads=heads, tag=f"long_decode S={S}")
+
+
+# ------------------------------------------------------ seeded random cases
+
+def _random_case(seed):
+    """A seeded random configuration: batch mix of decode and prefill
+    requests, GQA group, head_dim, block size, bias extent, mask and scale."""
+    g = torch.Generator().manual_seed(1000 + seed)
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=g))
+    Hkv = [1, 2, 4, 8][ri(0, 3)]
+    G = [1, 2, 4, 8][ri(0, 3)]
+    D = [64, 128][ri(0, 1)]
+    BS = [16, 32, 48][ri(0, 2)]
+    B = ri(1, 6)
+    q_lens, k_lens = [], []
+    for _ in range(B):
+        kind = ri(0, 2)
+        lq = 1 if kind == 0 else (ri(1, 3) if kind == 1 else ri(4, 160))
+        lk = ri(0, 700) + (lq if ri(0, 4) else 0)
+        q_lens.append(lq)
+        k_lens.append(lk)
+    R = [0, 1, 7, 64, 300][ri(0, 4)]
+    causal = bool(ri(0, 3))
+    left = [-1, -1, 0, 37, 200][ri(0, 4)]
+    right = [-1, 0, 0, 5][ri(0, 3)] if not causal else [-1, 0][ri(0, 1)]
+    scale = [None, None, 0.05, -0.08][ri(0, 3)]
+    S = [1, 1, 2, 5, 0][ri(0, 4)]
+    return dict(q_lens=q_lens, k_lens=k_lens, H=G * Hkv, Hkv=Hkv, D=D, BS=BS, R=R, causal=causal,
+                window=(left, right), scale=scale, S=S)
+
+
+@pytest.mark.parametrize("seed", list(range(24)))
+def test_random_configurations(seed):
+    """Parity on 24 seeded random configurations (mixed decode and prefill
+    batches, every GQA group size, both head sizes, three block sizes,
+    windows, bias extents from 0 to 300, negative and small scales, split
+    counts 0/1/2/5)."""
+    cfg = _random_case(seed)
+    kw = {} if cfg["scale"] is None else {"softmax_scale": cfg["scale"]}
+    w = wl.build(cfg["q_lens"], cfg["k_lens"], num_heads=cfg["H"], num_kv_heads=cfg["Hkv"], head_dim=cfg["D"],
+                 block_size=cfg["BS"], rel_extent=cfg["R"], causal=cfg["causal"], window_size=cfg["window"],
+                 seed=seed, extra_pages=2, poison=True, **kw)
+    ref = _oracle(w)
+    out, lse = _gpu_run(w.to("cuda"), cfg["S"])
+    _compare(out, lse, *ref, tag=f"random seed={seed} {cfg}")
