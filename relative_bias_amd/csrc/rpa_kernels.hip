@@ -1741,12 +1741,11 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
   if (cur < u1) {
     Piece P = make_piece(cur);
     bf16x8 qf[QK];
-    load_q(P, qf);
-    // Q is in before the first direct load is issued, so that no later
-    // wait on the Q registers can count the unit loads in flight.
-    wait_vm<0>();
+    // The first unit's loads go out before Q's, so that the two latencies
+    // overlap; the wait before the first unit is computed covers both.
     int slot0 = 0;        // stage of this wave's first unit of P
     if (P.my_n > 0) issue(P, 0, page_of(P, 0), 0);
+    load_q(P, qf);
     while (true) {
       const int cur_next = cur + (P.j1 - P.j0);
       const bool has_next = cur_next < u1;
@@ -2272,12 +2271,11 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
   if (cur < u1) {
     Piece P = make_piece(cur);
     bf16x8 qf[QK];
-    load_q(P, qf);
-    // Q is in before the first direct load is issued, so that no later
-    // wait on the Q registers can count the unit loads in flight.
-    wait_vm<0>();
+    // The first unit's loads go out before Q's, so that the two latencies
+    // overlap; the wait before the first unit is computed covers both.
     int slot = 0;  // stage of the next unit to compute
     issue(P, 0, page_of(P, 0), 0);
+    load_q(P, qf);
     while (true) {
       const int cur_next = cur + P.n;
       const bool has_next = cur_next < u1;
