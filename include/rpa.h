@@ -160,6 +160,47 @@ int rpa_split_combine(const float *partial_out, const float *partial_lse, int32_
 int rpa_choose_splits(int32_t batch, int32_t max_seqlen_q, int32_t num_heads,
                       int32_t num_kv_heads, int64_t max_seqlen_k, int is_local, int32_t num_cus);
 
+/*
+ * rpa_slot_mapping: the cache slot of every query token of a batch — the
+ * slot_mapping of "vLLM V1 Attention — Part 2: 标准Attention后端实现"
+ * (devpress.csdn.net), 附录O.1 Step 2.  Token j of request b (packed token
+ * cu_seqlens_q[b] + j, Lq = cu_seqlens_q[b+1] - cu_seqlens_q[b]) sits at
+ * position pos = cache_seqlens[b] - Lq + j and gets the slot
+ * block_table[b, pos / block_size] * block_size + pos % block_size, or -1
+ * when pos < 0 (a request with fewer keys than queries).
+ *
+ *   block_table, max_pages_per_seq, cache_seqlens, cu_seqlens_q, batch,
+ *   num_tokens, block_size   as for rpa_attn_varlen (device metadata is not
+ *                            checked; block_size any positive value).
+ *   slot_mapping             int64 [num_tokens], written.
+ */
+int rpa_slot_mapping(const int32_t *block_table, int32_t max_pages_per_seq, const int32_t *cache_seqlens,
+                     const int32_t *cu_seqlens_q, int32_t batch, int32_t num_tokens, int32_t block_size,
+                     int64_t *slot_mapping, void *stream);
+
+/*
+ * rpa_kv_cache_write: writes this step's keys and values into the paged
+ * caches before attention — reshape_and_cache in "vLLM V1 Attention — Part
+ * 2", 6.5 (FlashInferImpl.forward, step 2).  For every token t with
+ * 0 <= s = slot_mapping[t] < num_blocks * block_size:
+ *     key_cache[s / block_size, s % block_size] = key[t]
+ *     value_cache[s / block_size, s % block_size] = value[t]
+ * and other tokens write nothing (a negative slot is padding; a slot past the
+ * cache is skipped rather than faulted).  Slots must be distinct; rows are
+ * copied bit for bit.
+ *
+ *   key, value        bf16 [num_tokens, num_kv_heads, head_dim], 16-byte aligned.
+ *   slot_mapping      int64 [num_tokens].
+ *   key_cache,
+ *   value_cache       bf16 [num_blocks, block_size, num_kv_heads, head_dim],
+ *                     16-byte aligned, written in place.
+ * num_kv_heads * head_dim must be a multiple of 8 (16-byte rows), else
+ * RPA_ERR_UNSUPPORTED.
+ */
+int rpa_kv_cache_write(const void *key, const void *value, const int64_t *slot_mapping, int32_t num_tokens,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                       void *key_cache, void *value_cache, void *stream);
+
 /* rpa_status_string: static text for a status code (never NULL). */
 const char *rpa_status_string(int status);
 

@@ -58,6 +58,10 @@ def lib():
     L.rpa_choose_splits.restype = ctypes.c_int
     L.rpa_status_string.argtypes = [ctypes.c_int]
     L.rpa_status_string.restype = ctypes.c_char_p
+    L.rpa_slot_mapping.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, vp]
+    L.rpa_slot_mapping.restype = ctypes.c_int
+    L.rpa_kv_cache_write.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    L.rpa_kv_cache_write.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -185,6 +189,49 @@ def rpa_split_combine(partial_out: torch.Tensor, partial_lse: torch.Tensor,
     if st != RPA_OK:
         raise RpaError(st, "rpa_split_combine")
     return out, lse
+
+
+def rpa_slot_mapping(block_table: torch.Tensor, cache_seqlens: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                     block_size: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Cache slot (int64) of every packed query token; -1 where a request has
+    fewer keys than queries."""
+    dev = cu_seqlens_q.device
+    _check(block_table, "block_table", torch.int32, dev, 2)
+    _check(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
+    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, 1)
+    B = cache_seqlens.shape[0]
+    if cu_seqlens_q.shape[0] != B + 1 or block_table.shape[0] != B:
+        raise ValueError("batch sizes of block_table / cache_seqlens / cu_seqlens_q disagree")
+    T = int(cu_seqlens_q[-1].item()) if out is None else out.shape[0]
+    if out is None:
+        out = torch.empty((T,), dtype=torch.int64, device=dev)
+    _check(out, "slot_mapping", torch.int64, dev, 1)
+    st = lib().rpa_slot_mapping(_ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), _ptr(cu_seqlens_q),
+                                B, T, block_size, _ptr(out), _stream(dev))
+    if st != RPA_OK:
+        raise RpaError(st, "rpa_slot_mapping")
+    return out
+
+
+def rpa_kv_cache_write(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,
+                       key_cache: torch.Tensor, value_cache: torch.Tensor) -> None:
+    """Write key/value [T, Hkv, D] rows into the paged caches at their slots."""
+    dev = key.device
+    _check(key, "key", torch.bfloat16, dev, 3)
+    _check(value, "value", torch.bfloat16, dev, 3)
+    _check(slot_mapping, "slot_mapping", torch.int64, dev, 1)
+    _check(key_cache, "key_cache", torch.bfloat16, dev, 4)
+    _check(value_cache, "value_cache", torch.bfloat16, dev, 4)
+    T, Hkv, D = key.shape
+    NB, BS = key_cache.shape[0], key_cache.shape[1]
+    if tuple(value.shape) != (T, Hkv, D) or slot_mapping.shape[0] != T:
+        raise ValueError("key / value / slot_mapping shapes disagree")
+    if tuple(key_cache.shape) != (NB, BS, Hkv, D) or tuple(value_cache.shape) != (NB, BS, Hkv, D):
+        raise ValueError("cache shapes disagree with key")
+    st = lib().rpa_kv_cache_write(_ptr(key), _ptr(value), _ptr(slot_mapping), T, Hkv, D, NB, BS,
+                                  _ptr(key_cache), _ptr(value_cache), _stream(dev))
+    if st != RPA_OK:
+        raise RpaError(st, "rpa_kv_cache_write")
 
 
 def attn_workload(w, *, num_splits: Optional[int] = None, return_lse: bool = True, out=None, lse=None,

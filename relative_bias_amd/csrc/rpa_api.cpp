@@ -203,4 +203,45 @@ int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cach
   return RPA_OK;
 }
 
+int rpa_slot_mapping(const int32_t *block_table, int32_t max_pages_per_seq, const int32_t *cache_seqlens,
+                     const int32_t *cu_seqlens_q, int32_t batch, int32_t num_tokens, int32_t block_size,
+                     int64_t *slot_mapping, void *stream) {
+  if (batch < 0 || num_tokens < 0 || block_size <= 0 || max_pages_per_seq < 0) return RPA_ERR_SHAPE;
+  if (batch == 0 && num_tokens > 0) return RPA_ERR_SHAPE;
+  if (num_tokens == 0) return RPA_OK;
+  if (!block_table || !cache_seqlens || !cu_seqlens_q || !slot_mapping) return RPA_ERR_NULL;
+  rpa::SlotParams p;
+  p.block_table = block_table;
+  p.cache_seqlens = cache_seqlens;
+  p.cu_seqlens_q = cu_seqlens_q;
+  p.slots = slot_mapping;
+  p.batch = batch;
+  p.num_tokens = num_tokens;
+  p.P = max_pages_per_seq;
+  p.BS = block_size;
+  return rpa::launch_slot_mapping(p, static_cast<hipStream_t>(stream)) == hipSuccess ? RPA_OK : RPA_ERR_HIP;
+}
+
+int rpa_kv_cache_write(const void *key, const void *value, const int64_t *slot_mapping, int32_t num_tokens,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                       void *key_cache, void *value_cache, void *stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks < 0 || block_size <= 0)
+    return RPA_ERR_SHAPE;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (row % 8 != 0) return RPA_ERR_UNSUPPORTED;
+  if (row / 8 > INT32_MAX) return RPA_ERR_SHAPE;
+  if (num_tokens == 0) return RPA_OK;
+  if (!key || !value || !slot_mapping || !key_cache || !value_cache) return RPA_ERR_NULL;
+  rpa::KvWriteParams p;
+  p.key = static_cast<const uint16_t *>(key);
+  p.value = static_cast<const uint16_t *>(value);
+  p.slots = slot_mapping;
+  p.key_cache = static_cast<uint16_t *>(key_cache);
+  p.value_cache = static_cast<uint16_t *>(value_cache);
+  p.capacity = (int64_t)num_blocks * block_size;
+  p.num_tokens = num_tokens;
+  p.row_units = (int32_t)(row / 8);
+  return rpa::launch_kv_write(p, static_cast<hipStream_t>(stream)) == hipSuccess ? RPA_OK : RPA_ERR_HIP;
+}
+
 }  // extern "C"

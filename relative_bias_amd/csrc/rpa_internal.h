@@ -59,6 +59,24 @@ struct CombineParams {
   int32_t S, rows, D;           // rows = T * H
 };
 
+struct SlotParams {
+  const int32_t *block_table;   // [B, P]
+  const int32_t *cache_seqlens; // [B]
+  const int32_t *cu_seqlens_q;  // [B+1]
+  int64_t *slots;               // [T]
+  int32_t batch, num_tokens, P, BS;
+};
+
+struct KvWriteParams {
+  const uint16_t *key;          // bf16 [T, Hkv, D]
+  const uint16_t *value;        // bf16 [T, Hkv, D]
+  const int64_t *slots;         // [T]
+  uint16_t *key_cache;          // bf16 [NB, BS, Hkv, D]
+  uint16_t *value_cache;        // bf16 [NB, BS, Hkv, D]
+  int64_t capacity;             // NB * BS slots
+  int32_t num_tokens, row_units;  // row_units: 16-byte units per token row (Hkv * D / 8)
+};
+
 // Number of work items a request with lq query tokens contributes.
 __host__ __device__ inline int64_t items_for_request(int64_t lq, int64_t G) {
   if (lq <= 0) return 0;
@@ -71,6 +89,8 @@ __host__ __device__ inline int64_t items_for_request(int64_t lq, int64_t G) {
 hipError_t launch_attention(const AttnParams &p, int head_dim, int64_t n_items_ub, bool decode_only,
                             hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
+hipError_t launch_slot_mapping(const SlotParams &p, hipStream_t stream);
+hipError_t launch_kv_write(const KvWriteParams &p, hipStream_t stream);
 // Balanced decode: the attention kernel on p.bal_wgs workgroups, then the
 // combine of the pairs cut between workgroups.
 hipError_t launch_balanced_decode(const AttnParams &p, int head_dim, hipStream_t stream);

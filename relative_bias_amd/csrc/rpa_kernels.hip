@@ -2521,7 +2521,80 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   if (lane == 0 && p.lse) p.lse[row] = M + log2_fast(W) * kLn2;
 }
 
+// ------------------------------------------------------- paged KV write
+//
+// The step before attention ("vLLM V1 Attention — Part 2", 附录O.1 Step 2
+// and 6.5 step 2): each new token's cache slot, and the copy of its key
+// and value rows into the pages.
+
+// One thread per token: its request is the last b with cu_seqlens_q[b] <=
+// token (empty requests share their start with the next one).
+__global__ __launch_bounds__(kThreads) void slot_mapping_kernel(SlotParams p) {
+  const int tok = blockIdx.x * kThreads + threadIdx.x;
+  if (tok >= p.num_tokens) return;
+  int lo = 0, hi = p.batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.cu_seqlens_q[mid] <= tok) lo = mid;
+    else hi = mid - 1;
+  }
+  const int c0 = p.cu_seqlens_q[lo];
+  const int lq = p.cu_seqlens_q[lo + 1] - c0;
+  const int pos = p.cache_seqlens[lo] - lq + (tok - c0);
+  int64_t slot = -1;
+  if (pos >= 0) slot = (int64_t)p.block_table[(int64_t)lo * p.P + pos / p.BS] * p.BS + pos % p.BS;
+  p.slots[tok] = slot;
+}
+
+// One wave per token at a time: the token's key and value rows (row_units
+// 16-byte units each) are copied to row `slot` of the caches, which is
+// contiguous in the [blocks, block_size, kv heads, head_dim] layout.  Every
+// lane has its units of both rows in flight before any store.
+__global__ __launch_bounds__(kThreads) void kv_write_kernel(KvWriteParams p) {
+  const int lane = threadIdx.x & 63;
+  const int nwave = gridDim.x * (kThreads / 64);
+  const int n = p.row_units;
+  for (int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); t < p.num_tokens; t += nwave) {
+    const int64_t slot = p.slots[t];
+    if (slot < 0 || slot >= p.capacity) continue;
+    const u32x4 *sk = reinterpret_cast<const u32x4 *>(p.key) + (int64_t)t * n;
+    const u32x4 *sv = reinterpret_cast<const u32x4 *>(p.value) + (int64_t)t * n;
+    u32x4 *dk = reinterpret_cast<u32x4 *>(p.key_cache) + slot * n;
+    u32x4 *dv = reinterpret_cast<u32x4 *>(p.value_cache) + slot * n;
+    int c = lane;
+    for (; c + 64 < n; c += 128) {
+      const u32x4 k0 = sk[c], k1 = sk[c + 64], v0 = sv[c], v1 = sv[c + 64];
+      dk[c] = k0;
+      dk[c + 64] = k1;
+      dv[c] = v0;
+      dv[c + 64] = v1;
+    }
+    if (c < n) {
+      const u32x4 k0 = sk[c], v0 = sv[c];
+      dk[c] = k0;
+      dv[c] = v0;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_slot_mapping(const SlotParams &p, hipStream_t stream) {
+  if (p.num_tokens <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((p.num_tokens + kThreads - 1) / kThreads)), block(kThreads);
+  hipLaunchKernelGGL(slot_mapping_kernel, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_write(const KvWriteParams &p, hipStream_t stream) {
+  if (p.num_tokens <= 0) return hipSuccess;
+  // One wave per token up to 2048 workgroups (8 per CU); beyond that the
+  // waves loop over the tokens.
+  const int64_t wgs = ((int64_t)p.num_tokens + kThreads / 64 - 1) / (kThreads / 64);
+  const dim3 grid((unsigned)(wgs < 2048 ? wgs : 2048)), block(kThreads);
+  hipLaunchKernelGGL(kv_write_kernel, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_attention(const AttnParams &p, int head_dim, int64_t n_items_ub, bool decode_only,
                             hipStream_t stream) {

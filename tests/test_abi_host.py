@@ -34,7 +34,7 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("rpa_attn_varlen", "rpa_split_combine", "rpa_choose_splits", "rpa_workspace_bytes",
-              "rpa_status_string"):
+              "rpa_status_string", "rpa_slot_mapping", "rpa_kv_cache_write"):
         assert n in names
 
 
@@ -124,6 +124,32 @@ def test_combine_argument_errors(L):
     assert c(None, FAKE, 2, 4, 2, 64, FAKE, None, None) == NULL
     assert c(FAKE, FAKE, 2, 4, 2, 64, None, None, None) == NULL
     assert c(None, None, 2, 0, 2, 64, None, None, None) == OK
+
+
+def test_slot_mapping_argument_errors(L):
+    f = L.rpa_slot_mapping
+    assert f(FAKE, 4, FAKE, FAKE, -1, 3, 16, FAKE, None) == SHAPE
+    assert f(FAKE, 4, FAKE, FAKE, 2, -1, 16, FAKE, None) == SHAPE
+    assert f(FAKE, 4, FAKE, FAKE, 2, 3, 0, FAKE, None) == SHAPE
+    assert f(FAKE, -1, FAKE, FAKE, 2, 3, 16, FAKE, None) == SHAPE
+    assert f(FAKE, 4, FAKE, FAKE, 0, 3, 16, FAKE, None) == SHAPE
+    assert f(None, 4, FAKE, FAKE, 2, 3, 16, FAKE, None) == NULL
+    assert f(FAKE, 4, FAKE, FAKE, 2, 3, 16, None, None) == NULL
+    assert f(None, 4, None, None, 2, 0, 16, None, None) == OK
+
+
+def test_kv_cache_write_argument_errors(L):
+    f = L.rpa_kv_cache_write
+    assert f(FAKE, FAKE, FAKE, -1, 2, 64, 4, 16, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 3, 0, 64, 4, 16, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 3, 2, 0, 4, 16, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 3, 2, 64, -1, 16, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 3, 2, 64, 4, 0, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 3, 1, 12, 4, 16, FAKE, FAKE, None) == UNSUP  # 24-byte rows
+    assert f(None, FAKE, FAKE, 3, 2, 64, 4, 16, FAKE, FAKE, None) == NULL
+    assert f(FAKE, FAKE, None, 3, 2, 64, 4, 16, FAKE, FAKE, None) == NULL
+    assert f(FAKE, FAKE, FAKE, 3, 2, 64, 4, 16, FAKE, None, None) == NULL
+    assert f(None, None, None, 0, 2, 64, 4, 16, None, None, None) == OK
 
 
 # ------------------------------------------------------------------ planner
