@@ -137,6 +137,36 @@ def measure(runner, steps, warmup, settle_s=0.0):
     return ms, ms_comb, wk
 
 
+def measure_kv_write(steps, warmup):
+    """The paged KV write of the chunked-prefill batch's 8173 new tokens (8 kv
+    heads, head_dim 128): rpa_slot_mapping then rpa_kv_cache_write, timed
+    together.  Algorithmic bytes: the K and V rows read and written, the
+    slots written and read, and the metadata the slot kernel reads."""
+    import torch
+    from relative_bias_amd import binding as bnd
+    from relative_bias_amd import workloads as wl
+    w = wl.chunked_prefill(device="cpu").to("cuda")
+    T, Hkv, D = w.num_tokens, w.num_kv_heads, w.head_dim
+    g = torch.Generator(device="cuda").manual_seed(3)
+    key = torch.randn((T, Hkv, D), generator=g, device="cuda").to(torch.bfloat16)
+    val = torch.randn((T, Hkv, D), generator=g, device="cuda").to(torch.bfloat16)
+    slots = torch.empty((T,), dtype=torch.int64, device="cuda")
+
+    def step(i=0):
+        bnd.rpa_slot_mapping(w.block_table, w.cache_seqlens, w.cu_seqlens_q, w.block_size, out=slots)
+        bnd.rpa_kv_cache_write(key, val, slots, w.key_cache, w.value_cache)
+
+    settle(step, SETTLE_S)
+    ms = time_calls(step, steps, warmup, torch.cuda.current_stream())
+    row = Hkv * D * 2
+    nbytes = 2 * T * row * 2 + T * 8 * 2 + T * 4 + (2 * w.batch + 1) * 4
+    info = {"workload": "kv_write (chunked_prefill tokens)", "num_tokens": T, "num_kv_heads": Hkv,
+            "head_dim": D, "block_size": w.block_size, "alg_bytes": nbytes}
+    del w, key, val, slots
+    torch.cuda.empty_cache()
+    return ms, dict(info, bytes=nbytes)
+
+
 def cpu_baseline(w, budget_s=20.0):
     """The fp64 oracle on a bounded sample of the decode batch (whole requests,
     taken in order until about budget_s of CPU time), in GB/s of the same
@@ -177,7 +207,7 @@ def main(argv=None):
     ap.add_argument("--no-extra", action="store_true", help="only the headline decode batch")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None, help="run one workload: batched_decode, chunked_prefill, "
-                                                  "long_decode, continuous_batch")
+                                                  "long_decode, continuous_batch, kv_write")
     ap.add_argument("--splits", type=int, default=None,
                     help="override the planner's num_splits (0 = balanced decode) for the headline decode batch "
                          "(or for long_decode with --only long_decode)")
@@ -208,6 +238,7 @@ def main(argv=None):
     torch.manual_seed(0)
     dev = "cuda"
     results = {}
+    kv_summary = None
 
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
@@ -252,6 +283,16 @@ def main(argv=None):
                 f"{wk['flops'] / ms / 1e9:.1f} TFLOP/s")
             del r5, w5
             torch.cuda.empty_cache()
+        if a.only in (None, "kv_write"):
+            try:
+                ms_kv, kvinfo = measure_kv_write(max(5, a.steps // 2), a.warmup)
+                log(f"kv_write: {ms_kv * 1e3:.1f} us/step, {kvinfo['bytes'] / ms_kv / 1e6:.1f} GB/s")
+                kv_summary = dict(kvinfo, ms_per_step=round(ms_kv, 5),
+                                  gbs=round(kvinfo["bytes"] / ms_kv / 1e6, 2),
+                                  hbm_frac=round(kvinfo["bytes"] / ms_kv / 1e6 / HBM_PEAK_GBS, 4))
+            except Exception as e:  # reported in the line; never hides the headline
+                log(f"kv_write failed: {e!r}")
+                kv_summary = {"workload": "kv_write (chunked_prefill tokens)", "error": repr(e)}
 
     def summary(name):
         w, S, ms, ms_c, wk = results[name]
@@ -264,6 +305,9 @@ def main(argv=None):
                 "mfma_frac": round(wk["flops"] / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
                 "alg_bytes": wk["bytes"], "alg_flops": wk["flops"]}
 
+    if a.only == "kv_write":
+        print(json.dumps({"kv_write": kv_summary, "kernel_hash": kernel_hash()}))
+        return 0
     head = a.only if a.only else "batched_decode"
     w, S, ms, ms_c, wk = results[head]
     kernel_ms = ms - ms_c
@@ -300,6 +344,8 @@ def main(argv=None):
     for name in results:
         if name != head:
             line[name] = summary(name)
+    if kv_summary is not None:
+        line["kv_write"] = kv_summary
     if not a.no_cpu and head == "batched_decode":
         log("timing the CPU oracle on a sample ...")
         line["cpu_baseline"] = cpu_baseline(w)
