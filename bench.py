@@ -167,36 +167,37 @@ def measure_kv_write(steps, warmup):
     return ms, dict(info, bytes=nbytes)
 
 
-def cpu_baseline(w, budget_s=20.0):
-    """The fp64 oracle on a bounded sample of the decode batch (whole requests,
-    taken in order until about budget_s of CPU time), in GB/s of the same
-    algorithmic bytes."""
+def cpu_baseline(w, budget_s=12.0):
+    """The fp64 oracle on a bounded sample of the decode batch: whole requests
+    in order, passing over the batch again until about budget_s of CPU time
+    has been spent, in GB/s of the same algorithmic bytes."""
     import torch
     from oracle import attention as orc
     from relative_bias_amd import metrics
     wc = w.to("cpu")
     cu = wc.cu_seqlens_q.tolist()
     done_bytes, spent, nreq = 0, 0.0, 0
-    for b in range(wc.batch):
-        toks = list(range(cu[b], cu[b + 1]))
-        t0 = time.perf_counter()
-        orc.attention(wc.q, wc.key_cache, wc.value_cache, wc.block_table, wc.cache_seqlens,
-                      wc.cu_seqlens_q, wc.softmax_scale, wc.causal, wc.window_size, wc.rel_extent,
-                      wc.rel_logits, tokens=toks)
-        spent += time.perf_counter() - t0
-        sub = type("W", (), {})()
-        for k in ("num_heads", "num_kv_heads", "head_dim", "block_size", "rel_extent", "window_size",
-                  "causal"):
-            setattr(sub, k, getattr(wc, k))
-        sub.q_lens, sub.k_lens = [wc.q_lens[b]], [wc.k_lens[b]]
-        done_bytes += metrics.work(sub)["bytes"]
-        nreq += 1
-        if spent >= budget_s:
-            break
+    while spent < budget_s:
+        for b in range(wc.batch):
+            toks = list(range(cu[b], cu[b + 1]))
+            t0 = time.perf_counter()
+            orc.attention(wc.q, wc.key_cache, wc.value_cache, wc.block_table, wc.cache_seqlens,
+                          wc.cu_seqlens_q, wc.softmax_scale, wc.causal, wc.window_size, wc.rel_extent,
+                          wc.rel_logits, tokens=toks)
+            spent += time.perf_counter() - t0
+            sub = type("W", (), {})()
+            for k in ("num_heads", "num_kv_heads", "head_dim", "block_size", "rel_extent", "window_size",
+                      "causal"):
+                setattr(sub, k, getattr(wc, k))
+            sub.q_lens, sub.k_lens = [wc.q_lens[b]], [wc.k_lens[b]]
+            done_bytes += metrics.work(sub)["bytes"]
+            nreq += 1
+            if spent >= budget_s:
+                break
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": torch.get_num_threads(),
             "kind": "oracle",
-            "sample": f"{nreq} of {wc.batch} requests of the batched decode batch (all 32 heads), "
-                      f"{spent:.1f} s of fp64 CPU work"}
+            "sample": f"{nreq} request evaluations ({nreq / wc.batch:.1f} passes over the {wc.batch} requests) "
+                      f"of the batched decode batch, all {wc.num_heads} heads, {spent:.1f} s of fp64 CPU work"}
 
 
 def main(argv=None):
