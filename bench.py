@@ -111,6 +111,37 @@ class Runner:
         self.bnd.rpa_split_combine(self._po, self._pl, out=self.out, lse=self.lse)
 
 
+class Fp8Runner(Runner):
+    """Times rpa_attn_varlen_fp8 on a workload whose K/V are held as E4M3
+    codes of the bf16 caches divided by the scales (the codes a
+    quantise-at-store write of the same rows would hold)."""
+
+    K_SCALE, V_SCALE = 1.0 / 32, 1.0 / 16
+
+    def __init__(self, w, num_splits, pools=1):
+        import torch
+        super().__init__(w, num_splits, pools=1)
+        kv = []
+        for i in range(pools):
+            k = w.key_cache if i == 0 else w.key_cache.clone()
+            v = w.value_cache if i == 0 else w.value_cache.clone()
+            kv.append(((k.float() / self.K_SCALE).to(torch.float8_e4m3fn).view(torch.uint8),
+                       (v.float() / self.V_SCALE).to(torch.float8_e4m3fn).view(torch.uint8)))
+            del k, v
+        self.kv = kv
+        torch.cuda.empty_cache()
+
+    def call(self, i=0):
+        w = self.w
+        k, v = self.kv[i % len(self.kv)]
+        self.bnd.rpa_attn_varlen_fp8(
+            w.q, k, v, k_scale=self.K_SCALE, v_scale=self.V_SCALE, block_table=w.block_table,
+            cache_seqlens=w.cache_seqlens, cu_seqlens_q=w.cu_seqlens_q, max_seqlen_q=w.max_seqlen_q,
+            softmax_scale=w.softmax_scale, causal=w.causal, window_size=w.window_size,
+            rel_extent=w.rel_extent, rel_logits=w.rel_logits, num_splits=self.S, out=self.out, lse=self.lse,
+            workspace=self.ws)
+
+
 def settle(fn, seconds):
     """Untimed calls for about `seconds` of wall time (clock ramp-up)."""
     import torch
@@ -133,8 +164,40 @@ def measure(runner, steps, warmup, settle_s=0.0):
     ms_comb = 0.0
     if runner.S > 1:
         ms_comb = time_calls(runner.combine_only, steps, warmup, stream)
-    wk = metrics.work(runner.w)
+    wk = metrics.work(runner.w, kv_elem_bytes=1 if isinstance(runner, Fp8Runner) else 2)
     return ms, ms_comb, wk
+
+
+def measure_graph(runner, steps, warmup):
+    """The same step captured once per KV pool in a HIP graph and replayed:
+    device time per step (back-to-back replays) and host latency of one
+    step (launch or replay, then synchronize), median of 50, against the
+    eager call's."""
+    import statistics
+    import torch
+    graphs = []
+    for i in range(len(runner.kv)):
+        runner.call(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            runner.call(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ms = time_calls(lambda i: graphs[i % len(graphs)].replay(), steps, warmup, stream)
+    lat_e, lat_g = [], []
+    for i in range(50):
+        t0 = time.perf_counter()
+        runner.call(i)
+        torch.cuda.synchronize()
+        lat_e.append(time.perf_counter() - t0)
+        t0 = time.perf_counter()
+        graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        lat_g.append(time.perf_counter() - t0)
+    del graphs
+    return ms, statistics.median(lat_e) * 1e6, statistics.median(lat_g) * 1e6
 
 
 def measure_kv_write(steps, warmup):
@@ -208,7 +271,8 @@ def main(argv=None):
     ap.add_argument("--no-extra", action="store_true", help="only the headline decode batch")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None, help="run one workload: batched_decode, chunked_prefill, "
-                                                  "long_decode, continuous_batch, kv_write")
+                                                  "long_decode, continuous_batch, batched_decode_fp8, "
+                                                  "long_decode_fp8, kv_write")
     ap.add_argument("--splits", type=int, default=None,
                     help="override the planner's num_splits (0 = balanced decode) for the headline decode batch "
                          "(or for long_decode with --only long_decode)")
@@ -240,6 +304,7 @@ def main(argv=None):
     dev = "cuda"
     results = {}
     kv_summary = None
+    graph_summary = None
 
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
@@ -256,6 +321,19 @@ def main(argv=None):
         results["batched_decode"] = (w, S, ms, ms_c, wk)
         log(f"batched_decode S={S}: {ms * 1e3:.1f} us/step (combine {ms_c * 1e3:.1f} us), "
             f"{wk['bytes'] / ms / 1e6:.1f} GB/s")
+        if not a.no_extra and a.only is None:
+            try:
+                gms, lat_e, lat_g = measure_graph(r, a.steps, a.warmup)
+                graph_summary = {"workload": "batched_decode, one HIP graph per KV pool",
+                                 "ms_per_step": round(gms, 5), "eager_ms_per_step": round(ms, 5),
+                                 "host_latency_us_eager": round(lat_e, 1),
+                                 "host_latency_us_graph": round(lat_g, 1)}
+                log(f"batched_decode graph replay: {gms * 1e3:.1f} us/step; one-step latency "
+                    f"eager {lat_e:.1f} us, graph {lat_g:.1f} us")
+            except Exception as e:  # reported in the line; never hides the headline
+                log(f"graph replay failed: {e!r}")
+                graph_summary = {"workload": "batched_decode graph", "error": repr(e)}
+        del r
     if not a.no_extra or a.only:
         if a.only in (None, "chunked_prefill"):
             w3 = wl.chunked_prefill(device="cpu").to(dev)
@@ -284,6 +362,24 @@ def main(argv=None):
                 f"{wk['flops'] / ms / 1e9:.1f} TFLOP/s")
             del r5, w5
             torch.cuda.empty_cache()
+        if a.only in (None, "batched_decode_fp8"):
+            w6 = wl.batched_decode(device="cpu").to(dev)
+            r6 = Fp8Runner(w6, 0, pools=3)
+            ms, ms_c, wk = measure(r6, a.steps, a.warmup, SETTLE_S)
+            results["batched_decode_fp8"] = (w6, 0, ms, ms_c, wk)
+            log(f"batched_decode_fp8: {ms * 1e3:.1f} us/step, {wk['bytes'] / ms / 1e6:.1f} GB/s")
+            del r6, w6
+            torch.cuda.empty_cache()
+        if a.only in (None, "long_decode_fp8"):
+            w7 = wl.long_decode(device=dev)
+            r7 = Fp8Runner(w7, 0)
+            w7.key_cache = w7.value_cache = None  # the bf16 caches are not needed any more
+            torch.cuda.empty_cache()
+            ms, ms_c, wk = measure(r7, max(5, a.steps // 2), a.warmup, SETTLE_S)
+            results["long_decode_fp8"] = (w7, 0, ms, ms_c, wk)
+            log(f"long_decode_fp8: {ms * 1e3:.1f} us/step, {wk['bytes'] / ms / 1e6:.1f} GB/s")
+            del r7, w7
+            torch.cuda.empty_cache()
         if a.only in (None, "kv_write"):
             try:
                 ms_kv, kvinfo = measure_kv_write(max(5, a.steps // 2), a.warmup)
@@ -297,7 +393,11 @@ def main(argv=None):
 
     def summary(name):
         w, S, ms, ms_c, wk = results[name]
-        return {"workload": name, "batch": w.batch, "num_tokens": w.num_tokens, "num_heads": w.num_heads,
+        extra = {}
+        if name.endswith("_fp8"):
+            extra = {"kv_cache": "e4m3", "k_scale": Fp8Runner.K_SCALE, "v_scale": Fp8Runner.V_SCALE,
+                     "kernel": "decode_heads_kernel<128, true, true> + combine_heads_kernel<128>"}
+        return {**extra, "workload": name, "batch": w.batch, "num_tokens": w.num_tokens, "num_heads": w.num_heads,
                 "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                 "rel_extent": w.rel_extent, "window": list(w.window_size), "num_splits": S,
                 "ms_per_step": round(ms, 5), "combine_ms": round(ms_c, 5),
@@ -327,7 +427,9 @@ def main(argv=None):
         # Balanced decode: the attention kernel and the combine of the
         # requests cut between workgroups; kernel_ms is the whole step (both
         # kernels).  Eight kv heads take the form with one kv head per wave.
-        if w.num_kv_heads == 8:
+        if head.endswith("_fp8"):
+            roof["kernel"] = "decode_heads_kernel<128, e4m3> + combine_heads_kernel<128>"
+        elif w.num_kv_heads == 8:
             roof["kernel"] = "decode_heads_kernel<128> + combine_heads_kernel<128>"
         else:
             roof["kernel"] = "decode_balanced_kernel<128> + combine_balanced_kernel<128>"
@@ -347,6 +449,8 @@ def main(argv=None):
             line[name] = summary(name)
     if kv_summary is not None:
         line["kv_write"] = kv_summary
+    if graph_summary is not None:
+        line["batched_decode_graph"] = graph_summary
     if not a.no_cpu and head == "batched_decode":
         log("timing the CPU oracle on a sample ...")
         line["cpu_baseline"] = cpu_baseline(w)

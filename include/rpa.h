@@ -45,7 +45,7 @@ typedef enum {
   RPA_OK = 0,
   RPA_ERR_NULL = -1,        /* a required pointer is NULL                         */
   RPA_ERR_SHAPE = -2,       /* inconsistent or negative sizes                     */
-  RPA_ERR_UNSUPPORTED = -3, /* head_dim not 64/128, block_size not a multiple of 16 */
+  RPA_ERR_UNSUPPORTED = -3, /* head_dim not 64/128, block_size not a multiple of 16, FP8 call outside its path */
   RPA_ERR_WORKSPACE = -4,   /* num_splits != 1 and the workspace is missing/small */
   RPA_ERR_HIP = -5          /* a HIP launch failed                                */
 } rpa_status;
@@ -200,6 +200,58 @@ int rpa_slot_mapping(const int32_t *block_table, int32_t max_pages_per_seq, cons
 int rpa_kv_cache_write(const void *key, const void *value, const int64_t *slot_mapping, int32_t num_tokens,
                        int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
                        void *key_cache, void *value_cache, void *stream);
+
+/*
+ * FP8 KV cache.  "paged_attention_v2_pytorch.py — BI-V100 PagedAttention V2"
+ * (dev.modelhub.org.cn) takes kv_cache_dtype, k_scale and v_scale and turns
+ * the gathered cache rows into floats times their scale before the scores;
+ * the TurboQuant chapter of "vLLM V1 Attention — Part 2" stores K/V as FP8
+ * with a scale factor, quantised when written and dequantised when read.
+ * Here the cache holds OCP E4M3 codes (uint8: 4 exponent bits with bias 7,
+ * 3 mantissa bits, largest finite 448, S.1111.111 = NaN) with one k_scale
+ * and one v_scale per cache (finite, > 0): code c stands for
+ * e4m3(c) * scale.
+ */
+
+/*
+ * rpa_attn_varlen_fp8: rpa_attn_varlen over E4M3 caches.  The result is the
+ * definition above with k = e4m3(key code) * k_scale and
+ * v = e4m3(value code) * v_scale: k_scale multiplies <q, k> only (the bias is
+ * not scaled), v_scale the output only (not the LSE).
+ *
+ *   key_cache,
+ *   value_cache   uint8 E4M3 codes [num_blocks, block_size, num_kv_heads, head_dim].
+ *   k_scale,
+ *   v_scale       finite and > 0, else RPA_ERR_SHAPE.
+ * Every other argument is that of rpa_attn_varlen.  Supported: the balanced
+ * decode (num_splits = 0 on a batch where it applies, see above) with
+ * num_kv_heads = 8; any other call returns RPA_ERR_UNSUPPORTED before
+ * anything is enqueued.
+ */
+int rpa_attn_varlen_fp8(const void *q, const void *key_cache, const void *value_cache, float k_scale,
+                        float v_scale, const int32_t *block_table, int32_t max_pages_per_seq,
+                        const int32_t *cache_seqlens, const int32_t *cu_seqlens_q,
+                        int32_t batch, int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                        int32_t max_seqlen_q, float softmax_scale, int causal,
+                        int32_t window_left, int32_t window_right,
+                        int32_t rel_extent, const float *rel_logits,
+                        int32_t num_splits, void *workspace, size_t workspace_bytes,
+                        void *out, float *lse, void *stream);
+
+/*
+ * rpa_kv_cache_write_fp8: rpa_kv_cache_write into E4M3 caches.  Element x of
+ * a key row is stored as the code of y = x / k_scale (one IEEE fp32
+ * division): the nearest E4M3 value, ties to the even code; |y| >= 448
+ * (infinity included) stores +-448; NaN stores a NaN code with x's sign.
+ * Values use v_scale alike.  Slots, skipping and alignment are those of
+ * rpa_kv_cache_write; the caches are uint8 [num_blocks, block_size,
+ * num_kv_heads, head_dim], 8-byte aligned.  k_scale and v_scale must be
+ * finite and > 0, else RPA_ERR_SHAPE.
+ */
+int rpa_kv_cache_write_fp8(const void *key, const void *value, const int64_t *slot_mapping, int32_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                           float k_scale, float v_scale, void *key_cache, void *value_cache, void *stream);
 
 /* rpa_status_string: static text for a status code (never NULL). */
 const char *rpa_status_string(int status);

@@ -62,6 +62,11 @@ def lib():
     L.rpa_slot_mapping.restype = ctypes.c_int
     L.rpa_kv_cache_write.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     L.rpa_kv_cache_write.restype = ctypes.c_int
+    L.rpa_attn_varlen_fp8.argtypes = [vp, vp, vp, f32, f32, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                      i32, f32, ctypes.c_int, i32, i32, i32, vp, i32, vp, sz, vp, vp, vp]
+    L.rpa_attn_varlen_fp8.restype = ctypes.c_int
+    L.rpa_kv_cache_write_fp8.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, vp, vp, vp]
+    L.rpa_kv_cache_write_fp8.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -167,6 +172,98 @@ def rpa_attn_varlen(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
     if st != RPA_OK:
         raise RpaError(st, "rpa_attn_varlen")
     return (out, lse) if want_lse else out
+
+
+def _fp8_cache(t: torch.Tensor, name: str, device) -> torch.Tensor:
+    """An E4M3 cache given as uint8 codes or torch.float8_e4m3fn, seen as uint8."""
+    if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    _check(t, name, torch.uint8, device, 4)
+    return t
+
+
+def rpa_attn_varlen_fp8(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor, *,
+                        k_scale: float, v_scale: float, block_table: torch.Tensor, cache_seqlens: torch.Tensor,
+                        cu_seqlens_q: torch.Tensor, max_seqlen_q: int, softmax_scale: float,
+                        causal: bool = True, window_size: Tuple[int, int] = (-1, -1),
+                        rel_extent: int = 0, rel_logits: Optional[torch.Tensor] = None,
+                        num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, return_lse: bool = False,
+                        workspace: Optional[torch.Tensor] = None):
+    """rpa_attn_varlen over E4M3 caches (uint8 codes or float8_e4m3fn) with
+    per-cache scales: k = e4m3(code) * k_scale, v = e4m3(code) * v_scale."""
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    _check(q, "q", torch.bfloat16, dev, 3)
+    key_cache = _fp8_cache(key_cache, "key_cache", dev)
+    value_cache = _fp8_cache(value_cache, "value_cache", dev)
+    if key_cache.shape != value_cache.shape:
+        raise ValueError("key_cache and value_cache shapes differ")
+    _check(block_table, "block_table", torch.int32, dev, 2)
+    _check(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
+    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, 1)
+    T, H, D = q.shape
+    NB, BS, Hkv, Dk = key_cache.shape
+    if Dk != D:
+        raise ValueError("head_dim of q and the caches differ")
+    B = cache_seqlens.shape[0]
+    if cu_seqlens_q.shape[0] != B + 1 or block_table.shape[0] != B:
+        raise ValueError("batch sizes of cu_seqlens_q / block_table / cache_seqlens disagree")
+    R = int(rel_extent)
+    if R > 0:
+        if rel_logits is None:
+            raise ValueError("rel_extent > 0 needs rel_logits")
+        rel_logits = rel_logits.contiguous()
+        _check(rel_logits, "rel_logits", torch.float32, dev, 3)
+        if tuple(rel_logits.shape) != (T, H, R):
+            raise ValueError(f"rel_logits must be {(T, H, R)}, got {tuple(rel_logits.shape)}")
+    S = int(num_splits)
+    if out is None:
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, dev, 3)
+    want_lse = return_lse or lse is not None
+    if want_lse and lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, dev, 2)
+    ws_bytes = rpa_workspace_bytes(S, T, H, D) if S != 1 else 0
+    if ws_bytes and workspace is None:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    st = lib().rpa_attn_varlen_fp8(
+        _ptr(q), _ptr(key_cache), _ptr(value_cache), float(k_scale), float(v_scale), _ptr(block_table),
+        block_table.shape[1], _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB, BS,
+        int(max_seqlen_q), float(softmax_scale), int(bool(causal)), int(window_size[0]), int(window_size[1]),
+        R, _ptr(rel_logits) if R > 0 else None, S, _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _ptr(out), _ptr(lse), _stream(dev))
+    if st != RPA_OK:
+        raise RpaError(st, "rpa_attn_varlen_fp8")
+    return (out, lse) if want_lse else out
+
+
+def rpa_kv_cache_write_fp8(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,
+                           key_cache: torch.Tensor, value_cache: torch.Tensor, k_scale: float,
+                           v_scale: float) -> None:
+    """Quantise key/value [T, Hkv, D] (bf16) to E4M3 with k_scale / v_scale
+    and write the codes into the paged caches at their slots."""
+    dev = key.device
+    _check(key, "key", torch.bfloat16, dev, 3)
+    _check(value, "value", torch.bfloat16, dev, 3)
+    _check(slot_mapping, "slot_mapping", torch.int64, dev, 1)
+    key_cache = _fp8_cache(key_cache, "key_cache", dev)
+    value_cache = _fp8_cache(value_cache, "value_cache", dev)
+    T, Hkv, D = key.shape
+    NB, BS = key_cache.shape[0], key_cache.shape[1]
+    if tuple(value.shape) != (T, Hkv, D) or slot_mapping.shape[0] != T:
+        raise ValueError("key / value / slot_mapping shapes disagree")
+    if tuple(key_cache.shape) != (NB, BS, Hkv, D) or tuple(value_cache.shape) != (NB, BS, Hkv, D):
+        raise ValueError("cache shapes disagree with key")
+    st = lib().rpa_kv_cache_write_fp8(_ptr(key), _ptr(value), _ptr(slot_mapping), T, Hkv, D, NB, BS,
+                                      float(k_scale), float(v_scale), _ptr(key_cache), _ptr(value_cache),
+                                      _stream(dev))
+    if st != RPA_OK:
+        raise RpaError(st, "rpa_kv_cache_write_fp8")
 
 
 def rpa_split_combine(partial_out: torch.Tensor, partial_lse: torch.Tensor,

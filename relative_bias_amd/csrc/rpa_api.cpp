@@ -28,7 +28,7 @@ const char *rpa_status_string(int status) {
     case RPA_OK: return "ok";
     case RPA_ERR_NULL: return "a required pointer is NULL";
     case RPA_ERR_SHAPE: return "inconsistent or out-of-range sizes";
-    case RPA_ERR_UNSUPPORTED: return "unsupported head_dim or block_size";
+    case RPA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size or FP8-cache configuration";
     case RPA_ERR_WORKSPACE: return "workspace missing or too small for num_splits";
     case RPA_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";
@@ -92,14 +92,20 @@ int rpa_split_combine(const float *partial_out, const float *partial_lse, int32_
   return RPA_OK;
 }
 
-int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cache,
-                    const int32_t *block_table, int32_t max_pages_per_seq,
-                    const int32_t *cache_seqlens, const int32_t *cu_seqlens_q, int32_t batch,
-                    int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                    int32_t num_blocks, int32_t block_size, int32_t max_seqlen_q, float softmax_scale,
-                    int causal, int32_t window_left, int32_t window_right, int32_t rel_extent,
-                    const float *rel_logits, int32_t num_splits, void *workspace,
-                    size_t workspace_bytes, void *out, float *lse, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Both attention entry points: kv8 selects E4M3 caches with their scales.
+int attn_impl(const void *q, const void *key_cache, const void *value_cache, bool kv8, float k_scale,
+              float v_scale, const int32_t *block_table, int32_t max_pages_per_seq,
+              const int32_t *cache_seqlens, const int32_t *cu_seqlens_q, int32_t batch, int32_t num_tokens,
+              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+              int32_t max_seqlen_q, float softmax_scale, int causal, int32_t window_left, int32_t window_right,
+              int32_t rel_extent, const float *rel_logits, int32_t num_splits, void *workspace,
+              size_t workspace_bytes, void *out, float *lse, void *stream) {
+  if (kv8 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return RPA_ERR_SHAPE;
   // Sizes.
   if (batch < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       num_blocks < 0 || block_size <= 0 || max_pages_per_seq < 0 || max_seqlen_q < 0 ||
@@ -134,6 +140,8 @@ int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cach
   const bool balanced = num_splits == 0 && decode_only && batch <= rpa::kBalMaxBatch &&
                         (int64_t)num_tokens * num_heads * rel_extent * 4 < ((int64_t)1 << 31);
   if (num_splits == 0 && !balanced) num_splits = 1;
+  // E4M3 caches: the balanced decode with eight kv heads.
+  if (kv8 && !(balanced && num_kv_heads == rpa::kBalHeads)) return RPA_ERR_UNSUPPORTED;
   if (n_items_ub * num_kv_heads * (int64_t)num_splits > INT32_MAX) return RPA_ERR_SHAPE;
   int32_t bal_wgs = 0;
   if (balanced) {
@@ -183,8 +191,13 @@ int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cach
   p.bs_shift = -1;
   for (int sh = 4; sh < 31; ++sh)
     if ((1 << sh) == block_size) p.bs_shift = sh;
-  p.scale = softmax_scale;
-  p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  // An E4M3 cache's k_scale multiplies <q, k> alone, so it joins the softmax
+  // scale; v_scale multiplies the normalised output.
+  const double qk_scale = (double)softmax_scale * (kv8 ? (double)k_scale : 1.0);
+  p.scale = (float)qk_scale;
+  p.scale_log2 = (float)(qk_scale * 1.4426950408889634);
+  p.v_scale = kv8 ? v_scale : 1.f;
+  p.kv8 = kv8 ? 1 : 0;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (balanced) return rpa::launch_balanced_decode(p, head_dim, st) == hipSuccess ? RPA_OK : RPA_ERR_HIP;
@@ -201,6 +214,38 @@ int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cach
     if (rpa::launch_combine(c, st) != hipSuccess) return RPA_ERR_HIP;
   }
   return RPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cache,
+                    const int32_t *block_table, int32_t max_pages_per_seq,
+                    const int32_t *cache_seqlens, const int32_t *cu_seqlens_q, int32_t batch,
+                    int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t num_blocks, int32_t block_size, int32_t max_seqlen_q, float softmax_scale,
+                    int causal, int32_t window_left, int32_t window_right, int32_t rel_extent,
+                    const float *rel_logits, int32_t num_splits, void *workspace,
+                    size_t workspace_bytes, void *out, float *lse, void *stream) {
+  return attn_impl(q, key_cache, value_cache, false, 1.f, 1.f, block_table, max_pages_per_seq, cache_seqlens,
+                   cu_seqlens_q, batch, num_tokens, num_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                   max_seqlen_q, softmax_scale, causal, window_left, window_right, rel_extent, rel_logits,
+                   num_splits, workspace, workspace_bytes, out, lse, stream);
+}
+
+int rpa_attn_varlen_fp8(const void *q, const void *key_cache, const void *value_cache, float k_scale,
+                        float v_scale, const int32_t *block_table, int32_t max_pages_per_seq,
+                        const int32_t *cache_seqlens, const int32_t *cu_seqlens_q, int32_t batch,
+                        int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t num_blocks, int32_t block_size, int32_t max_seqlen_q, float softmax_scale,
+                        int causal, int32_t window_left, int32_t window_right, int32_t rel_extent,
+                        const float *rel_logits, int32_t num_splits, void *workspace,
+                        size_t workspace_bytes, void *out, float *lse, void *stream) {
+  return attn_impl(q, key_cache, value_cache, true, k_scale, v_scale, block_table, max_pages_per_seq,
+                   cache_seqlens, cu_seqlens_q, batch, num_tokens, num_heads, num_kv_heads, head_dim, num_blocks,
+                   block_size, max_seqlen_q, softmax_scale, causal, window_left, window_right, rel_extent,
+                   rel_logits, num_splits, workspace, workspace_bytes, out, lse, stream);
 }
 
 int rpa_slot_mapping(const int32_t *block_table, int32_t max_pages_per_seq, const int32_t *cache_seqlens,
@@ -236,12 +281,40 @@ int rpa_kv_cache_write(const void *key, const void *value, const int64_t *slot_m
   p.key = static_cast<const uint16_t *>(key);
   p.value = static_cast<const uint16_t *>(value);
   p.slots = slot_mapping;
-  p.key_cache = static_cast<uint16_t *>(key_cache);
-  p.value_cache = static_cast<uint16_t *>(value_cache);
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
   p.capacity = (int64_t)num_blocks * block_size;
   p.num_tokens = num_tokens;
   p.row_units = (int32_t)(row / 8);
+  p.k_scale = 1.f;
+  p.v_scale = 1.f;
   return rpa::launch_kv_write(p, static_cast<hipStream_t>(stream)) == hipSuccess ? RPA_OK : RPA_ERR_HIP;
+}
+
+int rpa_kv_cache_write_fp8(const void *key, const void *value, const int64_t *slot_mapping, int32_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                           float k_scale, float v_scale, void *key_cache, void *value_cache, void *stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks < 0 || block_size <= 0)
+    return RPA_ERR_SHAPE;
+  if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return RPA_ERR_SHAPE;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (row % 8 != 0) return RPA_ERR_UNSUPPORTED;
+  if (row / 8 > INT32_MAX) return RPA_ERR_SHAPE;
+  if (num_tokens == 0) return RPA_OK;
+  if (!key || !value || !slot_mapping || !key_cache || !value_cache) return RPA_ERR_NULL;
+  rpa::KvWriteParams p;
+  p.key = static_cast<const uint16_t *>(key);
+  p.value = static_cast<const uint16_t *>(value);
+  p.slots = slot_mapping;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.capacity = (int64_t)num_blocks * block_size;
+  p.num_tokens = num_tokens;
+  p.row_units = (int32_t)(row / 8);
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  return rpa::launch_kv_write_fp8(p, static_cast<hipStream_t>(stream)) == hipSuccess ? RPA_OK : RPA_ERR_HIP;
 }
 
 }  // extern "C"

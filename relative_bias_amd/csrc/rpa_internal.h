@@ -47,8 +47,10 @@ struct AttnParams {
   float *bal_part;              // balanced decode: partial slots
   int32_t *bal_desc;            // balanced decode: per-workgroup combine records
   int32_t bal_wgs;              // balanced decode: workgroups
-  float scale;                  // softmax_scale
-  float scale_log2;             // softmax_scale * log2(e)
+  float scale;                  // softmax_scale (times k_scale for E4M3 caches)
+  float scale_log2;             // scale * log2(e)
+  float v_scale;                // E4M3 caches: the value cache's scale (1 for bf16 caches)
+  int32_t kv8;                  // 1: k / v are E4M3 codes (uint8) instead of bf16
 };
 
 struct CombineParams {
@@ -71,10 +73,11 @@ struct KvWriteParams {
   const uint16_t *key;          // bf16 [T, Hkv, D]
   const uint16_t *value;        // bf16 [T, Hkv, D]
   const int64_t *slots;         // [T]
-  uint16_t *key_cache;          // bf16 [NB, BS, Hkv, D]
-  uint16_t *value_cache;        // bf16 [NB, BS, Hkv, D]
+  void *key_cache;              // bf16 (or E4M3 codes) [NB, BS, Hkv, D]
+  void *value_cache;            // bf16 (or E4M3 codes) [NB, BS, Hkv, D]
   int64_t capacity;             // NB * BS slots
-  int32_t num_tokens, row_units;  // row_units: 16-byte units per token row (Hkv * D / 8)
+  int32_t num_tokens, row_units;  // row_units: 16-byte bf16 units per token row (Hkv * D / 8)
+  float k_scale, v_scale;       // E4M3 caches: quantisation scales
 };
 
 // Number of work items a request with lq query tokens contributes.
@@ -91,6 +94,7 @@ hipError_t launch_attention(const AttnParams &p, int head_dim, int64_t n_items_u
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
 hipError_t launch_slot_mapping(const SlotParams &p, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteParams &p, hipStream_t stream);
+hipError_t launch_kv_write_fp8(const KvWriteParams &p, hipStream_t stream);
 // Balanced decode: the attention kernel on p.bal_wgs workgroups, then the
 // combine of the pairs cut between workgroups.
 hipError_t launch_balanced_decode(const AttnParams &p, int head_dim, hipStream_t stream);

@@ -32,6 +32,8 @@
 // exceeds it by more than kTau (log2 units), so the O rescale is skipped on
 // most tiles; exp2 arguments then stay <= kTau, and the final normalisation
 // uses the same running max, so the result is unchanged.
+#include <type_traits>
+
 #include "rpa_internal.h"
 
 namespace rpa {
@@ -1468,6 +1470,51 @@ __device__ __forceinline__ u32x2 lds_read_tr_at(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr) : "memory");
   return v;
 }
+__device__ __forceinline__ u32x2 lds_read_b64_asm(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait_n(u32x2 (&r)[2]) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r[0]), "+v"(r[1]) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait_n(u32x4 (&r)[1]) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r[0]) : "n"(N));
+}
+// Two or four 16-byte LDS writes, complete when the asm ends.
+__device__ __forceinline__ void lds_write_b128x2_now(uint32_t a0, uint32_t a1, u32x4 v0, u32x4 v1) {
+  asm volatile("ds_write_b128 %0, %2\n\tds_write_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               :
+               : "v"(a0), "v"(a1), "v"(v0), "v"(v1)
+               : "memory");
+}
+__device__ __forceinline__ void lds_write_b128x4_now(const uint32_t (&a)[4], const u32x4 (&v)[4]) {
+  asm volatile(
+      "ds_write_b128 %0, %4\n\tds_write_b128 %1, %5\n\tds_write_b128 %2, %6\n\tds_write_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      :
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3])
+      : "memory");
+}
+
+// E4M3 (OCP) codes to bf16: v_cvt_pk_f32_fp8 decodes two codes exactly to
+// fp32 (every E4M3 value has at most four significant bits, so its upper
+// 16 bits are its bf16 form); v_perm packs those halves.  Four codes of one
+// dword become two dwords of bf16 pairs in element order.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t x) {
+  typedef float f32x2_ __attribute__((ext_vector_type(2)));
+  const f32x2_ a = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, false);
+  const f32x2_ b = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, true);
+  return u32x2{__builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u),
+               __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u)};
+}
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t x0, uint32_t x1) {
+  const u32x2 lo = e4m3x4_to_bf16(x0), hi = e4m3x4_to_bf16(x1);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 __device__ __forceinline__ f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
                                                    0, 0, 0);
@@ -2038,13 +2085,20 @@ __global__ __launch_bounds__(kThreads) void combine_balanced_kernel(AttnParams p
 // for combine_heads_kernel.  Per unit and wave the loads, LDS layout and
 // arithmetic are those of decode_balanced.
 
-template <int D, bool BIAS>
+template <int D, bool BIAS, bool KV8>
 __device__ void decode_heads(const AttnParams &p, char *smem) {
   using L = BalLds<D>;
   constexpr int QK = D / 32, DB = D / 16, NI = L::NI, RPI = L::RPI, UNITS = L::UNITS, ROWB = L::ROWB;
   static_assert(L::NST == 2, "two stages per wave: one computed, one in flight");
   static_assert(kBalWaves == kBalHeads, "one wave per kv head");
-  constexpr int NPER = 2 * NI + (BIAS ? 4 : 0);  // vector-memory instructions per unit
+  // E4M3 caches: a stage is the unit's raw rows (K then V, D bytes a row);
+  // K operands are decoded from it, V is decoded into one bf16 V stage per
+  // wave that the transposing reads use.
+  constexpr int U8 = D / 16, RPI8 = 64 / U8, NI8 = 16 / RPI8;
+  constexpr uint32_t LAND = 32 * D;
+  static_assert(!KV8 || 2 * LAND + L::halfBytes <= 2 * L::stageBytes, "fp8 stages fit the wave's region");
+  constexpr int NLD = KV8 ? NI8 : NI;
+  constexpr int NPER = 2 * NLD + (BIAS ? 4 : 0);  // vector-memory instructions per unit
   constexpr int SLOT = kDecCols * (D + 1);
   int32_t *prefix = reinterpret_cast<int32_t *>(smem + L::prefixOff);
   bal_prefix(p, prefix, reinterpret_cast<int32_t *>(smem + L::mlOff), 1);
@@ -2068,17 +2122,40 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
     b_it = __builtin_amdgcn_readfirstlane(lo);
   }
 
-  const uint32_t slot_bytes = (uint32_t)kBalHeads * D * 2;
-  uint32_t gk[NI], gv[NI];
+  const uint32_t slot_bytes = (uint32_t)kBalHeads * D * (KV8 ? 1 : 2);
+  uint32_t gk[NLD], gv[NLD];
 #pragma unroll
-  for (int n = 0; n < NI; ++n) {
-    const int r = RPI * n + lane / UNITS, pu = lane % UNITS;
-    gk[n] = r * slot_bytes + ((pu ^ swz_k<D>(r)) << 4);
-    gv[n] = r * slot_bytes + ((pu ^ swz_vt<D>(r)) << 4);
+  for (int n = 0; n < NLD; ++n) {
+    if constexpr (KV8) {
+      // Raw K rows: piece pu of row r lands at (pu ^ (r % U8)) so that the
+      // 16 rows of an operand read spread over the banks.
+      const int r = RPI8 * n + lane / U8, pu = lane % U8;
+      gk[n] = r * slot_bytes + ((pu ^ (r & (U8 - 1))) << 4);
+      gv[n] = r * slot_bytes + (pu << 4);
+    } else {
+      const int r = RPI * n + lane / UNITS, pu = lane % UNITS;
+      gk[n] = r * slot_bytes + ((pu ^ swz_k<D>(r)) << 4);
+      gv[n] = r * slot_bytes + ((pu ^ swz_vt<D>(r)) << 4);
+    }
   }
   uint32_t lk_off[QK], lv_off[DB];
 #pragma unroll
-  for (int ks = 0; ks < QK; ++ks) lk_off[ks] = c16 * ROWB + (((4 * ks + q) ^ swz_k<D>(c16)) << 4);
+  for (int ks = 0; ks < QK; ++ks) {
+    if constexpr (KV8)
+      lk_off[ks] = c16 * D + (((2 * ks + (q >> 1)) ^ (c16 & (U8 - 1))) << 4) + 8 * (q & 1);
+    else
+      lk_off[ks] = c16 * ROWB + (((4 * ks + q) ^ swz_k<D>(c16)) << 4);
+  }
+  // fp8: where this lane's decoded V pieces go in the bf16 V stage.
+  uint32_t v8_dst[KV8 ? 2 * NI8 : 1];
+  if constexpr (KV8) {
+#pragma unroll
+    for (int n = 0; n < NI8; ++n) {
+      const int r = RPI8 * n + lane / U8, pu = lane % U8;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) v8_dst[2 * n + e] = r * ROWB + (((2 * pu + e) ^ swz_vt<D>(r)) << 4);
+    }
+  }
   {
     const int i = (lane & 15) >> 2, t = lane & 3, row = 4 * q + i;
 #pragma unroll
@@ -2092,6 +2169,7 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
   const float c = p.scale_log2;
   const bool pos_scale = c > 0.f;
   const uint32_t bias_bytes = BIAS ? (uint32_t)p.num_tokens * (uint32_t)p.H * (uint32_t)p.R * 4u : 0u;
+  const float v_scale = KV8 ? p.v_scale : 1.f;
 
   // A piece: units [j0, j1) of request b inside this workgroup's range,
   // with what its rows need (uniform fields, then the lane's column).
@@ -2157,8 +2235,8 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
     const int nvalid = __builtin_amdgcn_readfirstlane(min(max(P.kend - key0, 0), 16));
     const int slot0 = p.bs_shift >= 0 ? (key0 & (p.BS - 1)) : key0 % p.BS;
     const int64_t eoff = (((int64_t)page * p.BS + slot0) * kBalHeads + g) * D;
-    const auto rk = make_rsrc(p.k + eoff, (uint32_t)nvalid * slot_bytes);
-    const auto rv = make_rsrc(p.v + eoff, (uint32_t)nvalid * slot_bytes);
+    const auto rk = make_rsrc(reinterpret_cast<const char *>(p.k) + eoff * (KV8 ? 1 : 2), (uint32_t)nvalid * slot_bytes);
+    const auto rv = make_rsrc(reinterpret_cast<const char *>(p.v) + eoff * (KV8 ? 1 : 2), (uint32_t)nvalid * slot_bytes);
     if constexpr (BIAS) {
       const auto brs = make_rsrc(p.rel_logits, in_band(P, key0) ? bias_bytes : 0u);
       char *bst = smem + L::biasOff + (w * 2 + slot) * 1024;
@@ -2169,29 +2247,58 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
                                                  (P.rel_base + (uint32_t)d) * 4u, 0, 0, 0);
       }
     }
-    char *st = smem + (w * 2 + slot) * L::stageBytes;
+    char *st = KV8 ? smem + w * 2 * L::stageBytes + slot * LAND : smem + (w * 2 + slot) * L::stageBytes;
+    constexpr int VHALF = KV8 ? 16 * D : L::halfBytes;
 #pragma unroll
-    for (int n = 0; n < NI; ++n)
+    for (int n = 0; n < NLD; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void *)(st + n * 1024), 16,
                                                gk[n], 0, 0, 0);
 #pragma unroll
-    for (int n = 0; n < NI; ++n)
+    for (int n = 0; n < NLD; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void *)(st + L::halfBytes + n * 1024), 16, gv[n], 0, 0, 0);
+          rv, (__attribute__((address_space(3))) void *)(st + VHALF + n * 1024), 16, gv[n], 0, 0, 0);
   };
 
   f32x4 oacc[DB];
   float m_run, l_run;
   auto compute = [&](const Piece &P, int k, int slot, const bf16x8 (&qf)[QK]) __attribute__((always_inline)) {
     const int key0 = __builtin_amdgcn_readfirstlane(key_of(P, k));
-    const uint32_t st = lds_wave + slot * L::stageBytes;
     u32x4 kf[QK];
-#pragma unroll
-    for (int ks = 0; ks < QK; ++ks) kf[ks] = lds_read_b128_asm(st + lk_off[ks]);
     u32x2 va[DB];
+    if constexpr (KV8) {
+      // Raw rows of the unit: K operands decoded in registers; this lane's
+      // V pieces decoded into the bf16 V stage, then read transposed.
+      const uint32_t land = lds_wave + slot * LAND;
+      const uint32_t vst = lds_wave + 2 * LAND;
+      u32x2 k8[QK];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) va[db] = lds_read_tr_at(st + lv_off[db]);
-    lgkm_wait_n<DB>(kf);
+      for (int ks = 0; ks < QK; ++ks) k8[ks] = lds_read_b64_asm(land + lk_off[ks]);
+      u32x4 v8[NI8];
+#pragma unroll
+      for (int n = 0; n < NI8; ++n) v8[n] = lds_read_b128_asm(land + 16 * D + n * 1024 + 16 * lane);
+      lgkm_wait_n<0>(v8);
+      lgkm_wait_n<0>(k8);
+      if constexpr (NI8 == 2) {
+        const uint32_t a[4] = {vst + v8_dst[0], vst + v8_dst[1], vst + v8_dst[2], vst + v8_dst[3]};
+        const u32x4 vv[4] = {e4m3x8_to_bf16(v8[0][0], v8[0][1]), e4m3x8_to_bf16(v8[0][2], v8[0][3]),
+                             e4m3x8_to_bf16(v8[1][0], v8[1][1]), e4m3x8_to_bf16(v8[1][2], v8[1][3])};
+        lds_write_b128x4_now(a, vv);
+      } else {
+        lds_write_b128x2_now(vst + v8_dst[0], vst + v8_dst[1], e4m3x8_to_bf16(v8[0][0], v8[0][1]),
+                             e4m3x8_to_bf16(v8[0][2], v8[0][3]));
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) va[db] = lds_read_tr_at(vst - L::halfBytes + lv_off[db]);
+#pragma unroll
+      for (int ks = 0; ks < QK; ++ks) kf[ks] = e4m3x8_to_bf16(k8[ks][0], k8[ks][1]);
+    } else {
+      const uint32_t st = lds_wave + slot * L::stageBytes;
+#pragma unroll
+      for (int ks = 0; ks < QK; ++ks) kf[ks] = lds_read_b128_asm(st + lk_off[ks]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) va[db] = lds_read_tr_at(st + lv_off[db]);
+      lgkm_wait_n<DB>(kf);
+    }
     f32x4 sacc = f32x4{};
 #pragma unroll
     for (int ks = 0; ks < QK; ++ks) sacc = mfma16(as_bf16x8(kf[ks]), qf[ks], sacc);
@@ -2247,7 +2354,7 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
   // the column's l is spread over its four q lanes.
   auto finish_piece = [&](const Piece &P) __attribute__((always_inline)) {
     const float l_col = xor32_sum(xor16_sum(l_run));
-    const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
+    const float inv = l_col > 0.f ? (KV8 ? v_scale / l_col : 1.f / l_col) : 0.f;
     const float lse_v = l_col > 0.f ? (m_run + log2_fast(l_col)) * kLn2 : neg_inf();
     if (c16 >= P.ncols) return;
     if (P.j0 == 0 && P.j1 == P.nu) {
@@ -2343,10 +2450,10 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
   }
 }
 
-template <int D, bool BIAS>
+template <int D, bool BIAS, bool KV8>
 __global__ __launch_bounds__(64 * kBalWaves, 1) void decode_heads_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char smem[BalLds<D>::bytes];
-  decode_heads<D, BIAS>(p, smem);
+  decode_heads<D, BIAS, KV8>(p, smem);
 }
 
 // Combine of the requests cut by decode_heads.  A task is (recording
@@ -2577,7 +2684,65 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(KvWriteParams p) {
   }
 }
 
+// E4M3 (OCP) code of an fp32 value: nearest value, ties to the even code;
+// magnitudes of 448 and above (infinity included) saturate to 448; NaN
+// gives a NaN code with the value's sign.  Normal results round the fp32
+// mantissa to 3 bits (the carry may raise the exponent); below 2^-6 the
+// code is |y| * 2^9 rounded to an integer (0..8, where 8 is 2^-6).
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;
+  if (a >= 0x43e00000u) return sign | 0x7eu;
+  if (a >= 0x3c800000u) {
+    const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+    return sign | ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));
+  }
+  return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+}
+
+// Eight bf16 values (one 16-byte unit) to eight E4M3 codes of x / scale.
+__device__ __forceinline__ u32x2 quant8_e4m3(u32x4 x, float scale) {
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[2 * i] = e4m3_code(__fdiv_rn(__uint_as_float(x[i] << 16), scale));
+    c[2 * i + 1] = e4m3_code(__fdiv_rn(__uint_as_float(x[i] & 0xffff0000u), scale));
+  }
+  return u32x2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+}
+
+// kv_write_kernel for E4M3 caches: each 16-byte unit of a bf16 row becomes
+// 8 bytes of codes at the same element offsets of the slot's row.
+__global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(KvWriteParams p) {
+  const int lane = threadIdx.x & 63;
+  const int nwave = gridDim.x * (kThreads / 64);
+  const int n = p.row_units;
+  for (int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); t < p.num_tokens; t += nwave) {
+    const int64_t slot = p.slots[t];
+    if (slot < 0 || slot >= p.capacity) continue;
+    const u32x4 *sk = reinterpret_cast<const u32x4 *>(p.key) + (int64_t)t * n;
+    const u32x4 *sv = reinterpret_cast<const u32x4 *>(p.value) + (int64_t)t * n;
+    u32x2 *dk = reinterpret_cast<u32x2 *>(p.key_cache) + slot * n;
+    u32x2 *dv = reinterpret_cast<u32x2 *>(p.value_cache) + slot * n;
+    for (int c = lane; c < n; c += 64) {
+      const u32x4 k0 = sk[c], v0 = sv[c];
+      dk[c] = quant8_e4m3(k0, p.k_scale);
+      dv[c] = quant8_e4m3(v0, p.v_scale);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_kv_write_fp8(const KvWriteParams &p, hipStream_t stream) {
+  if (p.num_tokens <= 0) return hipSuccess;
+  const int64_t wgs = ((int64_t)p.num_tokens + kThreads / 64 - 1) / (kThreads / 64);
+  const dim3 grid((unsigned)(wgs < 2048 ? wgs : 2048)), block(kThreads);
+  hipLaunchKernelGGL(kv_write_fp8_kernel, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_slot_mapping(const SlotParams &p, hipStream_t stream) {
   if (p.num_tokens <= 0) return hipSuccess;
@@ -2619,17 +2784,27 @@ hipError_t launch_balanced_decode(const AttnParams &p, int head_dim, hipStream_t
   const bool bias = p.R > 0;
   if (p.Hkv == kBalHeads) {
     const dim3 hgrid((unsigned)(p.bal_wgs * 2));
+    auto heads = [&](auto d_tag, auto b_tag, auto k_tag) {
+      hipLaunchKernelGGL((decode_heads_kernel<decltype(d_tag)::value, decltype(b_tag)::value,
+                                              decltype(k_tag)::value>),
+                         grid, block, 0, stream, p);
+    };
+    using D128 = std::integral_constant<int, 128>;
+    using D64 = std::integral_constant<int, 64>;
+    using T_ = std::true_type;
+    using F_ = std::false_type;
     if (head_dim == 128) {
-      if (bias) hipLaunchKernelGGL((decode_heads_kernel<128, true>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((decode_heads_kernel<128, false>), grid, block, 0, stream, p);
+      if (p.kv8) bias ? heads(D128{}, T_{}, T_{}) : heads(D128{}, F_{}, T_{});
+      else bias ? heads(D128{}, T_{}, F_{}) : heads(D128{}, F_{}, F_{});
       hipLaunchKernelGGL((combine_heads_kernel<128>), hgrid, cblock, 0, stream, p);
     } else {
-      if (bias) hipLaunchKernelGGL((decode_heads_kernel<64, true>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((decode_heads_kernel<64, false>), grid, block, 0, stream, p);
+      if (p.kv8) bias ? heads(D64{}, T_{}, T_{}) : heads(D64{}, F_{}, T_{});
+      else bias ? heads(D64{}, T_{}, F_{}) : heads(D64{}, F_{}, F_{});
       hipLaunchKernelGGL((combine_heads_kernel<64>), hgrid, cblock, 0, stream, p);
     }
     return hipGetLastError();
   }
+  if (p.kv8) return hipErrorNotSupported;  // E4M3 caches: eight kv heads only
   if (head_dim == 128) {
     if (bias) hipLaunchKernelGGL((decode_balanced_kernel<128, true>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((decode_balanced_kernel<128, false>), grid, block, 0, stream, p);

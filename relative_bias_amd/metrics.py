@@ -1,7 +1,8 @@
 """Algorithmic work of one attention call, from host-side lengths only.
 
 bytes = K and V of every key visible to at least one row of a request, read
-        once per kv head (2 * Hkv * D * 2 B per key)
+        once per kv head (2 * Hkv * D * kv_elem_bytes B per key: 2 for bf16
+        caches, 1 for E4M3 caches)
       + q and out (bf16), lse (fp32)
       + the rel_logits entries inside the bias band of visible keys (fp32)
       + one int32 block_table entry per page touched, and the length arrays.
@@ -24,7 +25,7 @@ def _row_bounds(qa: int, lk: int, causal: bool, left: int, right: int):
     return lo, hi
 
 
-def work(w) -> dict:
+def work(w, kv_elem_bytes: int = 2) -> dict:
     H, Hkv, D, BS, R = w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, w.rel_extent
     left, right = w.window_size
     kv_bytes = 0
@@ -48,7 +49,7 @@ def work(w) -> dict:
             umin = lo if umin is None else min(umin, lo)
             umax = hi if umax is None else max(umax, hi)
         if umin is not None:
-            kv_bytes += (umax - umin + 1) * Hkv * D * 2 * 2
+            kv_bytes += (umax - umin + 1) * Hkv * D * 2 * kv_elem_bytes
             page_bytes += (umax // BS - umin // BS + 1) * 4
     T = sum(w.q_lens)
     qo_bytes = 2 * T * H * D * 2

@@ -28,13 +28,14 @@ def L():
 def _declared():
     with open(HEADER) as f:
         src = f.read()
-    return sorted(set(re.findall(r"\b(rpa_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(rpa_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("rpa_attn_varlen", "rpa_split_combine", "rpa_choose_splits", "rpa_workspace_bytes",
-              "rpa_status_string", "rpa_slot_mapping", "rpa_kv_cache_write"):
+              "rpa_status_string", "rpa_slot_mapping", "rpa_kv_cache_write", "rpa_attn_varlen_fp8",
+              "rpa_kv_cache_write_fp8"):
         assert n in names
 
 
@@ -150,6 +151,49 @@ def test_kv_cache_write_argument_errors(L):
     assert f(FAKE, FAKE, None, 3, 2, 64, 4, 16, FAKE, FAKE, None) == NULL
     assert f(FAKE, FAKE, FAKE, 3, 2, 64, 4, 16, FAKE, None, None) == NULL
     assert f(None, None, None, 0, 2, 64, 4, 16, None, None, None) == OK
+
+
+def _attn8(L, ks=1.0, vs=1.0, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, P=4, seqlens=FAKE, cu=FAKE, B=2, T=2, H=32, Hkv=8, D=128,
+             NB=8, BS=16, maxq=1, scale=0.125, causal=1, left=-1, right=-1, R=0, rel=None, S=0,
+             ws=FAKE, wsb=bnd.rpa_workspace_bytes(0, 2, 32, 128), out=FAKE, lse=None)
+    a.update(kw)
+    return L.rpa_attn_varlen_fp8(a["q"], a["k"], a["v"], ks, vs, a["bt"], a["P"], a["seqlens"], a["cu"], a["B"],
+                                 a["T"], a["H"], a["Hkv"], a["D"], a["NB"], a["BS"], a["maxq"], a["scale"],
+                                 a["causal"], a["left"], a["right"], a["R"], a["rel"], a["S"], a["ws"],
+                                 a["wsb"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("ks,vs", [(0.0, 1.0), (1.0, 0.0), (-1.0, 1.0), (1.0, -2.0), (float("nan"), 1.0),
+                                   (1.0, float("inf"))])
+def test_fp8_attention_rejects_bad_scales(L, ks, vs):
+    assert _attn8(L, ks, vs) == SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(S=1), dict(S=4, wsb=1 << 30), dict(Hkv=4, H=32),
+                                dict(maxq=40), dict(T=40, B=2, maxq=20)])
+def test_fp8_attention_outside_its_path_is_unsupported(L, kw):
+    # Only the balanced decode with eight kv heads reads E4M3 caches.
+    assert _attn8(L, **kw) == UNSUP
+
+
+def test_fp8_attention_argument_errors(L):
+    assert _attn8(L, k=None) == NULL
+    assert _attn8(L, D=96) == UNSUP
+    assert _attn8(L, ws=None) == WS
+    assert _attn8(L, T=0, B=0, q=None, out=None) == OK
+
+
+def test_kv_cache_write_fp8_argument_errors(L):
+    f = L.rpa_kv_cache_write_fp8
+    assert f(FAKE, FAKE, FAKE, 3, 2, 64, 4, 16, 0.0, 1.0, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 3, 2, 64, 4, 16, 1.0, float("nan"), FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 3, 2, 64, 4, 16, -1.0, 1.0, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, -1, 2, 64, 4, 16, 1.0, 1.0, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 3, 1, 12, 4, 16, 1.0, 1.0, FAKE, FAKE, None) == UNSUP
+    assert f(None, FAKE, FAKE, 3, 2, 64, 4, 16, 1.0, 1.0, FAKE, FAKE, None) == NULL
+    assert f(FAKE, FAKE, FAKE, 3, 2, 64, 4, 16, 1.0, 1.0, None, FAKE, None) == NULL
+    assert f(None, None, None, 0, 2, 64, 4, 16, 1.0, 1.0, None, None, None) == OK
 
 
 # ------------------------------------------------------------------ planner

@@ -1,0 +1,208 @@
+"""GPU parity of the FP8 KV cache against oracle/fp8.py.
+
+rpa_kv_cache_write_fp8 is integer work once the fp32 quotient is formed, so
+its codes are compared bit for bit (the oracle forms the same fp32 quotient).
+rpa_attn_varlen_fp8 is compared with the fp64 oracle over the dequantised
+caches to the attention tolerances (out max 2e-2, mean 2e-3; lse 1e-3).
+"""
+import math
+
+import pytest
+import torch
+
+from oracle import fp8 as ofp8
+from oracle import kv_cache as okv
+from relative_bias_amd import binding as bnd
+from relative_bias_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+OUT_MAX, OUT_MEAN, LSE_MAX = 2e-2, 2e-3, 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "these tests need a GPU"
+    bnd.lib()
+
+
+# ------------------------------------------------------------- KV write
+
+SPECIAL = [0.0, -0.0, 1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -10, -(2.0 ** -12), 447.0, 448.0, 460.0,
+           464.0, 1e30, -1e30, math.inf, -math.inf, math.nan, 1e-40, -3e-39, 2.0 ** -6, 2.0 ** -7 * 1.9375]
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(1.0, 1.0), (0.0371, 3.0), (0.125, 2.0 ** -7), (7.5, 0.01)])
+def test_kv_write_fp8_is_bit_exact(k_scale, v_scale):
+    w = wl.build([1, 5, 33, 2, 1], [40, 5, 100, 300, 17], num_heads=16, num_kv_heads=8, head_dim=128,
+                 block_size=16, seed=8)
+    g = torch.Generator().manual_seed(9)
+    T = w.num_tokens
+    key = (torch.randn((T, 8, 128), generator=g) * 4).to(torch.bfloat16)
+    val = (torch.randn((T, 8, 128), generator=g) * 0.3).to(torch.bfloat16)
+    sp = torch.tensor(SPECIAL, dtype=torch.float32).to(torch.bfloat16)
+    key.view(-1)[: sp.numel()] = sp
+    val.view(-1)[-sp.numel():] = sp
+    # Values near the rounding boundaries of x / scale.
+    key[3, 2] = (torch.linspace(-500, 500, 128) * k_scale).to(torch.bfloat16)
+    kc = torch.randint(0, 256, w.key_cache.shape, generator=g, dtype=torch.int32).to(torch.uint8)
+    vc = torch.randint(0, 256, w.key_cache.shape, generator=g, dtype=torch.int32).to(torch.uint8)
+    slots = okv.slot_mapping(w.block_table, w.k_lens, w.cu_seqlens_q.tolist(), 16)
+    want_k, want_v = ofp8.kv_cache_write_fp8(key, val, slots, kc, vc, k_scale, v_scale)
+    kg, vg = kc.cuda(), vc.cuda()
+    bnd.rpa_kv_cache_write_fp8(key.cuda(), val.cuda(), slots.cuda(), kg, vg, k_scale, v_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(kg.cpu(), want_k)
+    assert torch.equal(vg.cpu(), want_v)
+
+
+def test_kv_write_fp8_every_bf16_value():
+    """All 65536 bf16 bit patterns through the quantiser at two scales."""
+    allb = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    T, Hkv, D = 512, 1, 128
+    key = allb.reshape(T, Hkv, D).contiguous()
+    val = allb.flip(0).reshape(T, Hkv, D).contiguous()
+    slots = torch.arange(T, dtype=torch.int64)
+    kc = torch.zeros((T // 16, 16, Hkv, D), dtype=torch.uint8)
+    vc = torch.zeros_like(kc)
+    for ks, vs in ((1.0, 1.0), (0.3, 5.0)):
+        want_k, want_v = ofp8.kv_cache_write_fp8(key, val, slots, kc, vc, ks, vs)
+        kg, vg = kc.cuda(), vc.cuda()
+        bnd.rpa_kv_cache_write_fp8(key.cuda(), val.cuda(), slots.cuda(), kg, vg, ks, vs)
+        torch.cuda.synchronize()
+        assert torch.equal(kg.cpu(), want_k), f"key codes differ at scale {ks}"
+        assert torch.equal(vg.cpu(), want_v), f"value codes differ at scale {vs}"
+
+
+# ------------------------------------------------------------- attention
+
+def _fp8_workload(q_lens, k_lens, H, Hkv, D, R, k_scale, v_scale, seed, window=(-1, -1), extra_pages=0):
+    w = wl.build(q_lens, k_lens, num_heads=H, num_kv_heads=Hkv, head_dim=D, block_size=16, rel_extent=R,
+                 window_size=window, seed=seed, extra_pages=extra_pages)
+    g = torch.Generator().manual_seed(seed + 1000)
+    # Codes of N(0, 1) keys / values at the given scales (inputs, not results).
+    k8 = (torch.randn(w.key_cache.shape, generator=g) / k_scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    v8 = (torch.randn(w.key_cache.shape, generator=g) / v_scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    return w, k8, v8
+
+
+def _run_fp8(w, k8, v8, k_scale, v_scale, S=0):
+    wg = w.to("cuda")
+    out, lse = bnd.rpa_attn_varlen_fp8(
+        wg.q, k8.cuda(), v8.cuda(), k_scale=k_scale, v_scale=v_scale, block_table=wg.block_table,
+        cache_seqlens=wg.cache_seqlens, cu_seqlens_q=wg.cu_seqlens_q, max_seqlen_q=wg.max_seqlen_q,
+        softmax_scale=wg.softmax_scale, causal=wg.causal, window_size=wg.window_size,
+        rel_extent=wg.rel_extent, rel_logits=wg.rel_logits, num_splits=S, return_lse=True)
+    torch.cuda.synchronize()
+    return out.float().cpu().double(), lse.cpu().double()
+
+
+def _compare(out, lse, ref_out, ref_lse, tag):
+    assert not torch.isnan(out).any(), f"{tag}: NaN in GPU output"
+    err = (out - ref_out).abs()
+    assert err.max().item() <= OUT_MAX, f"{tag}: out max err {err.max().item():.3e}"
+    assert err.mean().item() <= OUT_MEAN, f"{tag}: out mean err {err.mean().item():.3e}"
+    inf = torch.isinf(ref_lse)
+    assert torch.equal(torch.isinf(lse), inf), f"{tag}: lse -inf pattern differs"
+    if inf.any():
+        assert (out[inf] == 0).all()
+    if (~inf).any():
+        le = (lse[~inf] - ref_lse[~inf]).abs().max().item()
+        assert le <= LSE_MAX, f"{tag}: lse max err {le:.3e}"
+
+
+CASES = {
+    # name: (q_lens, k_lens, H, Hkv, D, R, k_scale, v_scale, window)
+    "ragged_d128": ([1] * 12, [1, 15, 16, 17, 100, 333, 1024, 1500, 2048, 2999, 64, 700], 32, 8, 128, 64,
+                    1 / 32, 1 / 16, (-1, -1)),
+    "g1_d64_nobias": ([1] * 5, [5, 900, 31, 2000, 129], 8, 8, 64, 0, 0.05, 0.2, (-1, -1)),
+    "g16_bias_wider_than_kv": ([1] * 4, [70, 10, 300, 1], 128, 8, 128, 400, 0.02, 0.03, (-1, -1)),
+    "two_tokens_g8": ([2, 2, 2], [2, 500, 1200], 64, 8, 128, 32, 1 / 64, 1 / 8, (-1, -1)),
+    "window": ([1] * 6, [3000, 100, 2000, 700, 4096, 256], 32, 8, 128, 128, 1 / 32, 1 / 16, (255, 0)),
+    "empty_rows": ([1, 2, 1, 1], [0, 1, 40, 0], 16, 8, 128, 16, 0.1, 0.1, (-1, -1)),
+    "scales_above_one": ([1] * 3, [800, 77, 1600], 32, 8, 128, 50, 4.0, 3.0, (-1, -1)),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_fp8_attention_matches_oracle(name):
+    ql, kl, H, Hkv, D, R, ks, vs, win = CASES[name]
+    w, k8, v8 = _fp8_workload(ql, kl, H, Hkv, D, R, ks, vs, seed=21, window=win, extra_pages=3)
+    ref_out, ref_lse = ofp8.attention_fp8(w.q, k8, v8, ks, vs, w.block_table, w.cache_seqlens, w.cu_seqlens_q,
+                                          w.softmax_scale, w.causal, w.window_size, w.rel_extent, w.rel_logits)
+    out, lse = _run_fp8(w, k8, v8, ks, vs)
+    _compare(out, lse, ref_out, ref_lse, name)
+
+
+def test_fp8_attention_is_repeatable_and_page_invariant():
+    ql, kl = [1] * 40, [int(x) for x in torch.randint(1, 5000, (40,), generator=torch.Generator().manual_seed(4))]
+    w, k8, v8 = _fp8_workload(ql, kl, 32, 8, 128, 128, 1 / 32, 1 / 16, seed=22)
+    a = _run_fp8(w, k8, v8, 1 / 32, 1 / 16)
+    b = _run_fp8(w, k8, v8, 1 / 32, 1 / 16)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    # The same logical pages at other physical places.
+    NB = k8.shape[0]
+    perm = torch.randperm(NB, generator=torch.Generator().manual_seed(5))
+    inv = torch.argsort(perm)
+    bt = w.block_table.clone()
+    valid = bt >= 0
+    bt[valid] = inv[bt[valid].long()].to(torch.int32)
+    w2 = w.to("cpu")
+    w2.block_table = bt
+    c = _run_fp8(w2, k8[perm].contiguous(), v8[perm].contiguous(), 1 / 32, 1 / 16)
+    assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
+
+
+def test_fp8_attention_unsupported_paths_raise():
+    w, k8, v8 = _fp8_workload([1, 1], [100, 200], 8, 2, 128, 0, 0.1, 0.1, seed=23)
+    with pytest.raises(bnd.RpaError):
+        _run_fp8(w, k8, v8, 0.1, 0.1)
+    w, k8, v8 = _fp8_workload([1, 1], [100, 200], 32, 8, 128, 0, 0.1, 0.1, seed=23)
+    with pytest.raises(bnd.RpaError):
+        _run_fp8(w, k8, v8, 0.1, 0.1, S=2)
+
+
+def _subset(w, k8, v8, reqs):
+    """The requests `reqs` of a workload with only their pages (test
+    plumbing: pages are copied, nothing is computed)."""
+    BS = w.block_size
+    pages, rows, cu, q_idx = [], [], [0], []
+    cu_all = w.cu_seqlens_q.tolist()
+    for b in reqs:
+        n = (w.k_lens[b] + BS - 1) // BS
+        rows.append(list(range(len(pages), len(pages) + n)))
+        pages += w.block_table[b, :n].tolist()
+        q_idx += list(range(cu_all[b], cu_all[b + 1]))
+        cu.append(cu[-1] + w.q_lens[b])
+    width = max(len(r) for r in rows) + 1
+    bt = torch.full((len(reqs), width), -1, dtype=torch.int32)
+    for i, r in enumerate(rows):
+        bt[i, :len(r)] = torch.tensor(r, dtype=torch.int32)
+    idx = torch.tensor(pages, dtype=torch.long)
+    qi = torch.tensor(q_idx, dtype=torch.long)
+    sub = w.to("cpu")
+    sub.q = w.q[qi]
+    sub.rel_logits = None if w.rel_logits is None else w.rel_logits[qi]
+    sub.block_table = bt
+    sub.cache_seqlens = torch.tensor([w.k_lens[b] for b in reqs], dtype=torch.int32)
+    sub.cu_seqlens_q = torch.tensor(cu, dtype=torch.int32)
+    sub.q_lens = [w.q_lens[b] for b in reqs]
+    sub.k_lens = [w.k_lens[b] for b in reqs]
+    return sub, k8[idx], v8[idx], qi
+
+
+def test_fp8_full_size_batched_decode_sampled():
+    """The 32-request batched decode (H=32, Hkv=8, D=128, R=128) with E4M3
+    caches of its K/V at scales 1/32 and 1/16, in the launch the benchmark
+    times (balanced decode); six requests checked against the oracle."""
+    w = wl.batched_decode()
+    ks, vs = 1 / 32, 1 / 16
+    k8 = (w.key_cache.float() / ks).to(torch.float8_e4m3fn).view(torch.uint8)
+    v8 = (w.value_cache.float() / vs).to(torch.float8_e4m3fn).view(torch.uint8)
+    out, lse = _run_fp8(w, k8, v8, ks, vs)
+    reqs = [0, 5, 11, 17, 26, 31]
+    sub, sk8, sv8, qi = _subset(w, k8, v8, reqs)
+    ref_out, ref_lse = ofp8.attention_fp8(sub.q, sk8, sv8, ks, vs, sub.block_table, sub.cache_seqlens,
+                                          sub.cu_seqlens_q, sub.softmax_scale, sub.causal, sub.window_size,
+                                          sub.rel_extent, sub.rel_logits)
+    _compare(out[qi], lse[qi], ref_out, ref_lse, "batched_decode fp8")
