@@ -272,7 +272,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None, help="run one workload: batched_decode, chunked_prefill, "
                                                   "long_decode, continuous_batch, batched_decode_fp8, "
-                                                  "long_decode_fp8, kv_write")
+                                                  "chunked_prefill_fp8, long_decode_fp8, kv_write")
     ap.add_argument("--splits", type=int, default=None,
                     help="override the planner's num_splits (0 = balanced decode) for the headline decode batch "
                          "(or for long_decode with --only long_decode)")
@@ -370,6 +370,14 @@ def main(argv=None):
             log(f"batched_decode_fp8: {ms * 1e3:.1f} us/step, {wk['bytes'] / ms / 1e6:.1f} GB/s")
             del r6, w6
             torch.cuda.empty_cache()
+        if a.only in (None, "chunked_prefill_fp8"):
+            w8 = wl.chunked_prefill(device="cpu").to(dev)
+            r8 = Fp8Runner(w8, 1)
+            ms, ms_c, wk = measure(r8, max(5, a.steps // 2), a.warmup, SETTLE_S)
+            results["chunked_prefill_fp8"] = (w8, 1, ms, ms_c, wk)
+            log(f"chunked_prefill_fp8: {ms * 1e3:.1f} us/step, {wk['flops'] / ms / 1e9:.1f} TFLOP/s")
+            del r8, w8
+            torch.cuda.empty_cache()
         if a.only in (None, "long_decode_fp8"):
             w7 = wl.long_decode(device=dev)
             r7 = Fp8Runner(w7, 0)
@@ -395,8 +403,10 @@ def main(argv=None):
         w, S, ms, ms_c, wk = results[name]
         extra = {}
         if name.endswith("_fp8"):
+            kern = ("attn_kernel<128, false, true>" if S == 1 else
+                    "decode_heads_kernel<128, true, true> + combine_heads_kernel<128>")
             extra = {"kv_cache": "e4m3", "k_scale": Fp8Runner.K_SCALE, "v_scale": Fp8Runner.V_SCALE,
-                     "kernel": "decode_heads_kernel<128, true, true> + combine_heads_kernel<128>"}
+                     "kernel": kern}
         return {**extra, "workload": name, "batch": w.batch, "num_tokens": w.num_tokens, "num_heads": w.num_heads,
                 "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                 "rel_extent": w.rel_extent, "window": list(w.window_size), "num_splits": S,
@@ -412,7 +422,7 @@ def main(argv=None):
     head = a.only if a.only else "batched_decode"
     w, S, ms, ms_c, wk = results[head]
     kernel_ms = ms - ms_c
-    prefill_like = head == "chunked_prefill"
+    prefill_like = head in ("chunked_prefill", "chunked_prefill_fp8")
     if prefill_like:
         achieved = wk["flops"] / kernel_ms / 1e9
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -428,13 +438,13 @@ def main(argv=None):
         # requests cut between workgroups; kernel_ms is the whole step (both
         # kernels).  Eight kv heads take the form with one kv head per wave.
         if head.endswith("_fp8"):
-            roof["kernel"] = "decode_heads_kernel<128, e4m3> + combine_heads_kernel<128>"
+            roof["kernel"] = "decode_heads_kernel<128, true, true> + combine_heads_kernel<128>"
         elif w.num_kv_heads == 8:
             roof["kernel"] = "decode_heads_kernel<128> + combine_heads_kernel<128>"
         else:
             roof["kernel"] = "decode_balanced_kernel<128> + combine_balanced_kernel<128>"
     else:
-        roof["kernel"] = "attn_kernel<128>"
+        roof["kernel"] = "attn_kernel<128, false, true>" if head.endswith("_fp8") else "attn_kernel<128>"
     roof["kernel_ms"] = round(kernel_ms, 5)
     roof["alg_bytes_per_launch"] = wk["bytes"]
     roof["traffic"] = load_traffic(head)

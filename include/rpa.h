@@ -45,7 +45,7 @@ typedef enum {
   RPA_OK = 0,
   RPA_ERR_NULL = -1,        /* a required pointer is NULL                         */
   RPA_ERR_SHAPE = -2,       /* inconsistent or negative sizes                     */
-  RPA_ERR_UNSUPPORTED = -3, /* head_dim not 64/128, block_size not a multiple of 16, FP8 call outside its path */
+  RPA_ERR_UNSUPPORTED = -3, /* head_dim not 64/128, block_size not a multiple of 16     */
   RPA_ERR_WORKSPACE = -4,   /* num_splits != 1 and the workspace is missing/small */
   RPA_ERR_HIP = -5          /* a HIP launch failed                                */
 } rpa_status;
@@ -223,10 +223,9 @@ int rpa_kv_cache_write(const void *key, const void *value, const int64_t *slot_m
  *   value_cache   uint8 E4M3 codes [num_blocks, block_size, num_kv_heads, head_dim].
  *   k_scale,
  *   v_scale       finite and > 0, else RPA_ERR_SHAPE.
- * Every other argument is that of rpa_attn_varlen.  Supported: the balanced
- * decode (num_splits = 0 on a batch where it applies, see above) with
- * num_kv_heads = 8; any other call returns RPA_ERR_UNSUPPORTED before
- * anything is enqueued.
+ * Every other argument, the supported sizes and the error behaviour are
+ * those of rpa_attn_varlen (every split count and batch mix; the kernels
+ * decode the codes to bf16 exactly as they stage each page).
  */
 int rpa_attn_varlen_fp8(const void *q, const void *key_cache, const void *value_cache, float k_scale,
                         float v_scale, const int32_t *block_table, int32_t max_pages_per_seq,

@@ -28,7 +28,7 @@ const char *rpa_status_string(int status) {
     case RPA_OK: return "ok";
     case RPA_ERR_NULL: return "a required pointer is NULL";
     case RPA_ERR_SHAPE: return "inconsistent or out-of-range sizes";
-    case RPA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size or FP8-cache configuration";
+    case RPA_ERR_UNSUPPORTED: return "unsupported head_dim or block_size";
     case RPA_ERR_WORKSPACE: return "workspace missing or too small for num_splits";
     case RPA_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";
@@ -140,8 +140,6 @@ int attn_impl(const void *q, const void *key_cache, const void *value_cache, boo
   const bool balanced = num_splits == 0 && decode_only && batch <= rpa::kBalMaxBatch &&
                         (int64_t)num_tokens * num_heads * rel_extent * 4 < ((int64_t)1 << 31);
   if (num_splits == 0 && !balanced) num_splits = 1;
-  // E4M3 caches: the balanced decode with eight kv heads.
-  if (kv8 && !(balanced && num_kv_heads == rpa::kBalHeads)) return RPA_ERR_UNSUPPORTED;
   if (n_items_ub * num_kv_heads * (int64_t)num_splits > INT32_MAX) return RPA_ERR_SHAPE;
   int32_t bal_wgs = 0;
   if (balanced) {

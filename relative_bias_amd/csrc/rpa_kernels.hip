@@ -91,6 +91,64 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
 }
+__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 lds_read_b128_asm(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ u32x2 lds_read_b64_asm(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait_n(u32x2 (&r)[2]) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r[0]), "+v"(r[1]) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait_n(u32x4 (&r)[2]) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r[0]), "+v"(r[1]) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait_n(u32x4 (&r)[1]) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r[0]) : "n"(N));
+}
+// Two or four 16-byte LDS writes, complete when the asm ends.
+__device__ __forceinline__ void lds_write_b128x2_now(uint32_t a0, uint32_t a1, u32x4 v0, u32x4 v1) {
+  asm volatile("ds_write_b128 %0, %2\n\tds_write_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               :
+               : "v"(a0), "v"(a1), "v"(v0), "v"(v1)
+               : "memory");
+}
+__device__ __forceinline__ void lds_write_b128x4_now(const uint32_t (&a)[4], const u32x4 (&v)[4]) {
+  asm volatile(
+      "ds_write_b128 %0, %4\n\tds_write_b128 %1, %5\n\tds_write_b128 %2, %6\n\tds_write_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      :
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3])
+      : "memory");
+}
+
+// E4M3 (OCP) codes to bf16: v_cvt_pk_f32_fp8 decodes two codes exactly to
+// fp32 (every E4M3 value has at most four significant bits, so its upper
+// 16 bits are its bf16 form); v_perm packs those halves.  Four codes of one
+// dword become two dwords of bf16 pairs in element order.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t x) {
+  typedef float f32x2_ __attribute__((ext_vector_type(2)));
+  const f32x2_ a = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, false);
+  const f32x2_ b = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, true);
+  return u32x2{__builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u),
+               __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u)};
+}
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t x0, uint32_t x1) {
+  const u32x2 lo = e4m3x4_to_bf16(x0), hi = e4m3x4_to_bf16(x1);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 __device__ __forceinline__ u32x4 zero16() { return u32x4{0u, 0u, 0u, 0u}; }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -262,7 +320,7 @@ __device__ __forceinline__ Range split_range(Range r, int kmax, int S, int s, in
 
 // ---------------------------------------------------------------- prefill
 
-template <int D>
+template <int D, bool KV8 = false>
 struct PrefillLds {
   static constexpr int UNITS = D / 8;                 // 16-byte units per key row
   static constexpr int ROWB = D * 2;                  // bytes per key row (unpadded)
@@ -270,7 +328,10 @@ struct PrefillLds {
   static constexpr int NK = 2, NV = 2;                // double-buffered K and V tiles
   static constexpr int kOff(int i) { return i * tileBytes; }
   static constexpr int vOff(int i) { return (NK + i) * tileBytes; }
-  static constexpr int bytes = (NK + NV) * tileBytes;
+  // E4M3 caches: landing areas of the raw K and V rows of one tile.
+  static constexpr int land8K = (NK + NV) * tileBytes;
+  static constexpr int land8V = land8K + kTileKeys * D;
+  static constexpr int bytes = (NK + NV) * tileBytes + (KV8 ? 2 * kTileKeys * D : 0);
 };
 
 // K and V tiles are stored row-major (one key per row) with the 16-byte
@@ -604,12 +665,12 @@ __device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32
   return fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
 }
 
-template <int D>
+template <int D, bool KV8>
 __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, char *smem) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
   constexpr int ROWS = kTileRows;
-  using L = PrefillLds<D>;
+  using L = PrefillLds<D, KV8>;
 
   const int b = it.b;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -692,7 +753,8 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   float m_run = neg_inf(), l_run = 0.f;
 
   const int64_t tok_stride = (int64_t)p.Hkv * D;     // elements between consecutive slots
-  const uint32_t slot_bytes = (uint32_t)(tok_stride * 2);
+  constexpr int EB = KV8 ? 1 : 2;                     // bytes per cache element
+  const uint32_t slot_bytes = (uint32_t)(tok_stride * EB);
   const uint64_t page_bytes = (uint64_t)p.BS * slot_bytes;
   const int32_t *bt = p.block_table + (int64_t)b * p.P;
   auto pidx = [&](int key) { return p.bs_shift >= 0 ? key >> p.bs_shift : key / p.BS; };
@@ -733,8 +795,8 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   int pc = load_pages(0);
   int pc_next = load_pages(64);
   auto page_t = [&](int jt) { return __builtin_amdgcn_readlane(pc, jt - pc_base); };
-  const char *kcache = reinterpret_cast<const char *>(p.k) + (uint64_t)g * D * 2;
-  const char *vcache = reinterpret_cast<const char *>(p.v) + (uint64_t)g * D * 2;
+  const char *kcache = reinterpret_cast<const char *>(p.k) + (uint64_t)g * D * EB;
+  const char *vcache = reinterpret_cast<const char *>(p.v) + (uint64_t)g * D * EB;
   // Direct loads of tile jt (zeros past the last tile).
   auto dma = [&](const char *cache, int jt, int page, int lds_off, const uint32_t *voff) __attribute__((always_inline)) {
     const bool live = jt < nt;
@@ -746,6 +808,55 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     for (int n = 0; n < NI; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (__attribute__((address_space(3))) void *)(smem + lds_off + (kbw + RPI * n) * ROWB), 16, voff[n], 0, 0, 0);
+  };
+  // E4M3 caches: the direct loads bring the raw rows of a tile (key order,
+  // D bytes a row) to a landing area, wave w its own 16 keys; once they
+  // have arrived (the wait before the barrier that publishes the tile) the
+  // wave decodes its rows into the tile's bf16 slot at the places the bf16
+  // loads would have filled, so the rest of the pipeline is unchanged.
+  constexpr int U8 = D / 16, RPI8 = 64 / U8, NI8 = 16 / RPI8;
+  uint32_t voff8[KV8 ? NI8 : 1], dst_k8[KV8 ? 2 * NI8 : 1], dst_v8[KV8 ? 2 * NI8 : 1];
+  if constexpr (KV8) {
+#pragma unroll
+    for (int n = 0; n < NI8; ++n) {
+      const int kk = RPI8 * n + lane / U8, pc = lane % U8;
+      voff8[n] = (uint32_t)kk * slot_bytes + (uint32_t)(pc << 4);
+      const int R = kbw + rev4(kk);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        dst_k8[2 * n + e] = (uint32_t)(R * ROWB + (((2 * pc + e) ^ swz_k<D>(R)) << 4));
+        dst_v8[2 * n + e] = (uint32_t)(R * ROWB + (((2 * pc + e) ^ swz_v<D>(R)) << 4));
+      }
+    }
+  }
+  auto dma8 = [&](const char *cache, int jt, int page, int land_off) __attribute__((always_inline)) {
+    const bool live = jt < nt;
+    const int key = (live ? tile_kb(jt) : t0) + kbw;
+    const int nvalid = live ? min(max(kend - key, 0), 16) : 0;
+    const char *src = cache + (uint64_t)(uint32_t)page * page_bytes + (uint64_t)(uint32_t)pslot(key) * slot_bytes;
+    const auto rs = make_rsrc(src, (uint32_t)nvalid * slot_bytes);
+#pragma unroll
+    for (int n = 0; n < NI8; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void *)(smem + land_off + (kbw + RPI8 * n) * D), 16, voff8[n], 0, 0,
+          0);
+  };
+  const uint32_t smem_u = (uint32_t)(uintptr_t)smem;
+  auto decode8 = [&](int land_off, int slot_off, const uint32_t *dst) __attribute__((always_inline)) {
+    u32x4 raw[NI8];
+#pragma unroll
+    for (int n = 0; n < NI8; ++n) raw[n] = lds_read_b128_asm(smem_u + land_off + (kbw + RPI8 * n) * D + 16 * lane);
+    lgkm_wait_n<0>(raw);
+    const uint32_t base = smem_u + slot_off;
+    if constexpr (NI8 == 2) {
+      const uint32_t a[4] = {base + dst[0], base + dst[1], base + dst[2], base + dst[3]};
+      const u32x4 vv[4] = {e4m3x8_to_bf16(raw[0][0], raw[0][1]), e4m3x8_to_bf16(raw[0][2], raw[0][3]),
+                           e4m3x8_to_bf16(raw[1][0], raw[1][1]), e4m3x8_to_bf16(raw[1][2], raw[1][3])};
+      lds_write_b128x4_now(a, vv);
+    } else {
+      lds_write_b128x2_now(base + dst[0], base + dst[1], e4m3x8_to_bf16(raw[0][0], raw[0][1]),
+                           e4m3x8_to_bf16(raw[0][2], raw[0][3]));
+    }
   };
   // The LDS writes of direct loads are tracked by vmcnt only: wait for them
   // before the barrier that publishes a tile.  When the 32 bias loads of a
@@ -840,9 +951,20 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     int pg_k = page_t(2);
     {
       const int pg0 = page_t(0);
-      dma(kcache, 0, pg0, L::kOff(0), voff_k);
-      dma(vcache, 0, pg0, L::vOff(0), voff_v);
-      dma(kcache, 1, pg_v, L::kOff(1), voff_k);
+      if constexpr (KV8) {
+        dma8(kcache, 0, pg0, L::land8K);
+        dma8(vcache, 0, pg0, L::land8V);
+        wait_vm0();
+        decode8(L::land8K, L::kOff(0), dst_k8);
+        decode8(L::land8V, L::vOff(0), dst_v8);
+        dma8(kcache, 1, pg_v, L::land8K);
+        wait_vm0();
+        decode8(L::land8K, L::kOff(1), dst_k8);
+      } else {
+        dma(kcache, 0, pg0, L::kOff(0), voff_k);
+        dma(vcache, 0, pg0, L::vOff(0), voff_v);
+        dma(kcache, 1, pg_v, L::kOff(1), voff_k);
+      }
       zero(sa);
       begin(sa, tile_kb(0));
       prefetch_band_rows();
@@ -879,8 +1001,13 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       __builtin_amdgcn_sched_barrier(0);
       // Direct loads: K(j+2) into K slot PAR (K(j) was consumed before the
       // last barrier), V(j+1) into V slot 1-PAR.
-      dma(kcache, j + 2, pg_k, L::kOff(PAR), voff_k);
-      dma(vcache, j + 1, pg_v, L::vOff(1 - PAR), voff_v);
+      if constexpr (KV8) {
+        dma8(kcache, j + 2, pg_k, L::land8K);
+        dma8(vcache, j + 1, pg_v, L::land8V);
+      } else {
+        dma(kcache, j + 2, pg_k, L::kOff(PAR), voff_k);
+        dma(vcache, j + 1, pg_v, L::vOff(1 - PAR), voff_v);
+      }
       if (j + 3 - pc_base == 64) {
         pc = pc_next;
         pc_base += 64;
@@ -905,6 +1032,10 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       if (!band2) wait_vm0();
       else if (bias_fast) wait_vm8();
       else wait_vm32();
+      if constexpr (KV8) {
+        decode8(L::land8K, L::kOff(PAR), dst_k8);
+        decode8(L::land8V, L::vOff(1 - PAR), dst_v8);
+      }
       barrier_raw();
       if (has_next) update_max(xor32_max(mx));
     };
@@ -917,7 +1048,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
 
   // Epilogue: lane (l32, hf) holds O^T[d = 32 db + 8 (j/4) + 4 hf + j%4][row l32].
   const float l_tot = xor32_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? (KV8 ? p.v_scale / l_tot : 1.f / l_tot) : 0.f;
   const float lse_v = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : neg_inf();
   if (!row_valid) return;
   if (p.S == 1) {
@@ -970,16 +1101,18 @@ __device__ __forceinline__ int decode_key_of_slot(int p) {
   return 4 * (p >> 3) + (p & 7) + ((p & 4) ? 12 : 0);
 }
 
-template <int D>
+template <int D, bool KV8>
 struct DecodeRegs {
-  u32x4 k[2][D / 32];
-  u32x4 v[D / 16];
+  // bf16: 16-byte loads; E4M3 caches: 8-byte loads of the same elements.
+  using R = typename std::conditional<KV8, u32x2, u32x4>::type;
+  R k[2][D / 32];
+  R v[D / 16];
 };
 
 // NSET register sets form a ring: while block i is computed, the loads of
 // blocks i+1 .. i+NSET-1 (and, once block i's registers are consumed, of
 // block i+NSET) are in flight.
-template <int D, int NSET, int NW>
+template <int D, int NSET, int NW, bool KV8>
 __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, char *smem) {
   using DL = DecodeLds<D, NW>;
   constexpr int STEP = NW * kDecWaveKeys;  // keys per workgroup per iteration
@@ -1051,7 +1184,8 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
   struct BlockRsrc {
     __amdgpu_buffer_rsrc_t k[2], v[2];
   };
-  const uint32_t slot_bytes = (uint32_t)(tok_stride * 2);
+  constexpr int EB = KV8 ? 1 : 2;  // bytes per cache element
+  const uint32_t slot_bytes = (uint32_t)(tok_stride * EB);
   auto rows_of = [&](int base, BlockRsrc &br) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -1064,52 +1198,64 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
         page = __builtin_amdgcn_readfirstlane(pcache[pidx - pfirst]);
       }
       const int64_t off = (((int64_t)page * p.BS + slot0) * p.Hkv + g) * D;
-      br.k[blk] = make_rsrc(p.k + off, (uint32_t)nvalid * slot_bytes);
-      br.v[blk] = make_rsrc(p.v + off, (uint32_t)nvalid * slot_bytes);
+      br.k[blk] = make_rsrc(reinterpret_cast<const char *>(p.k) + off * EB, (uint32_t)nvalid * slot_bytes);
+      br.v[blk] = make_rsrc(reinterpret_cast<const char *>(p.v) + off * EB, (uint32_t)nvalid * slot_bytes);
     }
   };
   // Per-lane byte offsets inside a block (fixed for the whole loop).
   uint32_t koff[QK], voff[KPL];
 #pragma unroll
-  for (int ks = 0; ks < QK; ++ks) koff[ks] = c16 * slot_bytes + (uint32_t)(q * DQ + 8 * ks) * 2;
+  for (int ks = 0; ks < QK; ++ks) koff[ks] = c16 * slot_bytes + (uint32_t)(q * DQ + 8 * ks) * EB;
 #pragma unroll
   for (int rr = 0; rr < KPL; ++rr) {
     const int kr = decode_key_of_slot(vg * KPL + rr);
-    voff[rr] = (kr & 15) * slot_bytes + (uint32_t)vdc * 16;
+    voff[rr] = (kr & 15) * slot_bytes + (uint32_t)vdc * 8 * EB;
   }
-  auto issue_k = [&](DecodeRegs<D> &Rg, const BlockRsrc &br) {
+  auto ld = [&](__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (KV8) return bload8(r, off);
+    else return bload16(r, off);
+  };
+  // Eight elements as bf16 (E4M3 codes are decoded exactly).
+  auto as_bf = [&](const typename DecodeRegs<D, KV8>::R &x) {
+    if constexpr (KV8) return e4m3x8_to_bf16(x[0], x[1]);
+    else return x;
+  };
+  auto issue_k = [&](DecodeRegs<D, KV8> &Rg, const BlockRsrc &br) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int ks = 0; ks < QK; ++ks) Rg.k[blk][ks] = bload16(br.k[blk], koff[ks]);
+      for (int ks = 0; ks < QK; ++ks) Rg.k[blk][ks] = ld(br.k[blk], koff[ks]);
   };
-  auto issue_v = [&](DecodeRegs<D> &Rg, const BlockRsrc &br) {
+  auto issue_v = [&](DecodeRegs<D, KV8> &Rg, const BlockRsrc &br) {
 #pragma unroll
     for (int rr = 0; rr < KPL; ++rr) {
       const int kr = decode_key_of_slot(vg * KPL + rr);
-      Rg.v[rr] = bload16(br.v[kr >> 4], voff[rr]);
+      Rg.v[rr] = ld(br.v[kr >> 4], voff[rr]);
     }
   };
 
   // One 32-key block.  A single register set carries the block: V is moved
   // to LDS first and its registers immediately receive the next block's V;
   // once the QK MFMAs have read K, the next block's K loads land there too.
-  auto compute = [&](DecodeRegs<D> &Rg, int base, int nbase, bool has_next, auto mask_tag, auto bias_tag) {
+  auto compute = [&](DecodeRegs<D, KV8> &Rg, int base, int nbase, bool has_next, auto mask_tag, auto bias_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr bool BIAS = decltype(bias_tag)::value;
     constexpr bool PLAIN = !MASK && !BIAS;
     BlockRsrc nbr;
     if (has_next) rows_of(nbase, nbr);
     wave_lds_sync();
+    u32x4 vb[KPL];
+#pragma unroll
+    for (int rr = 0; rr < KPL; ++rr) vb[rr] = as_bf(Rg.v[rr]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       uint16_t *dst = Vt + (vdc * 8 + e) * VS + vg * KPL;
       if constexpr (KPL == 8) {
         *reinterpret_cast<u32x4 *>(dst) =
-            u32x4{pair_elem(Rg.v[0], Rg.v[1], e), pair_elem(Rg.v[2], Rg.v[3], e),
-                  pair_elem(Rg.v[4], Rg.v[5], e), pair_elem(Rg.v[6], Rg.v[7], e)};
+            u32x4{pair_elem(vb[0], vb[1], e), pair_elem(vb[2], vb[3], e),
+                  pair_elem(vb[4], vb[5], e), pair_elem(vb[6], vb[7], e)};
       } else {
-        *reinterpret_cast<u32x2 *>(dst) = u32x2{pair_elem(Rg.v[0], Rg.v[1], e), pair_elem(Rg.v[2], Rg.v[3], e)};
+        *reinterpret_cast<u32x2 *>(dst) = u32x2{pair_elem(vb[0], vb[1], e), pair_elem(vb[2], vb[3], e)};
       }
     }
     if (has_next) issue_v(Rg, nbr);
@@ -1118,7 +1264,7 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
     for (int blk = 0; blk < 2; ++blk) {
       sacc[blk] = f32x4{};
 #pragma unroll
-      for (int ks = 0; ks < QK; ++ks) sacc[blk] = mfma16(as_bf16x8(Rg.k[blk][ks]), qf[ks], sacc[blk]);
+      for (int ks = 0; ks < QK; ++ks) sacc[blk] = mfma16(as_bf16x8(as_bf(Rg.k[blk][ks])), qf[ks], sacc[blk]);
     }
     if (has_next) issue_k(Rg, nbr);
     // Lane (c16, q) holds S[col c16][key base + 16 blk + 4 q + j].
@@ -1185,7 +1331,7 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
     }
   };
 
-  auto step = [&](DecodeRegs<D> &Rg, int base, int nbase, bool has_next) {
+  auto step = [&](DecodeRegs<D, KV8> &Rg, int base, int nbase, bool has_next) {
     const bool interior = base >= in_lo && base + kDecWaveKeys - 1 <= in_hi;
     const bool bias = p.R > 0 && base <= band_hi && base + kDecWaveKeys - 1 >= band_lo;
     if (interior && !bias) compute(Rg, base, nbase, has_next, BoolTag<false>{}, BoolTag<false>{});
@@ -1208,7 +1354,7 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
     __syncthreads();
     const int nblk = (sg1 - sg0 + kDecWaveKeys - 1) / kDecWaveKeys;
     const int my_n = nblk > w ? (nblk - w + NW - 1) / NW : 0;
-    DecodeRegs<D> Rg[NSET];
+    DecodeRegs<D, KV8> Rg[NSET];
 #pragma unroll
     for (int j = 0; j < NSET; ++j) {
       if (j < my_n) {
@@ -1261,7 +1407,7 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
     sc[ww] = mw[ww] == neg_inf() ? 0.f : exp2_fast(mw[ww] - M);
     L += sc[ww] * red_l[ww * kDecCols + fc];
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const float inv = L > 0.f ? (KV8 ? p.v_scale / L : 1.f / L) : 0.f;
   const float lse_v = L > 0.f ? (M + log2_fast(L)) * kLn2 : neg_inf();
   float o[DPG];
 #pragma unroll
@@ -1304,18 +1450,19 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
 template <bool DECODE_ONLY>
 constexpr int attn_waves() { return 4; }
 
-template <int D, bool DECODE_ONLY>
+template <int D, bool DECODE_ONLY, bool KV8>
 constexpr int attn_lds_bytes() {
   using DL = DecodeLds<D, attn_waves<DECODE_ONLY>()>;
-  return (DECODE_ONLY || PrefillLds<D>::bytes < DL::bytes) ? DL::bytes : PrefillLds<D>::bytes;
+  using PL = PrefillLds<D, KV8>;
+  return (DECODE_ONLY || PL::bytes < DL::bytes) ? DL::bytes : PL::bytes;
 }
 
 // DECODE_ONLY: every request of the batch has Lq*G <= 16 (known on the host
 // from max_seqlen_q), so the prefill path is not compiled in.  Both variants
 // hold two workgroups, i.e. two waves per SIMD, per CU.
-template <int D, bool DECODE_ONLY>
+template <int D, bool DECODE_ONLY, bool KV8>
 __global__ __launch_bounds__(64 * attn_waves<DECODE_ONLY>(), 2) void attn_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[attn_lds_bytes<D, DECODE_ONLY>()];
+  __shared__ __attribute__((aligned(16))) char smem[attn_lds_bytes<D, DECODE_ONLY, KV8>()];
   const int bid = blockIdx.x;
   const int s = bid % p.S;
   const int rest = bid / p.S;
@@ -1324,9 +1471,9 @@ __global__ __launch_bounds__(64 * attn_waves<DECODE_ONLY>(), 2) void attn_kernel
   const Item it = resolve_item(p, item, DECODE_ONLY, kTileRows);
   const int kind = __builtin_amdgcn_readfirstlane(it.kind);
   if (kind == 2) {
-    decode_item<D, 1, attn_waves<DECODE_ONLY>()>(p, it, g, s, smem);
+    decode_item<D, 1, attn_waves<DECODE_ONLY>(), KV8>(p, it, g, s, smem);
   } else if constexpr (!DECODE_ONLY) {
-    if (kind == 1) prefill_item<D>(p, it, g, s, smem);
+    if (kind == 1) prefill_item<D, KV8>(p, it, g, s, smem);
   }
 }
 
@@ -1378,20 +1525,11 @@ struct BalLds {
 template <int D>
 __device__ __forceinline__ int swz_vt(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 
-__device__ __forceinline__ u32x4 lds_read_b128_asm(uint32_t addr) {
-  u32x4 v;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
-  return v;
-}
 // s_waitcnt lgkmcnt(N) that the listed registers wait for (their values
 // arrive by inline-asm LDS reads the compiler does not track).
 template <int N>
 __device__ __forceinline__ void lgkm_wait_n(u32x4 (&r)[4]) {
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "n"(N));
-}
-template <int N>
-__device__ __forceinline__ void lgkm_wait_n(u32x4 (&r)[2]) {
-  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r[0]), "+v"(r[1]) : "n"(N));
 }
 template <int N>
 __device__ __forceinline__ void lgkm_wait_n(u32x2 (&r)[8]) {
@@ -1470,51 +1608,6 @@ __device__ __forceinline__ u32x2 lds_read_tr_at(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr) : "memory");
   return v;
 }
-__device__ __forceinline__ u32x2 lds_read_b64_asm(uint32_t addr) {
-  u32x2 v;
-  asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(addr) : "memory");
-  return v;
-}
-template <int N>
-__device__ __forceinline__ void lgkm_wait_n(u32x2 (&r)[2]) {
-  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r[0]), "+v"(r[1]) : "n"(N));
-}
-template <int N>
-__device__ __forceinline__ void lgkm_wait_n(u32x4 (&r)[1]) {
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r[0]) : "n"(N));
-}
-// Two or four 16-byte LDS writes, complete when the asm ends.
-__device__ __forceinline__ void lds_write_b128x2_now(uint32_t a0, uint32_t a1, u32x4 v0, u32x4 v1) {
-  asm volatile("ds_write_b128 %0, %2\n\tds_write_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-               :
-               : "v"(a0), "v"(a1), "v"(v0), "v"(v1)
-               : "memory");
-}
-__device__ __forceinline__ void lds_write_b128x4_now(const uint32_t (&a)[4], const u32x4 (&v)[4]) {
-  asm volatile(
-      "ds_write_b128 %0, %4\n\tds_write_b128 %1, %5\n\tds_write_b128 %2, %6\n\tds_write_b128 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      :
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3])
-      : "memory");
-}
-
-// E4M3 (OCP) codes to bf16: v_cvt_pk_f32_fp8 decodes two codes exactly to
-// fp32 (every E4M3 value has at most four significant bits, so its upper
-// 16 bits are its bf16 form); v_perm packs those halves.  Four codes of one
-// dword become two dwords of bf16 pairs in element order.
-__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t x) {
-  typedef float f32x2_ __attribute__((ext_vector_type(2)));
-  const f32x2_ a = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, false);
-  const f32x2_ b = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, true);
-  return u32x2{__builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u),
-               __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u)};
-}
-__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t x0, uint32_t x1) {
-  const u32x2 lo = e4m3x4_to_bf16(x0), hi = e4m3x4_to_bf16(x1);
-  return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
-
 __device__ __forceinline__ f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
                                                    0, 0, 0);
@@ -1562,13 +1655,19 @@ __device__ void bal_prefix(const AttnParams &p, int32_t *prefix, int32_t *tmp, i
 
 __device__ __forceinline__ int bal_unit_at(int TU, int x, int nwg) { return (int)((int64_t)TU * x / nwg); }
 
-template <int D, bool BIAS>
+template <int D, bool BIAS, bool KV8>
 __device__ void decode_balanced(const AttnParams &p, char *smem) {
   using L = BalLds<D>;
   constexpr int NW = kBalWaves;
   constexpr int QK = D / 32, DB = D / 16, NI = L::NI, RPI = L::RPI, UNITS = L::UNITS, ROWB = L::ROWB;
   static_assert(L::NST == 2, "two stages per wave: one computed, one in flight");
-  constexpr int NPER = 2 * NI + (BIAS ? 4 : 0);  // vector-memory instructions per unit
+  // E4M3 caches (as in decode_heads): two raw stages, then the bf16 V stage,
+  // which the merge also uses for the wave's O^T (it holds no load).
+  constexpr int U8 = D / 16, RPI8 = 64 / U8, NI8 = 16 / RPI8;
+  constexpr uint32_t LAND = 32 * D;
+  static_assert(!KV8 || 2 * LAND + D * kDecCols * 4 <= 2 * L::stageBytes, "fp8 stages and merge fit");
+  constexpr int NLD = KV8 ? NI8 : NI;
+  constexpr int NPER = 2 * NLD + (BIAS ? 4 : 0);  // vector-memory instructions per unit
   int32_t *prefix = reinterpret_cast<int32_t *>(smem + L::prefixOff);
   bal_prefix(p, prefix, reinterpret_cast<int32_t *>(smem + L::mlOff), p.Hkv);
 
@@ -1590,17 +1689,37 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
     b_it = __builtin_amdgcn_readfirstlane(lo);
   }
 
-  const uint32_t slot_bytes = (uint32_t)Hkv * D * 2;
-  uint32_t gk[NI], gv[NI];
+  const uint32_t slot_bytes = (uint32_t)Hkv * D * (KV8 ? 1 : 2);
+  uint32_t gk[NLD], gv[NLD];
 #pragma unroll
-  for (int n = 0; n < NI; ++n) {
-    const int r = RPI * n + lane / UNITS, pu = lane % UNITS;
-    gk[n] = r * slot_bytes + ((pu ^ swz_k<D>(r)) << 4);
-    gv[n] = r * slot_bytes + ((pu ^ swz_vt<D>(r)) << 4);
+  for (int n = 0; n < NLD; ++n) {
+    if constexpr (KV8) {
+      const int r = RPI8 * n + lane / U8, pu = lane % U8;
+      gk[n] = r * slot_bytes + ((pu ^ (r & (U8 - 1))) << 4);
+      gv[n] = r * slot_bytes + (pu << 4);
+    } else {
+      const int r = RPI * n + lane / UNITS, pu = lane % UNITS;
+      gk[n] = r * slot_bytes + ((pu ^ swz_k<D>(r)) << 4);
+      gv[n] = r * slot_bytes + ((pu ^ swz_vt<D>(r)) << 4);
+    }
   }
   uint32_t lk_off[QK], lv_off[DB];
 #pragma unroll
-  for (int ks = 0; ks < QK; ++ks) lk_off[ks] = c16 * ROWB + (((4 * ks + q) ^ swz_k<D>(c16)) << 4);
+  for (int ks = 0; ks < QK; ++ks) {
+    if constexpr (KV8)
+      lk_off[ks] = c16 * D + (((2 * ks + (q >> 1)) ^ (c16 & (U8 - 1))) << 4) + 8 * (q & 1);
+    else
+      lk_off[ks] = c16 * ROWB + (((4 * ks + q) ^ swz_k<D>(c16)) << 4);
+  }
+  uint32_t v8_dst[KV8 ? 2 * NI8 : 1];
+  if constexpr (KV8) {
+#pragma unroll
+    for (int n = 0; n < NI8; ++n) {
+      const int r = RPI8 * n + lane / U8, pu = lane % U8;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) v8_dst[2 * n + e] = r * ROWB + (((2 * pu + e) ^ swz_vt<D>(r)) << 4);
+    }
+  }
   {
     const int i = (lane & 15) >> 2, t = lane & 3, row = 4 * q + i;
 #pragma unroll
@@ -1616,6 +1735,7 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
   const float c = p.scale_log2;
   const bool pos_scale = c > 0.f;
   const uint32_t bias_bytes = BIAS ? (uint32_t)p.num_tokens * (uint32_t)p.H * (uint32_t)p.R * 4u : 0u;
+  const float v_scale = KV8 ? p.v_scale : 1.f;
 
   // A piece: units [j0, j1) of pair (b, g) inside this workgroup's range,
   // with what its rows need (uniform fields, then the lane's column).
@@ -1689,8 +1809,8 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
     const int nvalid = __builtin_amdgcn_readfirstlane(min(max(P.kend - key0, 0), 16));
     const int slot0 = p.bs_shift >= 0 ? (key0 & (p.BS - 1)) : key0 % p.BS;
     const int64_t eoff = (((int64_t)page * p.BS + slot0) * Hkv + P.g) * D;
-    const auto rk = make_rsrc(p.k + eoff, (uint32_t)nvalid * slot_bytes);
-    const auto rv = make_rsrc(p.v + eoff, (uint32_t)nvalid * slot_bytes);
+    const auto rk = make_rsrc(reinterpret_cast<const char *>(p.k) + eoff * (KV8 ? 1 : 2), (uint32_t)nvalid * slot_bytes);
+    const auto rv = make_rsrc(reinterpret_cast<const char *>(p.v) + eoff * (KV8 ? 1 : 2), (uint32_t)nvalid * slot_bytes);
     if constexpr (BIAS) {
       // Raw logits of the lane's four keys (distance clamped into the row;
       // the band test in compute() discards what lies outside it), through
@@ -1705,31 +1825,58 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
                                                  (P.rel_base + (uint32_t)d) * 4u, 0, 0, 0);
       }
     }
-    char *st = smem + (w * 2 + slot) * L::stageBytes;
+    char *st = KV8 ? smem + w * 2 * L::stageBytes + slot * LAND : smem + (w * 2 + slot) * L::stageBytes;
+    constexpr int VHALF = KV8 ? 16 * D : L::halfBytes;
 #pragma unroll
-    for (int n = 0; n < NI; ++n)
+    for (int n = 0; n < NLD; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void *)(st + n * 1024), 16,
                                                gk[n], 0, 0, 0);
 #pragma unroll
-    for (int n = 0; n < NI; ++n)
+    for (int n = 0; n < NLD; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void *)(st + L::halfBytes + n * 1024), 16, gv[n], 0, 0, 0);
+          rv, (__attribute__((address_space(3))) void *)(st + VHALF + n * 1024), 16, gv[n], 0, 0, 0);
   };
 
   f32x4 oacc[DB];
   float m_run, l_run;
   auto compute = [&](const Piece &P, int k, int slot, const bf16x8 (&qf)[QK]) __attribute__((always_inline)) {
     const int key0 = __builtin_amdgcn_readfirstlane(key_of(P, k));
-    const uint32_t st = lds_wave + slot * L::stageBytes;
     u32x4 kf[QK];
-#pragma unroll
-    for (int ks = 0; ks < QK; ++ks) kf[ks] = lds_read_b128_asm(st + lk_off[ks]);
     u32x2 va[DB];
+    if constexpr (KV8) {
+      const uint32_t land = lds_wave + slot * LAND;
+      const uint32_t vst = lds_wave + 2 * LAND;
+      u32x2 k8[QK];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) va[db] = lds_read_tr_at(st + lv_off[db]);
-    // LDS reads complete in order: the K operands are in once at most the
-    // DB V reads issued after them are outstanding.
-    lgkm_wait_n<DB>(kf);
+      for (int ks = 0; ks < QK; ++ks) k8[ks] = lds_read_b64_asm(land + lk_off[ks]);
+      u32x4 v8[NI8];
+#pragma unroll
+      for (int n = 0; n < NI8; ++n) v8[n] = lds_read_b128_asm(land + 16 * D + n * 1024 + 16 * lane);
+      lgkm_wait_n<0>(v8);
+      lgkm_wait_n<0>(k8);
+      if constexpr (NI8 == 2) {
+        const uint32_t a[4] = {vst + v8_dst[0], vst + v8_dst[1], vst + v8_dst[2], vst + v8_dst[3]};
+        const u32x4 vv[4] = {e4m3x8_to_bf16(v8[0][0], v8[0][1]), e4m3x8_to_bf16(v8[0][2], v8[0][3]),
+                             e4m3x8_to_bf16(v8[1][0], v8[1][1]), e4m3x8_to_bf16(v8[1][2], v8[1][3])};
+        lds_write_b128x4_now(a, vv);
+      } else {
+        lds_write_b128x2_now(vst + v8_dst[0], vst + v8_dst[1], e4m3x8_to_bf16(v8[0][0], v8[0][1]),
+                             e4m3x8_to_bf16(v8[0][2], v8[0][3]));
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) va[db] = lds_read_tr_at(vst - L::halfBytes + lv_off[db]);
+#pragma unroll
+      for (int ks = 0; ks < QK; ++ks) kf[ks] = e4m3x8_to_bf16(k8[ks][0], k8[ks][1]);
+    } else {
+      const uint32_t st = lds_wave + slot * L::stageBytes;
+#pragma unroll
+      for (int ks = 0; ks < QK; ++ks) kf[ks] = lds_read_b128_asm(st + lk_off[ks]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) va[db] = lds_read_tr_at(st + lv_off[db]);
+      // LDS reads complete in order: the K operands are in once at most the
+      // DB V reads issued after them are outstanding.
+      lgkm_wait_n<DB>(kf);
+    }
     f32x4 sacc = f32x4{};
 #pragma unroll
     for (int ks = 0; ks < QK; ++ks) sacc = mfma16(as_bf16x8(kf[ks]), qf[ks], sacc);
@@ -1843,7 +1990,7 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
       const float l_col = xor32_sum(xor16_sum(l_run));
       const int rs = pslot == 0 ? 1 : 0;
       {
-        const uint32_t red = lds_wave + rs * L::stageBytes;
+        const uint32_t red = KV8 ? lds_wave + 2 * LAND : lds_wave + rs * L::stageBytes;
 #pragma unroll
         for (int d4 = 0; d4 < DB; d4 += 4) {
           uint32_t a[4];
@@ -1882,14 +2029,16 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
             sc[ww] = m_w == neg_inf() ? 0.f : exp2_fast(m_w - M);
             Lsum += sc[ww] * __builtin_bit_cast(float, lw[ww]);
           }
-          const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+          const float inv = Lsum > 0.f ? (KV8 ? v_scale / Lsum : 1.f / Lsum) : 0.f;
           const float lse_v = Lsum > 0.f ? (M + log2_fast(Lsum)) * kLn2 : neg_inf();
           // O^T of wave ww, head_dim d, column fc sits at float
           // ((d / 4) * 16 + fc) * 4 + d % 4 of its merge stage.
           uint32_t oaddr[NW];
 #pragma unroll
           for (int ww = 0; ww < NW; ++ww)
-            oaddr[ww] = smem_u + (uint32_t)((ww * 2 + (int)sl[ww]) * L::stageBytes) +
+            oaddr[ww] = smem_u +
+                        (KV8 ? (uint32_t)(ww * 2 * L::stageBytes) + 2 * LAND
+                             : (uint32_t)((ww * 2 + (int)sl[ww]) * L::stageBytes)) +
                         ((((fg * DPG) >> 2) * kDecCols + fc) * 4 + ((fg * DPG) & 3)) * 4;
           float o[DPG];
           if constexpr (DPG == 4) {
@@ -1973,10 +2122,10 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
   }
 }
 
-template <int D, bool BIAS>
+template <int D, bool BIAS, bool KV8>
 __global__ __launch_bounds__(64 * kBalWaves, 1) void decode_balanced_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char smem[BalLds<D>::bytes];
-  decode_balanced<D, BIAS>(p, smem);
+  decode_balanced<D, BIAS, KV8>(p, smem);
 }
 
 // Merges the pieces of the pair recorded by decode workgroup blockIdx.x /
@@ -2766,14 +2915,21 @@ hipError_t launch_attention(const AttnParams &p, int head_dim, int64_t n_items_u
   const int64_t blocks = n_items_ub * p.Hkv * p.S;
   if (blocks <= 0) return hipSuccess;
   const dim3 grid((unsigned)blocks);
-  if (decode_only) {
-    const dim3 block(64 * attn_waves<true>());
-    if (head_dim == 128) hipLaunchKernelGGL((attn_kernel<128, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((attn_kernel<64, true>), grid, block, 0, stream, p);
+  auto go = [&](auto d_tag, auto dec_tag, auto k_tag) {
+    const dim3 block(64 * attn_waves<decltype(dec_tag)::value>());
+    hipLaunchKernelGGL((attn_kernel<decltype(d_tag)::value, decltype(dec_tag)::value, decltype(k_tag)::value>),
+                       grid, block, 0, stream, p);
+  };
+  using D128 = std::integral_constant<int, 128>;
+  using D64 = std::integral_constant<int, 64>;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (head_dim == 128) {
+    if (decode_only) p.kv8 ? go(D128{}, T_{}, T_{}) : go(D128{}, T_{}, F_{});
+    else p.kv8 ? go(D128{}, F_{}, T_{}) : go(D128{}, F_{}, F_{});
   } else {
-    const dim3 block(64 * attn_waves<false>());
-    if (head_dim == 128) hipLaunchKernelGGL((attn_kernel<128, false>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((attn_kernel<64, false>), grid, block, 0, stream, p);
+    if (decode_only) p.kv8 ? go(D64{}, T_{}, T_{}) : go(D64{}, T_{}, F_{});
+    else p.kv8 ? go(D64{}, F_{}, T_{}) : go(D64{}, F_{}, F_{});
   }
   return hipGetLastError();
 }
@@ -2804,14 +2960,22 @@ hipError_t launch_balanced_decode(const AttnParams &p, int head_dim, hipStream_t
     }
     return hipGetLastError();
   }
-  if (p.kv8) return hipErrorNotSupported;  // E4M3 caches: eight kv heads only
+  auto pairs = [&](auto d_tag, auto b_tag, auto k_tag) {
+    hipLaunchKernelGGL((decode_balanced_kernel<decltype(d_tag)::value, decltype(b_tag)::value,
+                                               decltype(k_tag)::value>),
+                       grid, block, 0, stream, p);
+  };
+  using D128 = std::integral_constant<int, 128>;
+  using D64 = std::integral_constant<int, 64>;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
   if (head_dim == 128) {
-    if (bias) hipLaunchKernelGGL((decode_balanced_kernel<128, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((decode_balanced_kernel<128, false>), grid, block, 0, stream, p);
+    if (p.kv8) bias ? pairs(D128{}, T_{}, T_{}) : pairs(D128{}, F_{}, T_{});
+    else bias ? pairs(D128{}, T_{}, F_{}) : pairs(D128{}, F_{}, F_{});
     hipLaunchKernelGGL((combine_balanced_kernel<128>), cgrid, cblock, 0, stream, p);
   } else {
-    if (bias) hipLaunchKernelGGL((decode_balanced_kernel<64, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((decode_balanced_kernel<64, false>), grid, block, 0, stream, p);
+    if (p.kv8) bias ? pairs(D64{}, T_{}, T_{}) : pairs(D64{}, F_{}, T_{});
+    else bias ? pairs(D64{}, T_{}, F_{}) : pairs(D64{}, F_{}, F_{});
     hipLaunchKernelGGL((combine_balanced_kernel<64>), cgrid, cblock, 0, stream, p);
   }
   return hipGetLastError();

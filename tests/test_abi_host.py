@@ -170,17 +170,16 @@ def test_fp8_attention_rejects_bad_scales(L, ks, vs):
     assert _attn8(L, ks, vs) == SHAPE
 
 
-@pytest.mark.parametrize("kw", [dict(S=1), dict(S=4, wsb=1 << 30), dict(Hkv=4, H=32),
-                                dict(maxq=40), dict(T=40, B=2, maxq=20)])
-def test_fp8_attention_outside_its_path_is_unsupported(L, kw):
-    # Only the balanced decode with eight kv heads reads E4M3 caches.
-    assert _attn8(L, **kw) == UNSUP
-
-
 def test_fp8_attention_argument_errors(L):
+    # The same validation as the bf16 entry point, before any HIP call.
     assert _attn8(L, k=None) == NULL
+    assert _attn8(L, v=None) == NULL
+    assert _attn8(L, R=4, rel=None) == NULL
     assert _attn8(L, D=96) == UNSUP
+    assert _attn8(L, BS=24) == UNSUP
+    assert _attn8(L, H=12, Hkv=8) == SHAPE
     assert _attn8(L, ws=None) == WS
+    assert _attn8(L, S=4, ws=None) == WS
     assert _attn8(L, T=0, B=0, q=None, out=None) == OK
 
 

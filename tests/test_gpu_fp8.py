@@ -124,14 +124,33 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_fp8_attention_matches_oracle(name):
+CASES.update({
+    # other kv-head counts (balanced decode of one (request, kv head) pair per unit)
+    "gqa4_d128": ([1] * 7, [1, 17, 300, 1024, 2500, 64, 999], 8, 2, 128, 64, 1 / 32, 1 / 16, (-1, -1)),
+    "mha_d64": ([1] * 3, [33, 700, 129], 4, 4, 64, 16, 0.05, 0.2, (-1, -1)),
+    # prefill chunks and mixed batches (split mode: prefill tiles and decode items)
+    "prefill_d128": ([300, 77, 129], [900, 77, 1500], 16, 8, 128, 256, 1 / 32, 1 / 16, (-1, -1)),
+    "prefill_d64_gqa2": ([64, 200], [64, 333], 4, 2, 64, 40, 0.05, 0.2, (-1, -1)),
+    "mixed_window": ([1, 130, 1, 40, 1], [2000, 500, 70, 3000, 1], 16, 2, 128, 100, 1 / 32, 1 / 16, (127, 0)),
+    "prefill_nobias_mha": ([100, 3], [400, 3], 4, 4, 128, 0, 0.1, 0.1, (-1, -1)),
+})
+
+# Split counts per case: 0 (balanced when it applies, else 1) always, and
+# explicit splits for a few.
+SPLITS = {name: [0] for name in CASES}
+SPLITS.update({"ragged_d128": [0, 1, 3], "gqa4_d128": [0, 4], "prefill_d128": [1, 2], "mixed_window": [1, 3],
+               "two_tokens_g8": [0, 2]})
+PARAMS = [(n, S) for n in CASES for S in SPLITS[n]]
+
+
+@pytest.mark.parametrize("name,S", PARAMS)
+def test_fp8_attention_matches_oracle(name, S):
     ql, kl, H, Hkv, D, R, ks, vs, win = CASES[name]
     w, k8, v8 = _fp8_workload(ql, kl, H, Hkv, D, R, ks, vs, seed=21, window=win, extra_pages=3)
     ref_out, ref_lse = ofp8.attention_fp8(w.q, k8, v8, ks, vs, w.block_table, w.cache_seqlens, w.cu_seqlens_q,
                                           w.softmax_scale, w.causal, w.window_size, w.rel_extent, w.rel_logits)
-    out, lse = _run_fp8(w, k8, v8, ks, vs)
-    _compare(out, lse, ref_out, ref_lse, name)
+    out, lse = _run_fp8(w, k8, v8, ks, vs, S=S)
+    _compare(out, lse, ref_out, ref_lse, f"{name} S={S}")
 
 
 def test_fp8_attention_is_repeatable_and_page_invariant():
@@ -153,13 +172,31 @@ def test_fp8_attention_is_repeatable_and_page_invariant():
     assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
 
 
-def test_fp8_attention_unsupported_paths_raise():
-    w, k8, v8 = _fp8_workload([1, 1], [100, 200], 8, 2, 128, 0, 0.1, 0.1, seed=23)
-    with pytest.raises(bnd.RpaError):
-        _run_fp8(w, k8, v8, 0.1, 0.1)
+def test_fp8_bad_scales_raise():
     w, k8, v8 = _fp8_workload([1, 1], [100, 200], 32, 8, 128, 0, 0.1, 0.1, seed=23)
-    with pytest.raises(bnd.RpaError):
-        _run_fp8(w, k8, v8, 0.1, 0.1, S=2)
+    for ks, vs in ((0.0, 0.1), (0.1, -1.0), (float("nan"), 0.1)):
+        with pytest.raises(bnd.RpaError):
+            _run_fp8(w, k8, v8, ks, vs)
+
+
+def test_fp8_chunked_prefill_full_size_sampled():
+    """The 8-request chunked prefill (H=32, Hkv=8, D=128, R=256) over E4M3
+    caches, one split as the benchmark runs it; two requests' tokens (a
+    sample of 64 rows each) checked against the oracle."""
+    w = wl.chunked_prefill()
+    ks, vs = 1 / 32, 1 / 16
+    k8 = (w.key_cache.float() / ks).to(torch.float8_e4m3fn).view(torch.uint8)
+    v8 = (w.value_cache.float() / vs).to(torch.float8_e4m3fn).view(torch.uint8)
+    out, lse = _run_fp8(w, k8, v8, ks, vs, S=1)
+    reqs = [2, 6]
+    sub, sk8, sv8, qi = _subset(w, k8, v8, reqs)
+    g = torch.Generator().manual_seed(3)
+    local = sorted(torch.randperm(sub.num_tokens, generator=g)[:128].tolist())
+    ref_out, ref_lse = ofp8.attention_fp8(sub.q, sk8, sv8, ks, vs, sub.block_table, sub.cache_seqlens,
+                                          sub.cu_seqlens_q, sub.softmax_scale, sub.causal, sub.window_size,
+                                          sub.rel_extent, sub.rel_logits, tokens=local)
+    li = torch.tensor(local, dtype=torch.long)
+    _compare(out[qi][li], lse[qi][li], ref_out[li], ref_lse[li], "chunked_prefill fp8")
 
 
 def _subset(w, k8, v8, reqs):
