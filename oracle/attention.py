@@ -42,6 +42,13 @@ listed in the design notes):
   R9 kv head of q head h is h // (H / Hkv) ([V1-ATTN] 附录DD).
   R10 cache_seqlens includes this step's query tokens; only the first
      ceil(Lk / BS) block_table entries are read.
+  R11 ALiBi (optional, alibi_slopes fp32 [H]): the logit of key t gains
+     slope_h * (t - q_abs), added like the relative bias after scaling
+     ([V1-ATTN] FlexAttention chapter, score_modify example 1: scores plus
+     slopes times (k_pos - q_pos)).  [PA-V2]'s decode adds slopes times the
+     absolute key position instead, which shifts each row by slope_h * q_abs:
+     the same softmax, an LSE larger by that shift; the relative form is
+     taken.
 """
 from __future__ import annotations
 
@@ -52,7 +59,7 @@ import torch
 
 __all__ = [
     "page_walk", "cu_seqlens_from_lengths", "query_positions", "visible_mask",
-    "bias_matrix", "attention", "attention_split_partials", "combine",
+    "bias_matrix", "alibi_matrix", "attention", "attention_split_partials", "combine",
 ]
 
 _F64 = torch.float64
@@ -125,6 +132,14 @@ def bias_matrix(rel_rows: torch.Tensor, qa: torch.Tensor, k_len: int, rel_extent
     return torch.where(band, vals, torch.zeros((), dtype=_F64))
 
 
+def alibi_matrix(slope: float, qa: torch.Tensor, k_len: int) -> torch.Tensor:
+    """[n, k_len] ALiBi bias of one head: slope * (t - q_abs) (R11), with the
+    slope taken as its fp32 value."""
+    sl = float(torch.tensor(slope, dtype=torch.float32).item())
+    t = torch.arange(int(k_len), dtype=_F64)[None, :]
+    return sl * (t - qa.to(_F64)[:, None])
+
+
 def _gather_head(cache: torch.Tensor, pages: list, g: int, k_len: int) -> torch.Tensor:
     """K_b[t] = cache[pages[t // BS], t % BS, g, :] for t < k_len, as fp64."""
     if k_len == 0:
@@ -162,18 +177,21 @@ def _iter_requests(cu_seqlens_q, cache_seqlens):
         yield b, cu[b], cu[b + 1] - cu[b], lk[b]
 
 
-def _scores(q, K, h, rows_tok, qa, k_len, rel_logits, rel_extent, scale, vis):
-    """Scaled, biased, masked logits of q head h for the given rows (R2)."""
+def _scores(q, K, h, rows_tok, qa, k_len, rel_logits, rel_extent, scale, vis, alibi_slopes=None):
+    """Scaled, biased, masked logits of q head h for the given rows (R2, R11)."""
     Q = q[rows_tok, h, :].to(_F64)
     S = (Q @ K.T) * scale
     if rel_extent > 0 and rel_logits is not None:
         S = S + bias_matrix(rel_logits[rows_tok, h, :], qa, k_len, rel_extent)
+    if alibi_slopes is not None:
+        S = S + alibi_matrix(float(alibi_slopes[h]), qa, k_len)
     return torch.where(vis, S, torch.full((), -math.inf, dtype=_F64))
 
 
 def attention(q, key_cache, value_cache, block_table, cache_seqlens, cu_seqlens_q, softmax_scale,
               causal=True, window_size=(-1, -1), rel_extent=0, rel_logits=None, *,
-              tokens: Optional[Iterable[int]] = None, heads: Optional[Iterable[int]] = None):
+              tokens: Optional[Iterable[int]] = None, heads: Optional[Iterable[int]] = None,
+              alibi_slopes=None):
     """out [T, H, D] fp64 and lse [T, H] fp64 of the whole method.
 
     For request b with query rows i (packed token tok = cu[b] + i) and q head
@@ -214,7 +232,7 @@ def attention(q, key_cache, value_cache, block_table, cache_seqlens, cu_seqlens_
             for h in head_list:
                 if h // G != g:
                     continue
-                S = _scores(q, K, h, rows_tok, qa, lk, rel_logits, rel_extent, scale, vis)
+                S = _scores(q, K, h, rows_tok, qa, lk, rel_logits, rel_extent, scale, vis, alibi_slopes)
                 o, l = _softmax_rows(S, V)
                 out[rows_tok, h, :] = o
                 lse[rows_tok, h] = l

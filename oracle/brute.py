@@ -18,7 +18,7 @@ def _to_lists(x):
 
 
 def attention(q, key_cache, value_cache, block_table, cache_seqlens, cu_seqlens_q, softmax_scale,
-              causal=True, window_size=(-1, -1), rel_extent=0, rel_logits=None):
+              causal=True, window_size=(-1, -1), rel_extent=0, rel_logits=None, alibi_slopes=None):
     """Nested lists out[T][H][D], lse[T][H] (floats).  Keep inputs tiny."""
     import torch  # only to read tensors; all arithmetic below is scalar Python
     qf = _to_lists(torch.as_tensor(q).double())
@@ -29,6 +29,7 @@ def attention(q, key_cache, value_cache, block_table, cache_seqlens, cu_seqlens_
     cu = [int(x) for x in _to_lists(torch.as_tensor(cu_seqlens_q))]
     rl = None if rel_logits is None else _to_lists(torch.as_tensor(rel_logits).double())
     scale = float(torch.tensor(softmax_scale, dtype=torch.float32).item())
+    slopes = None if alibi_slopes is None else _to_lists(torch.as_tensor(alibi_slopes, dtype=torch.float32).double())
     T = len(qf)
     H = len(qf[0]) if T else 0
     D = len(qf[0][0]) if T else 0
@@ -66,6 +67,8 @@ def attention(q, key_cache, value_cache, block_table, cache_seqlens, cu_seqlens_
                         rel_idx = rel_idx if rel_idx < rel_extent else rel_extent - 1
                         if rel_dist == rel_idx:
                             s += rl[tok][h][rel_idx]
+                    if slopes is not None:
+                        s += slopes[h] * (t - pos)  # ALiBi: slope times (key position - query position)
                     logits.append(s)
                     values.append(vf[page][slot][kvh])
                 if not logits:
