@@ -424,8 +424,8 @@ def test_planted_mistakes_are_caught(monkeypatch, mistake):
     if mistake == "scaled_bias":
         real_scores = orc._scores
 
-        def scores(q, K, h, rows_tok, qa, k_len, rel, R, scale, vis):
-            S = real_scores(q, K, h, rows_tok, qa, k_len, None, 0, scale, vis)
+        def scores(q, K, h, rows_tok, qa, k_len, rel, R, scale, vis, alibi_slopes=None):
+            S = real_scores(q, K, h, rows_tok, qa, k_len, None, 0, scale, vis, alibi_slopes)
             if R > 0 and rel is not None:
                 S = S + scale * real_bias(rel[rows_tok, h, :], qa, k_len, R)
             return torch.where(vis, S, torch.full((), -math.inf, dtype=torch.float64))
