@@ -91,6 +91,8 @@ class Runner:
         for _ in range(pools - 1):
             self.kv.append((w.key_cache.clone(), w.value_cache.clone()))
 
+    alibi = None  # fp32 [H] ALiBi slopes on the device, or None
+
     def call(self, i=0):
         w = self.w
         k, v = self.kv[i % len(self.kv)]
@@ -98,7 +100,8 @@ class Runner:
             w.q, k, v, block_table=w.block_table, cache_seqlens=w.cache_seqlens,
             cu_seqlens_q=w.cu_seqlens_q, max_seqlen_q=w.max_seqlen_q, softmax_scale=w.softmax_scale,
             causal=w.causal, window_size=w.window_size, rel_extent=w.rel_extent,
-            rel_logits=w.rel_logits, num_splits=self.S, out=self.out, lse=self.lse, workspace=self.ws)
+            rel_logits=w.rel_logits, num_splits=self.S, out=self.out, lse=self.lse, workspace=self.ws,
+            alibi_slopes=self.alibi)
 
     def combine_only(self, i=0):
         """The split combine alone, on partial buffers of this call's shape."""
@@ -272,7 +275,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None, help="run one workload: batched_decode, chunked_prefill, "
                                                   "long_decode, continuous_batch, batched_decode_fp8, "
-                                                  "chunked_prefill_fp8, long_decode_fp8, kv_write")
+                                                  "chunked_prefill_fp8, long_decode_fp8, batched_decode_alibi, "
+                                                  "chunked_prefill_alibi, kv_write")
     ap.add_argument("--splits", type=int, default=None,
                     help="override the planner's num_splits (0 = balanced decode) for the headline decode batch "
                          "(or for long_decode with --only long_decode)")
@@ -388,6 +392,21 @@ def main(argv=None):
             log(f"long_decode_fp8: {ms * 1e3:.1f} us/step, {wk['bytes'] / ms / 1e6:.1f} GB/s")
             del r7, w7
             torch.cuda.empty_cache()
+        for name, make, S_a in (("batched_decode_alibi", wl.batched_decode, 0),
+                                ("chunked_prefill_alibi", wl.chunked_prefill, 1)):
+            if a.only not in (None, name):
+                continue
+            wa = make(device="cpu").to(dev)
+            ra = Runner(wa, S_a, pools=3 if S_a == 0 else 1)
+            H = wa.num_heads
+            ra.alibi = torch.tensor([2.0 ** (-8.0 * (i + 1) / H) for i in range(H)], dtype=torch.float32,
+                                    device=dev)
+            ms, ms_c, wk = measure(ra, max(5, a.steps // 2), a.warmup, SETTLE_S)
+            results[name] = (wa, S_a, ms, ms_c, wk)
+            log(f"{name}: {ms * 1e3:.1f} us/step, {wk['bytes'] / ms / 1e6:.1f} GB/s, "
+                f"{wk['flops'] / ms / 1e9:.1f} TFLOP/s")
+            del ra, wa
+            torch.cuda.empty_cache()
         if a.only in (None, "kv_write"):
             try:
                 ms_kv, kvinfo = measure_kv_write(max(5, a.steps // 2), a.warmup)
@@ -402,6 +421,8 @@ def main(argv=None):
     def summary(name):
         w, S, ms, ms_c, wk = results[name]
         extra = {}
+        if name.endswith("_alibi"):
+            extra = {"alibi_slopes": "2^(-8 (h + 1) / H)"}
         if name.endswith("_fp8"):
             kern = ("attn_kernel<128, false, true>" if S == 1 else
                     "decode_heads_kernel<128, true, true> + combine_heads_kernel<128>")
@@ -422,7 +443,7 @@ def main(argv=None):
     head = a.only if a.only else "batched_decode"
     w, S, ms, ms_c, wk = results[head]
     kernel_ms = ms - ms_c
-    prefill_like = head in ("chunked_prefill", "chunked_prefill_fp8")
+    prefill_like = head.startswith("chunked_prefill")
     if prefill_like:
         achieved = wk["flops"] / kernel_ms / 1e9
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,

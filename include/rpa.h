@@ -239,6 +239,36 @@ int rpa_attn_varlen_fp8(const void *q, const void *key_cache, const void *value_
                         void *out, float *lse, void *stream);
 
 /*
+ * rpa_attn_varlen_ex: rpa_attn_varlen with every option of the path.
+ *
+ *   kv_e4m3        0: bf16 caches (k_scale, v_scale ignored); nonzero: E4M3
+ *                  caches with k_scale, v_scale as for rpa_attn_varlen_fp8.
+ *   alibi_slopes   NULL, or fp32 [num_heads] device array: the logit of key t
+ *                  for a row at position qa of q head h gains
+ *                  alibi_slopes[h] * (t - qa), added like the relative bias
+ *                  (after softmax_scale; not scaled by it, nor by k_scale).
+ *                  This is the ALiBi example of the FlexAttention chapter of
+ *                  "vLLM V1 Attention — Part 2" (scores plus slopes times
+ *                  (k_pos - q_pos)); the BI-V100 decode's form with the
+ *                  absolute key position gives the same output and an LSE
+ *                  larger by slope * qa.  Finite slopes of any sign; with
+ *                  slopes the prefill kernel carries the bias as bias / scale,
+ *                  so |slope * (t - qa)| must stay below 2^27 on visible keys.
+ * Every other argument is that of rpa_attn_varlen; rpa_attn_varlen and
+ * rpa_attn_varlen_fp8 are this call without slopes.
+ */
+int rpa_attn_varlen_ex(const void *q, const void *key_cache, const void *value_cache, int kv_e4m3,
+                       float k_scale, float v_scale, const int32_t *block_table, int32_t max_pages_per_seq,
+                       const int32_t *cache_seqlens, const int32_t *cu_seqlens_q,
+                       int32_t batch, int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                       int32_t max_seqlen_q, float softmax_scale, int causal,
+                       int32_t window_left, int32_t window_right,
+                       int32_t rel_extent, const float *rel_logits, const float *alibi_slopes,
+                       int32_t num_splits, void *workspace, size_t workspace_bytes,
+                       void *out, float *lse, void *stream);
+
+/*
  * rpa_kv_cache_write_fp8: rpa_kv_cache_write into E4M3 caches.  Element x of
  * a key row is stored as the code of y = x / k_scale (one IEEE fp32
  * division): the nearest E4M3 value, ties to the even code; |y| >= 448

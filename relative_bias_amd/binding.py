@@ -67,6 +67,10 @@ def lib():
     L.rpa_attn_varlen_fp8.restype = ctypes.c_int
     L.rpa_kv_cache_write_fp8.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, vp, vp, vp]
     L.rpa_kv_cache_write_fp8.restype = ctypes.c_int
+    L.rpa_attn_varlen_ex.argtypes = [vp, vp, vp, ctypes.c_int, f32, f32, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                     i32, i32, i32, f32, ctypes.c_int, i32, i32, i32, vp, vp, i32, vp, sz, vp, vp,
+                                     vp]
+    L.rpa_attn_varlen_ex.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -77,6 +81,16 @@ def _ptr(t: Optional[torch.Tensor]):
 
 def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _alibi(alibi_slopes, H: int, device):
+    if alibi_slopes is None:
+        return None
+    a = alibi_slopes.contiguous()
+    _check(a, "alibi_slopes", torch.float32, device, 1)
+    if a.shape[0] != H:
+        raise ValueError(f"alibi_slopes must have {H} entries, got {a.shape[0]}")
+    return a
 
 
 def _check(t: torch.Tensor, name: str, dtype, device, ndim=None):
@@ -112,8 +126,10 @@ def rpa_attn_varlen(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
                     rel_extent: int = 0, rel_logits: Optional[torch.Tensor] = None,
                     num_splits: Optional[int] = None, max_seqlen_k: Optional[int] = None,
                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                    return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
-    """Paged varlen causal attention with the additive relative bias.
+                    return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
+                    alibi_slopes: Optional[torch.Tensor] = None):
+    """Paged varlen causal attention with the additive relative bias (and
+    optional ALiBi slopes, fp32 [H], through rpa_attn_varlen_ex).
 
     Returns ``out`` (bf16 [T, H, D]), or ``(out, lse)`` when ``return_lse``
     or an ``lse`` tensor is given.  ``num_splits=None`` uses
@@ -162,13 +178,23 @@ def rpa_attn_varlen(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
     ws_bytes = rpa_workspace_bytes(S, T, H, D) if S != 1 else 0
     if ws_bytes and workspace is None:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
-    st = lib().rpa_attn_varlen(
-        _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(block_table), block_table.shape[1],
-        _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB, BS, int(max_seqlen_q),
-        float(softmax_scale), int(bool(causal)), int(window_size[0]), int(window_size[1]), R,
-        _ptr(rel_logits) if R > 0 else None, S, _ptr(workspace),
-        0 if workspace is None else workspace.numel() * workspace.element_size(),
-        _ptr(out), _ptr(lse), _stream(dev))
+    alibi = _alibi(alibi_slopes, H, dev)
+    if alibi is None:
+        st = lib().rpa_attn_varlen(
+            _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(block_table), block_table.shape[1],
+            _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB, BS, int(max_seqlen_q),
+            float(softmax_scale), int(bool(causal)), int(window_size[0]), int(window_size[1]), R,
+            _ptr(rel_logits) if R > 0 else None, S, _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _ptr(out), _ptr(lse), _stream(dev))
+    else:
+        st = lib().rpa_attn_varlen_ex(
+            _ptr(q), _ptr(key_cache), _ptr(value_cache), 0, 1.0, 1.0, _ptr(block_table), block_table.shape[1],
+            _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB, BS, int(max_seqlen_q),
+            float(softmax_scale), int(bool(causal)), int(window_size[0]), int(window_size[1]), R,
+            _ptr(rel_logits) if R > 0 else None, _ptr(alibi), S, _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _ptr(out), _ptr(lse), _stream(dev))
     if st != RPA_OK:
         raise RpaError(st, "rpa_attn_varlen")
     return (out, lse) if want_lse else out
@@ -189,7 +215,7 @@ def rpa_attn_varlen_fp8(q: torch.Tensor, key_cache: torch.Tensor, value_cache: t
                         rel_extent: int = 0, rel_logits: Optional[torch.Tensor] = None,
                         num_splits: int = 0, out: Optional[torch.Tensor] = None,
                         lse: Optional[torch.Tensor] = None, return_lse: bool = False,
-                        workspace: Optional[torch.Tensor] = None):
+                        workspace: Optional[torch.Tensor] = None, alibi_slopes: Optional[torch.Tensor] = None):
     """rpa_attn_varlen over E4M3 caches (uint8 codes or float8_e4m3fn) with
     per-cache scales: k = e4m3(code) * k_scale, v = e4m3(code) * v_scale."""
     dev = q.device
@@ -230,13 +256,23 @@ def rpa_attn_varlen_fp8(q: torch.Tensor, key_cache: torch.Tensor, value_cache: t
     ws_bytes = rpa_workspace_bytes(S, T, H, D) if S != 1 else 0
     if ws_bytes and workspace is None:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
-    st = lib().rpa_attn_varlen_fp8(
-        _ptr(q), _ptr(key_cache), _ptr(value_cache), float(k_scale), float(v_scale), _ptr(block_table),
-        block_table.shape[1], _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB, BS,
-        int(max_seqlen_q), float(softmax_scale), int(bool(causal)), int(window_size[0]), int(window_size[1]),
-        R, _ptr(rel_logits) if R > 0 else None, S, _ptr(workspace),
-        0 if workspace is None else workspace.numel() * workspace.element_size(),
-        _ptr(out), _ptr(lse), _stream(dev))
+    alibi = _alibi(alibi_slopes, H, dev)
+    if alibi is None:
+        st = lib().rpa_attn_varlen_fp8(
+            _ptr(q), _ptr(key_cache), _ptr(value_cache), float(k_scale), float(v_scale), _ptr(block_table),
+            block_table.shape[1], _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB, BS,
+            int(max_seqlen_q), float(softmax_scale), int(bool(causal)), int(window_size[0]), int(window_size[1]),
+            R, _ptr(rel_logits) if R > 0 else None, S, _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _ptr(out), _ptr(lse), _stream(dev))
+    else:
+        st = lib().rpa_attn_varlen_ex(
+            _ptr(q), _ptr(key_cache), _ptr(value_cache), 1, float(k_scale), float(v_scale), _ptr(block_table),
+            block_table.shape[1], _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB, BS,
+            int(max_seqlen_q), float(softmax_scale), int(bool(causal)), int(window_size[0]), int(window_size[1]),
+            R, _ptr(rel_logits) if R > 0 else None, _ptr(alibi), S, _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _ptr(out), _ptr(lse), _stream(dev))
     if st != RPA_OK:
         raise RpaError(st, "rpa_attn_varlen_fp8")
     return (out, lse) if want_lse else out
@@ -332,7 +368,7 @@ def rpa_kv_cache_write(key: torch.Tensor, value: torch.Tensor, slot_mapping: tor
 
 
 def attn_workload(w, *, num_splits: Optional[int] = None, return_lse: bool = True, out=None, lse=None,
-                  workspace=None):
+                  workspace=None, alibi_slopes=None):
     """Run rpa_attn_varlen on a relative_bias_amd.workloads.Workload (on the GPU)."""
     S = num_splits if num_splits is not None else w.num_splits
     return rpa_attn_varlen(
@@ -340,4 +376,4 @@ def attn_workload(w, *, num_splits: Optional[int] = None, return_lse: bool = Tru
         cu_seqlens_q=w.cu_seqlens_q, max_seqlen_q=w.max_seqlen_q, softmax_scale=w.softmax_scale,
         causal=w.causal, window_size=w.window_size, rel_extent=w.rel_extent, rel_logits=w.rel_logits,
         num_splits=S, max_seqlen_k=max(w.k_lens + [0]), return_lse=return_lse, out=out, lse=lse,
-        workspace=workspace)
+        workspace=workspace, alibi_slopes=alibi_slopes)

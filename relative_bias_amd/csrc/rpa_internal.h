@@ -51,6 +51,7 @@ struct AttnParams {
   float scale_log2;             // scale * log2(e)
   float v_scale;                // E4M3 caches: the value cache's scale (1 for bf16 caches)
   int32_t kv8;                  // 1: k / v are E4M3 codes (uint8) instead of bf16
+  const float *alibi;           // [H] ALiBi slopes, or null
 };
 
 struct CombineParams {

@@ -409,6 +409,7 @@ __device__ __forceinline__ void tile_bias_load(f32x16 *sacc, int kb, int qa, con
 // get the bias.
 struct TileBounds {
   int vis_lo, vis_hi, band_lo, band_hi;
+  float al0, al_s;  // ALiBi in raw score units: al0 + al_s * offset (0 and 0 without ALiBi)
 };
 
 // Initial value of the score accumulator of a general tile (a mask edge or
@@ -455,11 +456,21 @@ __device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t a, uint32_t 
 // need only one of the two masks measured no faster with a form of their
 // own, which costs registers.)
 enum { kInitEdge, kInitBand, kInitFull };
+// Key offset (without the 4 hf shift) of accumulator element (kb2, j).
+__device__ __forceinline__ constexpr int offset_of(int kb2, int j) { return 32 * kb2 + 8 * (j >> 2) + 3 - (j & 3); }
+
 template <int MODE>
-__device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv_scale, float masked) {
+__device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv_scale, float masked,
+                                          bool alibi = false) {
   if constexpr (MODE == kInitFull) {
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) sacc[kb2] *= inv_scale;
+    if (alibi) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sacc[kb2][j] += __builtin_fmaf(tb.al_s, (float)offset_of(kb2, j), tb.al0);
+    }
     return;
   }
   constexpr bool USE_VIS = true;
@@ -467,6 +478,21 @@ __device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv
   const uint32_t vis = USE_VIS ? range_bits(tb.vis_lo, tb.vis_hi) : 0u;
   const uint32_t band = USE_BAND ? range_bits(tb.band_lo, tb.band_hi) : 0u;
   const uint32_t mbits = __float_as_uint(masked);
+  if (alibi) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int pos = order_of(kb2, j);
+        uint32_t v = 0u;
+        if constexpr (MODE != kInitEdge) v = __float_as_uint(sacc[kb2][j] * inv_scale);
+        if constexpr (USE_BAND) v &= bit_mask(band, pos);
+        const float f = __uint_as_float(v) + __builtin_fmaf(tb.al_s, (float)offset_of(kb2, j), tb.al0);
+        sacc[kb2][j] = __uint_as_float(bit_select(bit_mask(vis, pos), __float_as_uint(f), mbits));
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
@@ -665,7 +691,7 @@ __device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32
   return fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
 }
 
-template <int D, bool KV8>
+template <int D, bool KV8, bool ALIBI>
 __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, char *smem) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
@@ -735,6 +761,9 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   const float c = zero_scale ? kLog2e : fabsf(p.scale_log2);
   const float inv_scale = zero_scale ? 1.f : 1.f / fabsf(p.scale);
   const float masked = neg_inf();
+  // ALiBi enters the accumulator like the bias: slope * (t - qa) / scale.
+  constexpr bool alibi = ALIBI;
+  const float al_s = alibi ? p.alibi[head] * inv_scale : 0.f;
 
   bf16x8 qf[KSTEPS];
   {
@@ -870,14 +899,14 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   };
 
   auto is_band = [&](int kb) { return p.R > 0 && kb <= band_hi && kb + kTileKeys - 1 >= band_lo; };
-  auto is_plain = [&](int kb) { return kb >= in_lo && kb + kTileKeys - 1 <= in_hi && !is_band(kb); };
+  auto is_plain = [&](int kb) { return !alibi && kb >= in_lo && kb + kTileKeys - 1 <= in_hi && !is_band(kb); };
   // Every key of the tile visible to, and in the band of, every row.
   const int full_lo = __builtin_amdgcn_readfirstlane(max(in_lo, qa_max - p.R + 1));
   const int full_hi = __builtin_amdgcn_readfirstlane(min(in_hi, qa_min));
   auto is_full_band = [&](int kb) { return kb >= full_lo && kb + kTileKeys - 1 <= full_hi; };
   auto bounds = [&](int kb) {
     const int off = kb + 4 * hf;
-    return TileBounds{lo_r - off, hi_r - off, qa - p.R + 1 - off, qa - off};
+    return TileBounds{lo_r - off, hi_r - off, qa - p.R + 1 - off, qa - off, al_s * (float)(off - qa), al_s};
   };
   // Lazy max update after the row max mx of a tile: O and l are rescaled
   // only when some row's max grew by more than kTau.
@@ -898,12 +927,12 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   // those loads have landed (band tiles only).
   auto begin = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
     if (is_band(kb)) load_bias(sacc, kb);
-    else if (!is_plain(kb)) tile_init<kInitEdge>(sacc, bounds(kb), inv_scale, masked);
+    else if (!is_plain(kb)) tile_init<kInitEdge>(sacc, bounds(kb), inv_scale, masked, alibi);
   };
   auto finish = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
     if (is_band(kb)) {
-      if (is_full_band(kb)) tile_init<kInitFull>(sacc, bounds(kb), inv_scale, masked);
-      else tile_init<kInitBand>(sacc, bounds(kb), inv_scale, masked);
+      if (is_full_band(kb)) tile_init<kInitFull>(sacc, bounds(kb), inv_scale, masked, alibi);
+      else tile_init<kInitBand>(sacc, bounds(kb), inv_scale, masked, alibi);
     }
   };
   auto zero = [&](f32x16 *sacc) __attribute__((always_inline)) {
@@ -1027,7 +1056,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       // Masks of an edge tile j+2 in the released set, then the barrier that
       // publishes K(j+2) and V(j+1).  Raw bias loads may stay in flight.
       if (!band2 && j + 2 < nt && !is_plain(tile_kb(j + 2)))
-        tile_init<kInitEdge>(cur, bounds(tile_kb(j + 2)), inv_scale, masked);
+        tile_init<kInitEdge>(cur, bounds(tile_kb(j + 2)), inv_scale, masked, alibi);
       __builtin_amdgcn_sched_barrier(0);
       if (!band2) wait_vm0();
       else if (bias_fast) wait_vm8();
@@ -1160,6 +1189,8 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
   const float *rel_row = p.R > 0 ? p.rel_logits + ((int64_t)tok * p.H + head) * p.R : nullptr;
   const float c = p.scale_log2;
   const bool pos_scale = c > 0.f;
+  const bool alibi = p.alibi != nullptr;
+  const float al = alibi ? p.alibi[head] * kLog2e : 0.f;
 
   bf16x8 qf[QK];
   {
@@ -1293,6 +1324,7 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
           if constexpr (BIAS) {
             const int d = qa - t;
             v = __builtin_fmaf((unsigned)d < (unsigned)p.R ? rel_row[d] : 0.f, kLog2e, v);
+            if (alibi) v = __builtin_fmaf(al, (float)(t - qa), v);
           }
           if constexpr (MASK) {
             if (t < lo_c || t > hi_c) v = neg_inf();
@@ -1333,7 +1365,7 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
 
   auto step = [&](DecodeRegs<D, KV8> &Rg, int base, int nbase, bool has_next) {
     const bool interior = base >= in_lo && base + kDecWaveKeys - 1 <= in_hi;
-    const bool bias = p.R > 0 && base <= band_hi && base + kDecWaveKeys - 1 >= band_lo;
+    const bool bias = (p.R > 0 && base <= band_hi && base + kDecWaveKeys - 1 >= band_lo) || alibi;
     if (interior && !bias) compute(Rg, base, nbase, has_next, BoolTag<false>{}, BoolTag<false>{});
     else compute(Rg, base, nbase, has_next, BoolTag<true>{}, BoolTag<true>{});
   };
@@ -1460,7 +1492,9 @@ constexpr int attn_lds_bytes() {
 // DECODE_ONLY: every request of the batch has Lq*G <= 16 (known on the host
 // from max_seqlen_q), so the prefill path is not compiled in.  Both variants
 // hold two workgroups, i.e. two waves per SIMD, per CU.
-template <int D, bool DECODE_ONLY, bool KV8>
+// ALIBI: the prefill tiles carry the ALiBi term (every tile then starts from
+// an initialised accumulator); the decode items test p.alibi at run time.
+template <int D, bool DECODE_ONLY, bool KV8, bool ALIBI>
 __global__ __launch_bounds__(64 * attn_waves<DECODE_ONLY>(), 2) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char smem[attn_lds_bytes<D, DECODE_ONLY, KV8>()];
   const int bid = blockIdx.x;
@@ -1473,7 +1507,7 @@ __global__ __launch_bounds__(64 * attn_waves<DECODE_ONLY>(), 2) void attn_kernel
   if (kind == 2) {
     decode_item<D, 1, attn_waves<DECODE_ONLY>(), KV8>(p, it, g, s, smem);
   } else if constexpr (!DECODE_ONLY) {
-    if (kind == 1) prefill_item<D, KV8>(p, it, g, s, smem);
+    if (kind == 1) prefill_item<D, KV8, ALIBI>(p, it, g, s, smem);
   }
 }
 
@@ -1736,6 +1770,7 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
   const bool pos_scale = c > 0.f;
   const uint32_t bias_bytes = BIAS ? (uint32_t)p.num_tokens * (uint32_t)p.H * (uint32_t)p.R * 4u : 0u;
   const float v_scale = KV8 ? p.v_scale : 1.f;
+  const bool alibi = p.alibi != nullptr;
 
   // A piece: units [j0, j1) of pair (b, g) inside this workgroup's range,
   // with what its rows need (uniform fields, then the lane's column).
@@ -1744,6 +1779,7 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
     int tok0, lq, ncols, lo_a, kend, in_lo, in_hi, band_lo, band_hi, my_n;
     int qa, lo_c, hi_c, tok, head;
     uint32_t rel_base;
+    float al;  // ALiBi slope of the lane's head times log2(e), or 0
   };
   // LDS reads while direct loads are in flight go through inline asm (the
   // compiler would wait for the loads first).
@@ -1786,6 +1822,7 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
     P.band_lo = qa_min - p.R + 1;
     P.band_hi = qa_max;
     P.rel_base = BIAS ? (uint32_t)((P.tok * p.H + P.head) * p.R) : 0u;
+    P.al = alibi ? p.alibi[P.head] * kLog2e : 0.f;
     const int n_units = P.j1 - P.j0;
     P.my_n = n_units > w ? (n_units - w + NW - 1) / NW : 0;
     return P;
@@ -1883,7 +1920,7 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
     // Lane (c16, q) holds S[col c16][key key0 + 4q + j].
     const bool interior = key0 >= P.in_lo && key0 + 15 <= P.in_hi;
     const bool band = in_band(P, key0);
-    const bool plain = interior && !band;
+    const bool plain = interior && !band && !alibi;
     float mx = neg_inf();
     if (plain) {
       if (pos_scale) {
@@ -1904,6 +1941,7 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
         const int t = key0 + 4 * q + j;
         float v = sacc[j] * c;
         if (band && (unsigned)(P.qa - t) < (unsigned)p.R) v = __builtin_fmaf(bias[j], kLog2e, v);
+        if (alibi) v = __builtin_fmaf(P.al, (float)(t - P.qa), v);
         if (t < P.lo_c || t > P.hi_c) v = neg_inf();
         sacc[j] = v;
         mx = fmaxf(mx, v);
@@ -2319,6 +2357,7 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
   const bool pos_scale = c > 0.f;
   const uint32_t bias_bytes = BIAS ? (uint32_t)p.num_tokens * (uint32_t)p.H * (uint32_t)p.R * 4u : 0u;
   const float v_scale = KV8 ? p.v_scale : 1.f;
+  const bool alibi = p.alibi != nullptr;
 
   // A piece: units [j0, j1) of request b inside this workgroup's range,
   // with what its rows need (uniform fields, then the lane's column).
@@ -2327,6 +2366,7 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
     int tok0, lq, ncols, lo_a, kend, in_lo, in_hi, band_lo, band_hi, n;
     int qa, lo_c, hi_c, tok, head;
     uint32_t rel_base;
+    float al;  // ALiBi slope of the lane's head times log2(e), or 0
   };
   auto prefix_at = [&](int i) { return __builtin_amdgcn_readfirstlane(lds_read_i32_now(lds_prefix + 4u * i)); };
   auto make_piece = [&](int cur) __attribute__((always_inline)) {
@@ -2365,6 +2405,7 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
     P.band_lo = qa_min - p.R + 1;
     P.band_hi = qa_max;
     P.rel_base = BIAS ? (uint32_t)((P.tok * p.H + P.head) * p.R) : 0u;
+    P.al = alibi ? p.alibi[P.head] * kLog2e : 0.f;
     return P;
   };
   auto key_of = [&](const Piece &P, int k) { return P.lo_a + 16 * (P.j0 + k); };
@@ -2453,7 +2494,7 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
     for (int ks = 0; ks < QK; ++ks) sacc = mfma16(as_bf16x8(kf[ks]), qf[ks], sacc);
     const bool interior = key0 >= P.in_lo && key0 + 15 <= P.in_hi;
     const bool band = in_band(P, key0);
-    const bool plain = interior && !band;
+    const bool plain = interior && !band && !alibi;
     float mx = neg_inf();
     if (plain) {
       if (pos_scale) {
@@ -2474,6 +2515,7 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
         const int t = key0 + 4 * q + j;
         float v = sacc[j] * c;
         if (band && (unsigned)(P.qa - t) < (unsigned)p.R) v = __builtin_fmaf(bias[j], kLog2e, v);
+        if (alibi) v = __builtin_fmaf(P.al, (float)(t - P.qa), v);
         if (t < P.lo_c || t > P.hi_c) v = neg_inf();
         sacc[j] = v;
         mx = fmaxf(mx, v);
@@ -2915,22 +2957,21 @@ hipError_t launch_attention(const AttnParams &p, int head_dim, int64_t n_items_u
   const int64_t blocks = n_items_ub * p.Hkv * p.S;
   if (blocks <= 0) return hipSuccess;
   const dim3 grid((unsigned)blocks);
-  auto go = [&](auto d_tag, auto dec_tag, auto k_tag) {
+  auto go = [&](auto d_tag, auto dec_tag, auto k_tag, auto a_tag) {
     const dim3 block(64 * attn_waves<decltype(dec_tag)::value>());
-    hipLaunchKernelGGL((attn_kernel<decltype(d_tag)::value, decltype(dec_tag)::value, decltype(k_tag)::value>),
+    hipLaunchKernelGGL((attn_kernel<decltype(d_tag)::value, decltype(dec_tag)::value, decltype(k_tag)::value,
+                                    decltype(a_tag)::value>),
                        grid, block, 0, stream, p);
   };
-  using D128 = std::integral_constant<int, 128>;
-  using D64 = std::integral_constant<int, 64>;
-  using T_ = std::true_type;
-  using F_ = std::false_type;
-  if (head_dim == 128) {
-    if (decode_only) p.kv8 ? go(D128{}, T_{}, T_{}) : go(D128{}, T_{}, F_{});
-    else p.kv8 ? go(D128{}, F_{}, T_{}) : go(D128{}, F_{}, F_{});
-  } else {
-    if (decode_only) p.kv8 ? go(D64{}, T_{}, T_{}) : go(D64{}, T_{}, F_{});
-    else p.kv8 ? go(D64{}, F_{}, T_{}) : go(D64{}, F_{}, F_{});
-  }
+  auto go_d = [&](auto d_tag) {
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    if (decode_only) p.kv8 ? go(d_tag, T_{}, T_{}, F_{}) : go(d_tag, T_{}, F_{}, F_{});
+    else if (p.alibi) p.kv8 ? go(d_tag, F_{}, T_{}, T_{}) : go(d_tag, F_{}, F_{}, T_{});
+    else p.kv8 ? go(d_tag, F_{}, T_{}, F_{}) : go(d_tag, F_{}, F_{}, F_{});
+  };
+  if (head_dim == 128) go_d(std::integral_constant<int, 128>{});
+  else go_d(std::integral_constant<int, 64>{});
   return hipGetLastError();
 }
 

@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ("rpa_attn_varlen", "rpa_split_combine", "rpa_choose_splits", "rpa_workspace_bytes",
               "rpa_status_string", "rpa_slot_mapping", "rpa_kv_cache_write", "rpa_attn_varlen_fp8",
-              "rpa_kv_cache_write_fp8"):
+              "rpa_kv_cache_write_fp8", "rpa_attn_varlen_ex"):
         assert n in names
 
 
@@ -181,6 +181,18 @@ def test_fp8_attention_argument_errors(L):
     assert _attn8(L, ws=None) == WS
     assert _attn8(L, S=4, ws=None) == WS
     assert _attn8(L, T=0, B=0, q=None, out=None) == OK
+
+
+def test_ex_entry_validates_like_the_others(L):
+    f = L.rpa_attn_varlen_ex
+    def call(kv, ks, vs, D=128, S=1, ws=None, wsb=0, q=FAKE, T=2, B=2):
+        return f(q, FAKE, FAKE, kv, ks, vs, FAKE, 4, FAKE, FAKE, B, T, 32, 8, D, 8, 16, 1, 0.125, 1, -1, -1,
+                 0, None, FAKE, S, ws, wsb, FAKE, None, None)
+    assert call(1, 0.0, 1.0) == SHAPE        # E4M3 caches need positive scales
+    assert call(0, 0.0, 1.0, D=96) == UNSUP  # bf16 caches ignore them
+    assert call(1, 1.0, 1.0, S=4) == WS
+    assert call(0, 1.0, 1.0, q=None) == NULL
+    assert call(1, 1.0, 1.0, T=0, B=0, q=None) == OK
 
 
 def test_kv_cache_write_fp8_argument_errors(L):

@@ -1,0 +1,100 @@
+"""GPU parity of the ALiBi term (rpa_attn_varlen_ex through the binding's
+alibi_slopes) against the fp64 oracle, on every kernel path: both balanced
+decodes, split-mode decode items, prefill tiles, mixed batches with a
+window, bf16 and E4M3 caches.  Tolerances as for the other parity tests."""
+import pytest
+import torch
+
+from oracle import attention as orc
+from oracle import fp8 as ofp8
+from relative_bias_amd import binding as bnd
+from relative_bias_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+OUT_MAX, OUT_MEAN, LSE_MAX = 2e-2, 2e-3, 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "these tests need a GPU"
+    bnd.lib()
+
+
+def _slopes(H, kind):
+    if kind == "geometric":  # the usual ALiBi slopes 2^(-8 (i + 1) / H)
+        return torch.tensor([2.0 ** (-8.0 * (i + 1) / H) for i in range(H)], dtype=torch.float32)
+    g = torch.Generator().manual_seed(H)
+    s = torch.rand(H, generator=g) * 0.5 - 0.1  # some negative, one zero
+    s[0] = 0.0
+    return s.to(torch.float32)
+
+
+def _compare(out, lse, ref_out, ref_lse, tag):
+    assert not torch.isnan(out).any(), f"{tag}: NaN"
+    err = (out - ref_out).abs()
+    assert err.max().item() <= OUT_MAX, f"{tag}: out max err {err.max().item():.3e}"
+    assert err.mean().item() <= OUT_MEAN, f"{tag}: out mean err {err.mean().item():.3e}"
+    inf = torch.isinf(ref_lse)
+    assert torch.equal(torch.isinf(lse), inf), f"{tag}: lse -inf pattern differs"
+    if (~inf).any():
+        le = (lse[~inf] - ref_lse[~inf]).abs().max().item()
+        assert le <= LSE_MAX, f"{tag}: lse max err {le:.3e}"
+
+
+CASES = {
+    # name: (q_lens, k_lens, H, Hkv, D, R, window, splits)
+    "decode_heads8": ([1] * 10, [1, 16, 17, 300, 1024, 2000, 77, 5, 700, 3001], 32, 8, 128, 64, (-1, -1), [0, 3]),
+    "decode_pairs_gqa4": ([1] * 6, [1, 33, 400, 1500, 64, 999], 8, 2, 128, 0, (-1, -1), [0, 2]),
+    "decode_d64_window": ([1] * 5, [50, 900, 2000, 3, 1200], 16, 8, 64, 32, (255, 0), [0, 1]),
+    "prefill_d128": ([300, 77, 129], [900, 77, 1500], 16, 8, 128, 256, (-1, -1), [1, 2]),
+    "prefill_d64_nobias": ([64, 200], [64, 333], 4, 2, 64, 0, (-1, -1), [1]),
+    "mixed_window": ([1, 130, 1, 40, 1], [2000, 500, 70, 3000, 1], 16, 2, 128, 100, (127, 0), [1, 3]),
+}
+PARAMS = [(n, S, kind) for n in CASES for S in CASES[n][-1] for kind in ("geometric", "mixed_sign")]
+
+
+@pytest.mark.parametrize("name,S,kind", PARAMS)
+def test_alibi_matches_oracle(name, S, kind):
+    ql, kl, H, Hkv, D, R, win, _ = CASES[name]
+    w = wl.build(ql, kl, num_heads=H, num_kv_heads=Hkv, head_dim=D, rel_extent=R, window_size=win, seed=31)
+    sl = _slopes(H, kind)
+    ref_out, ref_lse = orc.attention(w.q, w.key_cache, w.value_cache, w.block_table, w.cache_seqlens,
+                                     w.cu_seqlens_q, w.softmax_scale, w.causal, w.window_size, w.rel_extent,
+                                     w.rel_logits, alibi_slopes=sl)
+    wg = w.to("cuda")
+    out, lse = bnd.attn_workload(wg, num_splits=S, alibi_slopes=sl.cuda())
+    torch.cuda.synchronize()
+    _compare(out.float().cpu().double(), lse.cpu().double(), ref_out, ref_lse, f"{name} S={S} {kind}")
+
+
+def test_alibi_zero_slopes_equal_plain_call():
+    w = wl.build([1, 50, 1], [400, 600, 90], num_heads=8, num_kv_heads=2, head_dim=128, rel_extent=16, seed=32)
+    wg = w.to("cuda")
+    a = bnd.attn_workload(wg, num_splits=1, alibi_slopes=torch.zeros(8, device="cuda"))
+    b = bnd.attn_workload(wg, num_splits=1)
+    torch.cuda.synchronize()
+    ea = (a[0].float() - b[0].float()).abs().max().item()
+    assert ea <= 1e-2 and (a[1] - b[1]).abs().max().item() <= 1e-4
+
+
+@pytest.mark.parametrize("S", [0, 1])
+def test_alibi_with_fp8_cache(S):
+    ql, kl = ([1] * 6, [100, 2000, 5, 777, 1500, 64]) if S == 0 else ([1, 90, 1], [500, 300, 1000])
+    w = wl.build(ql, kl, num_heads=32, num_kv_heads=8, head_dim=128, rel_extent=64, seed=33)
+    g = torch.Generator().manual_seed(34)
+    ks, vs = 1 / 32, 1 / 16
+    k8 = (torch.randn(w.key_cache.shape, generator=g) / ks).to(torch.float8_e4m3fn).view(torch.uint8)
+    v8 = (torch.randn(w.key_cache.shape, generator=g) / vs).to(torch.float8_e4m3fn).view(torch.uint8)
+    sl = _slopes(32, "geometric")
+    ref_out, ref_lse = ofp8.attention_fp8(w.q, k8, v8, ks, vs, w.block_table, w.cache_seqlens, w.cu_seqlens_q,
+                                          w.softmax_scale, w.causal, w.window_size, w.rel_extent, w.rel_logits,
+                                          alibi_slopes=sl)
+    wg = w.to("cuda")
+    out, lse = bnd.rpa_attn_varlen_fp8(
+        wg.q, k8.cuda(), v8.cuda(), k_scale=ks, v_scale=vs, block_table=wg.block_table,
+        cache_seqlens=wg.cache_seqlens, cu_seqlens_q=wg.cu_seqlens_q, max_seqlen_q=wg.max_seqlen_q,
+        softmax_scale=wg.softmax_scale, causal=wg.causal, window_size=wg.window_size, rel_extent=wg.rel_extent,
+        rel_logits=wg.rel_logits, num_splits=S, return_lse=True, alibi_slopes=sl.cuda())
+    torch.cuda.synchronize()
+    _compare(out.float().cpu().double(), lse.cpu().double(), ref_out, ref_lse, f"fp8 alibi S={S}")
