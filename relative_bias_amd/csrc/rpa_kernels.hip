@@ -458,6 +458,24 @@ __device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t a, uint32_t 
 enum { kInitEdge, kInitBand, kInitFull };
 // Key offset (without the 4 hf shift) of accumulator element (kb2, j).
 __device__ __forceinline__ constexpr int offset_of(int kb2, int j) { return 32 * kb2 + 8 * (j >> 2) + 3 - (j & 3); }
+// ALiBi ramp al0 + al_s * offset_of(kb2, j) of the 32 elements, by additions
+// from a few registers (per-element constants would each need a register).
+__device__ __forceinline__ void alibi_ramp(float (&r)[2][16], float al0, float al_s) {
+  const float s8 = 8.f * al_s, s32 = 32.f * al_s;
+  float g0 = __builtin_fmaf(3.f, al_s, al0);
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+    float gb = kb2 ? g0 + s32 : g0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float b = g ? gb + (float)g * s8 : gb;
+      r[kb2][4 * g] = b;
+      r[kb2][4 * g + 1] = b - al_s;
+      r[kb2][4 * g + 2] = b - 2.f * al_s;
+      r[kb2][4 * g + 3] = b - 3.f * al_s;
+    }
+  }
+}
 
 template <int MODE>
 __device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv_scale, float masked,
@@ -466,10 +484,12 @@ __device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) sacc[kb2] *= inv_scale;
     if (alibi) {
+      float r[2][16];
+      alibi_ramp(r, tb.al0, tb.al_s);
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[kb2][j] += __builtin_fmaf(tb.al_s, (float)offset_of(kb2, j), tb.al0);
+        for (int j = 0; j < 16; ++j) sacc[kb2][j] += r[kb2][j];
     }
     return;
   }
@@ -479,6 +499,8 @@ __device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv
   const uint32_t band = USE_BAND ? range_bits(tb.band_lo, tb.band_hi) : 0u;
   const uint32_t mbits = __float_as_uint(masked);
   if (alibi) {
+    float r[2][16];
+    alibi_ramp(r, tb.al0, tb.al_s);
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
@@ -487,7 +509,7 @@ __device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv
         uint32_t v = 0u;
         if constexpr (MODE != kInitEdge) v = __float_as_uint(sacc[kb2][j] * inv_scale);
         if constexpr (USE_BAND) v &= bit_mask(band, pos);
-        const float f = __uint_as_float(v) + __builtin_fmaf(tb.al_s, (float)offset_of(kb2, j), tb.al0);
+        const float f = __uint_as_float(v) + r[kb2][j];
         sacc[kb2][j] = __uint_as_float(bit_select(bit_mask(vis, pos), __float_as_uint(f), mbits));
       }
     }
@@ -899,7 +921,11 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   };
 
   auto is_band = [&](int kb) { return p.R > 0 && kb <= band_hi && kb + kTileKeys - 1 >= band_lo; };
-  auto is_plain = [&](int kb) { return !alibi && kb >= in_lo && kb + kTileKeys - 1 <= in_hi && !is_band(kb); };
+  // Plain: every key visible to every row, outside the band.  With ALiBi no
+  // tile is plain (each needs its ALiBi start), but such a tile only needs
+  // the ALiBi ramp, no mask.
+  auto is_plain_geo = [&](int kb) { return kb >= in_lo && kb + kTileKeys - 1 <= in_hi && !is_band(kb); };
+  auto is_plain = [&](int kb) { return !alibi && is_plain_geo(kb); };
   // Every key of the tile visible to, and in the band of, every row.
   const int full_lo = __builtin_amdgcn_readfirstlane(max(in_lo, qa_max - p.R + 1));
   const int full_hi = __builtin_amdgcn_readfirstlane(min(in_hi, qa_min));
@@ -925,9 +951,22 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   // after the set is released (raw bias loads for a band tile, the masks
   // of an edge tile; a plain tile's set is zeroed first), finish() once
   // those loads have landed (band tiles only).
+  auto start_general = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
+    if (alibi && is_plain_geo(kb)) {
+      const TileBounds tb = bounds(kb);
+      float r[2][16];
+      alibi_ramp(r, tb.al0, tb.al_s);
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sacc[kb2][j] = r[kb2][j];
+    } else {
+      tile_init<kInitEdge>(sacc, bounds(kb), inv_scale, masked, alibi);
+    }
+  };
   auto begin = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
     if (is_band(kb)) load_bias(sacc, kb);
-    else if (!is_plain(kb)) tile_init<kInitEdge>(sacc, bounds(kb), inv_scale, masked, alibi);
+    else if (!is_plain(kb)) start_general(sacc, kb);
   };
   auto finish = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
     if (is_band(kb)) {
@@ -1055,8 +1094,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       const float mx = phase_b<D, L::vOff(PAR)>(smem, pb, oacc, lane, nxt) * c;
       // Masks of an edge tile j+2 in the released set, then the barrier that
       // publishes K(j+2) and V(j+1).  Raw bias loads may stay in flight.
-      if (!band2 && j + 2 < nt && !is_plain(tile_kb(j + 2)))
-        tile_init<kInitEdge>(cur, bounds(tile_kb(j + 2)), inv_scale, masked, alibi);
+      if (!band2 && j + 2 < nt && !is_plain(tile_kb(j + 2))) start_general(cur, tile_kb(j + 2));
       __builtin_amdgcn_sched_barrier(0);
       if (!band2) wait_vm0();
       else if (bias_fast) wait_vm8();
