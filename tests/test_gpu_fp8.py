@@ -76,13 +76,28 @@ def test_kv_write_fp8_every_bf16_value():
 
 # ------------------------------------------------------------- attention
 
-def _fp8_workload(q_lens, k_lens, H, Hkv, D, R, k_scale, v_scale, seed, window=(-1, -1), extra_pages=0):
-    w = wl.build(q_lens, k_lens, num_heads=H, num_kv_heads=Hkv, head_dim=D, block_size=16, rel_extent=R,
+def _fp8_workload(q_lens, k_lens, H, Hkv, D, R, k_scale, v_scale, seed, window=(-1, -1), extra_pages=0,
+                  block_size=16, poison=False):
+    w = wl.build(q_lens, k_lens, num_heads=H, num_kv_heads=Hkv, head_dim=D, block_size=block_size, rel_extent=R,
                  window_size=window, seed=seed, extra_pages=extra_pages)
     g = torch.Generator().manual_seed(seed + 1000)
     # Codes of N(0, 1) keys / values at the given scales (inputs, not results).
     k8 = (torch.randn(w.key_cache.shape, generator=g) / k_scale).to(torch.float8_e4m3fn).view(torch.uint8)
     v8 = (torch.randn(w.key_cache.shape, generator=g) / v_scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    if poison:
+        # NaN codes in every page no request references and in every slot past
+        # a request's last key: a correct kernel never lets them into a result.
+        used = torch.zeros(k8.shape[0], dtype=torch.bool)
+        for b, lk in enumerate(w.k_lens):
+            n = (lk + block_size - 1) // block_size
+            for j in range(n):
+                pg = int(w.block_table[b, j])
+                used[pg] = True
+                if j == n - 1 and lk % block_size:
+                    k8[pg, lk % block_size:] = 0x7F
+                    v8[pg, lk % block_size:] = 0xFF
+        k8[~used] = 0x7F
+        v8[~used] = 0x7F
     return w, k8, v8
 
 
@@ -170,6 +185,70 @@ def test_fp8_attention_is_repeatable_and_page_invariant():
     w2.block_table = bt
     c = _run_fp8(w2, k8[perm].contiguous(), v8[perm].contiguous(), 1 / 32, 1 / 16)
     assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
+
+
+@pytest.mark.parametrize("BS", [32, 48])
+@pytest.mark.parametrize("kind", ["decode_heads", "decode_pairs", "prefill"])
+def test_fp8_block_sizes_and_nan_poison(BS, kind):
+    """Block sizes other than 16 (48: not a power of two) with NaN codes in
+    unreferenced pages and tail slots."""
+    if kind == "decode_heads":
+        args = ([1] * 5, [1, 100, 777, 2000, 48], 32, 8, 128, 64)
+    elif kind == "decode_pairs":
+        args = ([1] * 4, [3, 96, 1000, 500], 8, 2, 128, 32)
+    else:
+        args = ([70, 1, 33], [300, 40, 33], 8, 2, 64, 16)
+    ql, kl, H, Hkv, D, R = args
+    w, k8, v8 = _fp8_workload(ql, kl, H, Hkv, D, R, 1 / 32, 1 / 16, seed=24, extra_pages=2, block_size=BS,
+                              poison=True)
+    ref_out, ref_lse = ofp8.attention_fp8(w.q, k8, v8, 1 / 32, 1 / 16, w.block_table, w.cache_seqlens,
+                                          w.cu_seqlens_q, w.softmax_scale, w.causal, w.window_size, w.rel_extent,
+                                          w.rel_logits)
+    for S in (0, 2):
+        out, lse = _run_fp8(w, k8, v8, 1 / 32, 1 / 16, S=S)
+        _compare(out, lse, ref_out, ref_lse, f"{kind} BS={BS} S={S}")
+
+
+def test_fp8_graph_replay():
+    """A captured E4M3 decode replayed over new lengths equals the eager call."""
+    B, kmax = 10, 2000
+    w, k8, v8 = _fp8_workload([1] * B, [kmax] * B, 32, 8, 128, 64, 1 / 32, 1 / 16, seed=25)
+    wg = w.to("cuda")
+    k8g, v8g = k8.cuda(), v8.cuda()
+    T, H, D = wg.q.shape
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty((bnd.rpa_workspace_bytes(0, T, H, D),), dtype=torch.uint8, device="cuda")
+
+    def call(o, l):
+        bnd.rpa_attn_varlen_fp8(wg.q, k8g, v8g, k_scale=1 / 32, v_scale=1 / 16, block_table=wg.block_table,
+                                cache_seqlens=wg.cache_seqlens, cu_seqlens_q=wg.cu_seqlens_q, max_seqlen_q=1,
+                                softmax_scale=wg.softmax_scale, rel_extent=wg.rel_extent, rel_logits=wg.rel_logits,
+                                num_splits=0, out=o, lse=l, workspace=ws)
+
+    call(out, lse)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        call(out, lse)
+    gen = torch.Generator().manual_seed(26)
+    for _ in range(3):
+        kl = torch.randint(1, kmax + 1, (B,), generator=gen, dtype=torch.int32)
+        wg.cache_seqlens.copy_(kl)
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        got = (out.clone(), lse.clone())
+        eo, el = torch.empty_like(out), torch.empty_like(lse)
+        call(eo, el)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], eo) and torch.equal(got[1], el)
+        wc = w.to("cpu")
+        wc.cache_seqlens = kl
+        ref_out, ref_lse = ofp8.attention_fp8(wc.q, k8, v8, 1 / 32, 1 / 16, wc.block_table, wc.cache_seqlens,
+                                              wc.cu_seqlens_q, wc.softmax_scale, wc.causal, wc.window_size,
+                                              wc.rel_extent, wc.rel_logits)
+        _compare(got[0].float().cpu().double(), got[1].cpu().double(), ref_out, ref_lse, "fp8 graph replay")
 
 
 def test_fp8_bad_scales_raise():
