@@ -233,6 +233,43 @@ def measure_kv_write(steps, warmup):
     return ms, dict(info, bytes=nbytes)
 
 
+def hbm_read_ceiling(gib=4, reps=10):
+    """Streaming-read rate of the device: one pass of 16-byte nontemporal
+    loads over a `gib` GiB buffer (larger than the 256 MB last-level cache)
+    by libhbmprobe.so's kernel, best and median of `reps` passes."""
+    import ctypes
+    import statistics
+    import torch
+    from relative_bias_amd import build as bld
+    if not os.path.exists(bld.PROBE_LIB):
+        raise RuntimeError(f"{bld.PROBE_LIB} is missing: build it with `python -m relative_bias_amd.build`")
+    L = ctypes.CDLL(bld.PROBE_LIB)
+    L.hbm_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                  ctypes.c_void_p]
+    L.hbm_stream_read.restype = ctypes.c_int
+    nbytes = gib << 30
+    buf = torch.ones((nbytes // 2,), dtype=torch.bfloat16, device="cuda")
+    blocks = 256 * 8
+    sink = torch.empty((blocks,), dtype=torch.int32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    times = []
+    for i in range(reps + 2):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rc = L.hbm_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), blocks, st)
+        e1.record()
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise RuntimeError(f"hbm_stream_read failed: {rc}")
+        if i >= 2:
+            times.append(e0.elapsed_time(e1))
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"kernel": "stream_read_kernel (libhbmprobe.so)", "bytes": nbytes,
+            "best_gbs": round(nbytes / min(times) / 1e6, 1), "median_gbs": round(nbytes / statistics.median(times) / 1e6, 1)}
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The fp64 oracle on a bounded sample of the decode batch: whole requests
     in order, passing over the batch again until about budget_s of CPU time
@@ -482,6 +519,14 @@ def main(argv=None):
         line["kv_write"] = kv_summary
     if graph_summary is not None:
         line["batched_decode_graph"] = graph_summary
+    if not a.no_extra and a.only is None:
+        try:
+            hc = hbm_read_ceiling()
+            hc["decode_frac_of_ceiling"] = round(roof["achieved"] / hc["best_gbs"], 4) if not prefill_like else None
+            line["hbm_read_ceiling"] = hc
+            log(f"HBM streaming-read ceiling: best {hc['best_gbs']} GB/s, median {hc['median_gbs']} GB/s")
+        except Exception as e:  # reported in the line; never hides the headline
+            line["hbm_read_ceiling"] = {"error": repr(e)}
     if not a.no_cpu and head == "batched_decode":
         log("timing the CPU oracle on a sample ...")
         line["cpu_baseline"] = cpu_baseline(w)

@@ -19,6 +19,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 SOURCES = [os.path.join(CSRC, "rpa_kernels.hip"), os.path.join(CSRC, "rpa_api.cpp")]
 LIB = os.path.join(HERE, "librpa.so")
+# The benchmark's HBM streaming-read probe, a library of its own.
+PROBE_SOURCES = [os.path.join(CSRC, "hbm_probe.hip")]
+PROBE_LIB = os.path.join(HERE, "libhbmprobe.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU ops.
@@ -38,8 +41,13 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, asm_dir: str | None = None) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, *SOURCES, "-o", tmp]
+    _build_one(PROBE_SOURCES, PROBE_LIB, verbose, None)
+    return _build_one(SOURCES, LIB, verbose, asm_dir)
+
+
+def _build_one(sources, lib, verbose: bool, asm_dir: str | None) -> str:
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), *FLAGS, *sources, "-o", tmp]
     env = dict(os.environ)
     cwd = None
     if asm_dir:
@@ -55,8 +63,8 @@ def build(verbose: bool = False, asm_dir: str | None = None) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def main(argv=None):
