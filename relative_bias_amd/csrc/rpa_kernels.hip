@@ -1532,8 +1532,11 @@ constexpr int attn_lds_bytes() {
 // hold two workgroups, i.e. two waves per SIMD, per CU.
 // ALIBI: the prefill tiles carry the ALiBi term (every tile then starts from
 // an initialised accumulator); the decode items test p.alibi at run time.
+// The ALiBi variant runs one workgroup per CU: with two it spills about 24
+// VGPRs inside the tile loop, and the scratch traffic costs more than the
+// second workgroup's overlap gains.
 template <int D, bool DECODE_ONLY, bool KV8, bool ALIBI>
-__global__ __launch_bounds__(64 * attn_waves<DECODE_ONLY>(), 2) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * attn_waves<DECODE_ONLY>(), ALIBI ? 1 : 2) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char smem[attn_lds_bytes<D, DECODE_ONLY, KV8>()];
   const int bid = blockIdx.x;
   const int s = bid % p.S;
