@@ -243,6 +243,9 @@ int rpa_attn_varlen_fp8(const void *q, const void *key_cache, const void *value_
  *
  *   kv_e4m3        0: bf16 caches (k_scale, v_scale ignored); nonzero: E4M3
  *                  caches with k_scale, v_scale as for rpa_attn_varlen_fp8.
+ *   rel_logits_bf16  0: rel_logits is fp32 [num_tokens, num_heads, R];
+ *                  nonzero: bf16 of the same shape (half the bias bytes; the
+ *                  values are widened exactly to fp32 where they are added).
  *   alibi_slopes   NULL, or fp32 [num_heads] device array: the logit of key t
  *                  for a row at position qa of q head h gains
  *                  alibi_slopes[h] * (t - qa), added like the relative bias
@@ -264,9 +267,9 @@ int rpa_attn_varlen_ex(const void *q, const void *key_cache, const void *value_c
                        int32_t head_dim, int32_t num_blocks, int32_t block_size,
                        int32_t max_seqlen_q, float softmax_scale, int causal,
                        int32_t window_left, int32_t window_right,
-                       int32_t rel_extent, const float *rel_logits, const float *alibi_slopes,
-                       int32_t num_splits, void *workspace, size_t workspace_bytes,
-                       void *out, float *lse, void *stream);
+                       int32_t rel_extent, const void *rel_logits, int rel_logits_bf16,
+                       const float *alibi_slopes, int32_t num_splits, void *workspace,
+                       size_t workspace_bytes, void *out, float *lse, void *stream);
 
 /*
  * rpa_kv_cache_write_fp8: rpa_kv_cache_write into E4M3 caches.  Element x of

@@ -68,8 +68,8 @@ def lib():
     L.rpa_kv_cache_write_fp8.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, vp, vp, vp]
     L.rpa_kv_cache_write_fp8.restype = ctypes.c_int
     L.rpa_attn_varlen_ex.argtypes = [vp, vp, vp, ctypes.c_int, f32, f32, vp, i32, vp, vp, i32, i32, i32, i32, i32,
-                                     i32, i32, i32, f32, ctypes.c_int, i32, i32, i32, vp, vp, i32, vp, sz, vp, vp,
-                                     vp]
+                                     i32, i32, i32, f32, ctypes.c_int, i32, i32, i32, vp, ctypes.c_int, vp, i32, vp,
+                                     sz, vp, vp, vp]
     L.rpa_attn_varlen_ex.restype = ctypes.c_int
     _lib = L
     return L
@@ -128,8 +128,9 @@ def rpa_attn_varlen(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                     return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
                     alibi_slopes: Optional[torch.Tensor] = None):
-    """Paged varlen causal attention with the additive relative bias (and
-    optional ALiBi slopes, fp32 [H], through rpa_attn_varlen_ex).
+    """Paged varlen causal attention with the additive relative bias
+    (rel_logits fp32 or bf16; optional ALiBi slopes, fp32 [H]: both through
+    rpa_attn_varlen_ex).
 
     Returns ``out`` (bf16 [T, H, D]), or ``(out, lse)`` when ``return_lse``
     or an ``lse`` tensor is given.  ``num_splits=None`` uses
@@ -158,7 +159,8 @@ def rpa_attn_varlen(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
         if rel_logits is None:
             raise ValueError("rel_extent > 0 needs rel_logits")
         rel_logits = rel_logits.contiguous()  # the walkthrough's wrapper does the same
-        _check(rel_logits, "rel_logits", torch.float32, dev, 3)
+        _check(rel_logits, "rel_logits", torch.bfloat16 if rel_logits.dtype == torch.bfloat16 else torch.float32,
+               dev, 3)
         if tuple(rel_logits.shape) != (T, H, R):
             raise ValueError(f"rel_logits must be {(T, H, R)}, got {tuple(rel_logits.shape)}")
     if num_splits is None:
@@ -179,7 +181,8 @@ def rpa_attn_varlen(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
     if ws_bytes and workspace is None:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
     alibi = _alibi(alibi_slopes, H, dev)
-    if alibi is None:
+    rel_bf16 = int(R > 0 and rel_logits.dtype == torch.bfloat16)
+    if alibi is None and not rel_bf16:
         st = lib().rpa_attn_varlen(
             _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(block_table), block_table.shape[1],
             _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB, BS, int(max_seqlen_q),
@@ -192,7 +195,7 @@ def rpa_attn_varlen(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
             _ptr(q), _ptr(key_cache), _ptr(value_cache), 0, 1.0, 1.0, _ptr(block_table), block_table.shape[1],
             _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB, BS, int(max_seqlen_q),
             float(softmax_scale), int(bool(causal)), int(window_size[0]), int(window_size[1]), R,
-            _ptr(rel_logits) if R > 0 else None, _ptr(alibi), S, _ptr(workspace),
+            _ptr(rel_logits) if R > 0 else None, rel_bf16, _ptr(alibi), S, _ptr(workspace),
             0 if workspace is None else workspace.numel() * workspace.element_size(),
             _ptr(out), _ptr(lse), _stream(dev))
     if st != RPA_OK:
@@ -241,7 +244,8 @@ def rpa_attn_varlen_fp8(q: torch.Tensor, key_cache: torch.Tensor, value_cache: t
         if rel_logits is None:
             raise ValueError("rel_extent > 0 needs rel_logits")
         rel_logits = rel_logits.contiguous()
-        _check(rel_logits, "rel_logits", torch.float32, dev, 3)
+        _check(rel_logits, "rel_logits", torch.bfloat16 if rel_logits.dtype == torch.bfloat16 else torch.float32,
+               dev, 3)
         if tuple(rel_logits.shape) != (T, H, R):
             raise ValueError(f"rel_logits must be {(T, H, R)}, got {tuple(rel_logits.shape)}")
     S = int(num_splits)
@@ -257,7 +261,8 @@ def rpa_attn_varlen_fp8(q: torch.Tensor, key_cache: torch.Tensor, value_cache: t
     if ws_bytes and workspace is None:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
     alibi = _alibi(alibi_slopes, H, dev)
-    if alibi is None:
+    rel_bf16 = int(R > 0 and rel_logits.dtype == torch.bfloat16)
+    if alibi is None and not rel_bf16:
         st = lib().rpa_attn_varlen_fp8(
             _ptr(q), _ptr(key_cache), _ptr(value_cache), float(k_scale), float(v_scale), _ptr(block_table),
             block_table.shape[1], _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB, BS,
@@ -270,7 +275,7 @@ def rpa_attn_varlen_fp8(q: torch.Tensor, key_cache: torch.Tensor, value_cache: t
             _ptr(q), _ptr(key_cache), _ptr(value_cache), 1, float(k_scale), float(v_scale), _ptr(block_table),
             block_table.shape[1], _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB, BS,
             int(max_seqlen_q), float(softmax_scale), int(bool(causal)), int(window_size[0]), int(window_size[1]),
-            R, _ptr(rel_logits) if R > 0 else None, _ptr(alibi), S, _ptr(workspace),
+            R, _ptr(rel_logits) if R > 0 else None, rel_bf16, _ptr(alibi), S, _ptr(workspace),
             0 if workspace is None else workspace.numel() * workspace.element_size(),
             _ptr(out), _ptr(lse), _stream(dev))
     if st != RPA_OK:

@@ -102,8 +102,8 @@ int attn_impl(const void *q, const void *key_cache, const void *value_cache, boo
               const int32_t *cache_seqlens, const int32_t *cu_seqlens_q, int32_t batch, int32_t num_tokens,
               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
               int32_t max_seqlen_q, float softmax_scale, int causal, int32_t window_left, int32_t window_right,
-              int32_t rel_extent, const float *rel_logits, const float *alibi_slopes, int32_t num_splits,
-              void *workspace, size_t workspace_bytes, void *out, float *lse, void *stream) {
+              int32_t rel_extent, const float *rel_logits, bool rel_bf16, const float *alibi_slopes,
+              int32_t num_splits, void *workspace, size_t workspace_bytes, void *out, float *lse, void *stream) {
   if (kv8 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
     return RPA_ERR_SHAPE;
   // Sizes.
@@ -197,6 +197,7 @@ int attn_impl(const void *q, const void *key_cache, const void *value_cache, boo
   p.v_scale = kv8 ? v_scale : 1.f;
   p.kv8 = kv8 ? 1 : 0;
   p.alibi = alibi_slopes;
+  p.rel_bf16 = rel_bf16 ? 1 : 0;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (balanced) return rpa::launch_balanced_decode(p, head_dim, st) == hipSuccess ? RPA_OK : RPA_ERR_HIP;
@@ -229,8 +230,8 @@ int rpa_attn_varlen(const void *q, const void *key_cache, const void *value_cach
                     size_t workspace_bytes, void *out, float *lse, void *stream) {
   return attn_impl(q, key_cache, value_cache, false, 1.f, 1.f, block_table, max_pages_per_seq, cache_seqlens,
                    cu_seqlens_q, batch, num_tokens, num_heads, num_kv_heads, head_dim, num_blocks, block_size,
-                   max_seqlen_q, softmax_scale, causal, window_left, window_right, rel_extent, rel_logits, nullptr,
-                   num_splits, workspace, workspace_bytes, out, lse, stream);
+                   max_seqlen_q, softmax_scale, causal, window_left, window_right, rel_extent, rel_logits, false,
+                   nullptr, num_splits, workspace, workspace_bytes, out, lse, stream);
 }
 
 int rpa_attn_varlen_fp8(const void *q, const void *key_cache, const void *value_cache, float k_scale,
@@ -244,7 +245,7 @@ int rpa_attn_varlen_fp8(const void *q, const void *key_cache, const void *value_
   return attn_impl(q, key_cache, value_cache, true, k_scale, v_scale, block_table, max_pages_per_seq,
                    cache_seqlens, cu_seqlens_q, batch, num_tokens, num_heads, num_kv_heads, head_dim, num_blocks,
                    block_size, max_seqlen_q, softmax_scale, causal, window_left, window_right, rel_extent,
-                   rel_logits, nullptr, num_splits, workspace, workspace_bytes, out, lse, stream);
+                   rel_logits, false, nullptr, num_splits, workspace, workspace_bytes, out, lse, stream);
 }
 
 int rpa_attn_varlen_ex(const void *q, const void *key_cache, const void *value_cache, int kv_e4m3, float k_scale,
@@ -253,12 +254,13 @@ int rpa_attn_varlen_ex(const void *q, const void *key_cache, const void *value_c
                        int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t num_blocks, int32_t block_size, int32_t max_seqlen_q, float softmax_scale,
                        int causal, int32_t window_left, int32_t window_right, int32_t rel_extent,
-                       const float *rel_logits, const float *alibi_slopes, int32_t num_splits, void *workspace,
-                       size_t workspace_bytes, void *out, float *lse, void *stream) {
+                       const void *rel_logits, int rel_logits_bf16, const float *alibi_slopes, int32_t num_splits,
+                       void *workspace, size_t workspace_bytes, void *out, float *lse, void *stream) {
   return attn_impl(q, key_cache, value_cache, kv_e4m3 != 0, k_scale, v_scale, block_table, max_pages_per_seq,
                    cache_seqlens, cu_seqlens_q, batch, num_tokens, num_heads, num_kv_heads, head_dim, num_blocks,
                    block_size, max_seqlen_q, softmax_scale, causal, window_left, window_right, rel_extent,
-                   rel_logits, alibi_slopes, num_splits, workspace, workspace_bytes, out, lse, stream);
+                   static_cast<const float *>(rel_logits), rel_logits_bf16 != 0, alibi_slopes, num_splits, workspace,
+                   workspace_bytes, out, lse, stream);
 }
 
 int rpa_slot_mapping(const int32_t *block_table, int32_t max_pages_per_seq, const int32_t *cache_seqlens,

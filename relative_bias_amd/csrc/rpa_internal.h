@@ -52,6 +52,7 @@ struct AttnParams {
   float v_scale;                // E4M3 caches: the value cache's scale (1 for bf16 caches)
   int32_t kv8;                  // 1: k / v are E4M3 codes (uint8) instead of bf16
   const float *alibi;           // [H] ALiBi slopes, or null
+  int32_t rel_bf16;             // 1: rel_logits holds bf16 values (uint16) instead of fp32
 };
 
 struct CombineParams {

@@ -402,6 +402,26 @@ __device__ __forceinline__ void tile_bias_load(f32x16 *sacc, int kb, int qa, con
     }
   }
 }
+// bf16 rel_logits: the raw 16 bits land in the low half of each element (no
+// use of the loaded value here, so the loads stay in flight); tile_bf16_widen
+// turns them into fp32 once they have arrived.
+__device__ __forceinline__ void tile_bias_load_bf16(f32x16 *sacc, int kb, int qa, const uint16_t *rel_row, int R,
+                                                    int hf) {
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int d = qa - (kb + key_of(kb2, j) + 4 * hf);
+      sacc[kb2][j] = __uint_as_float((uint32_t)rel_row[min(max(d, 0), R - 1)]);
+    }
+  }
+}
+__device__ __forceinline__ void tile_bf16_widen(f32x16 *sacc) {
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sacc[kb2][j] = __uint_as_float(__float_as_uint(sacc[kb2][j]) << 16);
+}
 
 
 // Per-lane bounds of one tile, relative to the lane's first key kb + 4 hf:
@@ -713,7 +733,11 @@ __device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32
   return fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
 }
 
-template <int D, bool KV8, bool ALIBI>
+// Prefill variants (compile-time, so that calls without them run the plain
+// kernel): bit 0 ALiBi slopes, bit 1 bf16 rel_logits.
+constexpr int kFeatAlibi = 1, kFeatRelBf16 = 2;
+
+template <int D, bool KV8, int FEAT>
 __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, char *smem) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
@@ -765,7 +789,10 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   const int64_t first_row = (int64_t)(tok0 + row0 / G) * p.H + g * G + row0 % G;
   const int64_t last_row = (int64_t)(tok0 + row_last / G) * p.H + g * G + row_last % G;
   const int64_t bias_lo = first_row * p.R - 4, bias_hi = (last_row + 1) * p.R + 4;
-  const bool bias_fast = p.R > 0 && bias_lo >= 0 && bias_hi <= (int64_t)p.num_tokens * p.H * p.R &&
+  constexpr bool rel_bf16 = (FEAT & kFeatRelBf16) != 0;
+  const uint16_t *rel_row16 =
+      p.R > 0 ? reinterpret_cast<const uint16_t *>(p.rel_logits) + ((int64_t)tok * p.H + head) * p.R : nullptr;
+  const bool bias_fast = !rel_bf16 && p.R > 0 && bias_lo >= 0 && bias_hi <= (int64_t)p.num_tokens * p.H * p.R &&
                          (bias_hi - bias_lo) * 4 < ((int64_t)1 << 31);
   __amdgpu_buffer_rsrc_t bias_rs = make_rsrc(p.rel_logits, 0);
   uint32_t bias_lane_base = 0;
@@ -784,7 +811,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   const float inv_scale = zero_scale ? 1.f : 1.f / fabsf(p.scale);
   const float masked = neg_inf();
   // ALiBi enters the accumulator like the bias: slope * (t - qa) / scale.
-  constexpr bool alibi = ALIBI;
+  constexpr bool alibi = (FEAT & kFeatAlibi) != 0;
   const float al_s = alibi ? p.alibi[head] * inv_scale : 0.f;
 
   bf16x8 qf[KSTEPS];
@@ -917,6 +944,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   auto wait_vm32 = [&]() { __builtin_amdgcn_s_waitcnt(0x8F70); };  // vmcnt(32)
   auto load_bias = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
     if (bias_fast) tile_bias_load4(sacc, bias_rs, bias_lane_base, kb);
+    else if (rel_bf16) tile_bias_load_bf16(sacc, kb, qa, rel_row16, p.R, hf);
     else tile_bias_load(sacc, kb, qa, rel_row, p.R, hf);
   };
 
@@ -970,6 +998,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   };
   auto finish = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
     if (is_band(kb)) {
+      if (rel_bf16) tile_bf16_widen(sacc);
       if (is_full_band(kb)) tile_init<kInitFull>(sacc, bounds(kb), inv_scale, masked, alibi);
       else tile_init<kInitBand>(sacc, bounds(kb), inv_scale, masked, alibi);
     }
@@ -1229,6 +1258,9 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
   const bool pos_scale = c > 0.f;
   const bool alibi = p.alibi != nullptr;
   const float al = alibi ? p.alibi[head] * kLog2e : 0.f;
+  // bf16 rel_logits: the same row in 16-bit elements.
+  const uint16_t *rel_row16 =
+      p.R > 0 ? reinterpret_cast<const uint16_t *>(p.rel_logits) + ((int64_t)tok * p.H + head) * p.R : nullptr;
 
   bf16x8 qf[QK];
   {
@@ -1361,7 +1393,10 @@ __device__ void decode_item(const AttnParams &p, const Item &it, int g, int s, c
           float v = sacc[blk][j] * c;
           if constexpr (BIAS) {
             const int d = qa - t;
-            v = __builtin_fmaf((unsigned)d < (unsigned)p.R ? rel_row[d] : 0.f, kLog2e, v);
+            float rb = 0.f;
+            if ((unsigned)d < (unsigned)p.R)
+              rb = p.rel_bf16 ? __uint_as_float((uint32_t)rel_row16[d] << 16) : rel_row[d];
+            v = __builtin_fmaf(rb, kLog2e, v);
             if (alibi) v = __builtin_fmaf(al, (float)(t - qa), v);
           }
           if constexpr (MASK) {
@@ -1530,13 +1565,14 @@ constexpr int attn_lds_bytes() {
 // DECODE_ONLY: every request of the batch has Lq*G <= 16 (known on the host
 // from max_seqlen_q), so the prefill path is not compiled in.  Both variants
 // hold two workgroups, i.e. two waves per SIMD, per CU.
-// ALIBI: the prefill tiles carry the ALiBi term (every tile then starts from
-// an initialised accumulator); the decode items test p.alibi at run time.
-// The ALiBi variant runs one workgroup per CU: with two it spills about 24
-// VGPRs inside the tile loop, and the scratch traffic costs more than the
-// second workgroup's overlap gains.
-template <int D, bool DECODE_ONLY, bool KV8, bool ALIBI>
-__global__ __launch_bounds__(64 * attn_waves<DECODE_ONLY>(), ALIBI ? 1 : 2) void attn_kernel(AttnParams p) {
+// FEAT: the prefill variant (ALiBi: every tile starts from an initialised
+// accumulator; bf16 rel_logits: band tiles load 16-bit values); the decode
+// items test p.alibi and p.rel_bf16 at run time.  The ALiBi variants run one
+// workgroup per CU: with two they spill about 24 VGPRs inside the tile loop,
+// and the scratch traffic costs more than the second workgroup's overlap
+// gains.
+template <int D, bool DECODE_ONLY, bool KV8, int FEAT>
+__global__ __launch_bounds__(64 * attn_waves<DECODE_ONLY>(), (FEAT & kFeatAlibi) ? 1 : 2) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char smem[attn_lds_bytes<D, DECODE_ONLY, KV8>()];
   const int bid = blockIdx.x;
   const int s = bid % p.S;
@@ -1548,7 +1584,7 @@ __global__ __launch_bounds__(64 * attn_waves<DECODE_ONLY>(), ALIBI ? 1 : 2) void
   if (kind == 2) {
     decode_item<D, 1, attn_waves<DECODE_ONLY>(), KV8>(p, it, g, s, smem);
   } else if constexpr (!DECODE_ONLY) {
-    if (kind == 1) prefill_item<D, KV8, ALIBI>(p, it, g, s, smem);
+    if (kind == 1) prefill_item<D, KV8, FEAT>(p, it, g, s, smem);
   }
 }
 
@@ -1809,7 +1845,14 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
   const uint32_t lds_prefix = smem_u + L::prefixOff;
   const float c = p.scale_log2;
   const bool pos_scale = c > 0.f;
-  const uint32_t bias_bytes = BIAS ? (uint32_t)p.num_tokens * (uint32_t)p.H * (uint32_t)p.R * 4u : 0u;
+  // bf16 rel_logits: each lane loads the dword holding its element (the
+  // range rounded up to whole dwords; a page never ends inside one) and
+  // compute() keeps the element's half.
+  const bool rel_bf16 = p.rel_bf16 != 0;
+  const uint32_t bias_bytes =
+      BIAS ? (rel_bf16 ? ((uint32_t)p.num_tokens * (uint32_t)p.H * (uint32_t)p.R * 2u + 3u) & ~3u
+                       : (uint32_t)p.num_tokens * (uint32_t)p.H * (uint32_t)p.R * 4u)
+           : 0u;
   const float v_scale = KV8 ? p.v_scale : 1.f;
   const bool alibi = p.alibi != nullptr;
 
@@ -1899,8 +1942,9 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = min(max(P.qa - (key0 + 4 * q + j), 0), p.R - 1);
+        const uint32_t boff = rel_bf16 ? ((P.rel_base + (uint32_t)d) * 2u) & ~3u : (P.rel_base + (uint32_t)d) * 4u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (__attribute__((address_space(3))) void *)(bst + 256 * j), 4,
-                                                 (P.rel_base + (uint32_t)d) * 4u, 0, 0, 0);
+                                                 boff, 0, 0, 0);
       }
     }
     char *st = KV8 ? smem + w * 2 * L::stageBytes + slot * LAND : smem + (w * 2 + slot) * L::stageBytes;
@@ -1981,7 +2025,14 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
       for (int j = 0; j < 4; ++j) {
         const int t = key0 + 4 * q + j;
         float v = sacc[j] * c;
-        if (band && (unsigned)(P.qa - t) < (unsigned)p.R) v = __builtin_fmaf(bias[j], kLog2e, v);
+        if (band && (unsigned)(P.qa - t) < (unsigned)p.R) {
+          float bv = bias[j];
+          if (rel_bf16) {
+            const uint32_t bits = __float_as_uint(bv);
+            bv = __uint_as_float(((P.rel_base + (uint32_t)(P.qa - t)) & 1u) ? (bits & 0xffff0000u) : (bits << 16));
+          }
+          v = __builtin_fmaf(bv, kLog2e, v);
+        }
         if (alibi) v = __builtin_fmaf(P.al, (float)(t - P.qa), v);
         if (t < P.lo_c || t > P.hi_c) v = neg_inf();
         sacc[j] = v;
@@ -2396,7 +2447,14 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
   const uint32_t lds_prefix = smem_u + L::prefixOff;
   const float c = p.scale_log2;
   const bool pos_scale = c > 0.f;
-  const uint32_t bias_bytes = BIAS ? (uint32_t)p.num_tokens * (uint32_t)p.H * (uint32_t)p.R * 4u : 0u;
+  // bf16 rel_logits: each lane loads the dword holding its element (the
+  // range rounded up to whole dwords; a page never ends inside one) and
+  // compute() keeps the element's half.
+  const bool rel_bf16 = p.rel_bf16 != 0;
+  const uint32_t bias_bytes =
+      BIAS ? (rel_bf16 ? ((uint32_t)p.num_tokens * (uint32_t)p.H * (uint32_t)p.R * 2u + 3u) & ~3u
+                       : (uint32_t)p.num_tokens * (uint32_t)p.H * (uint32_t)p.R * 4u)
+           : 0u;
   const float v_scale = KV8 ? p.v_scale : 1.f;
   const bool alibi = p.alibi != nullptr;
 
@@ -2474,8 +2532,9 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = min(max(P.qa - (key0 + 4 * q + j), 0), p.R - 1);
+        const uint32_t boff = rel_bf16 ? ((P.rel_base + (uint32_t)d) * 2u) & ~3u : (P.rel_base + (uint32_t)d) * 4u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (__attribute__((address_space(3))) void *)(bst + 256 * j), 4,
-                                                 (P.rel_base + (uint32_t)d) * 4u, 0, 0, 0);
+                                                 boff, 0, 0, 0);
       }
     }
     char *st = KV8 ? smem + w * 2 * L::stageBytes + slot * LAND : smem + (w * 2 + slot) * L::stageBytes;
@@ -2555,7 +2614,14 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
       for (int j = 0; j < 4; ++j) {
         const int t = key0 + 4 * q + j;
         float v = sacc[j] * c;
-        if (band && (unsigned)(P.qa - t) < (unsigned)p.R) v = __builtin_fmaf(bias[j], kLog2e, v);
+        if (band && (unsigned)(P.qa - t) < (unsigned)p.R) {
+          float bv = bias[j];
+          if (rel_bf16) {
+            const uint32_t bits = __float_as_uint(bv);
+            bv = __uint_as_float(((P.rel_base + (uint32_t)(P.qa - t)) & 1u) ? (bits & 0xffff0000u) : (bits << 16));
+          }
+          v = __builtin_fmaf(bv, kLog2e, v);
+        }
         if (alibi) v = __builtin_fmaf(P.al, (float)(t - P.qa), v);
         if (t < P.lo_c || t > P.hi_c) v = neg_inf();
         sacc[j] = v;
@@ -2998,18 +3064,28 @@ hipError_t launch_attention(const AttnParams &p, int head_dim, int64_t n_items_u
   const int64_t blocks = n_items_ub * p.Hkv * p.S;
   if (blocks <= 0) return hipSuccess;
   const dim3 grid((unsigned)blocks);
-  auto go = [&](auto d_tag, auto dec_tag, auto k_tag, auto a_tag) {
+  auto go = [&](auto d_tag, auto dec_tag, auto k_tag, auto f_tag) {
     const dim3 block(64 * attn_waves<decltype(dec_tag)::value>());
     hipLaunchKernelGGL((attn_kernel<decltype(d_tag)::value, decltype(dec_tag)::value, decltype(k_tag)::value,
-                                    decltype(a_tag)::value>),
+                                    decltype(f_tag)::value>),
                        grid, block, 0, stream, p);
   };
-  auto go_d = [&](auto d_tag) {
+  auto go_k = [&](auto d_tag, auto k_tag) {
     using T_ = std::true_type;
     using F_ = std::false_type;
-    if (decode_only) p.kv8 ? go(d_tag, T_{}, T_{}, F_{}) : go(d_tag, T_{}, F_{}, F_{});
-    else if (p.alibi) p.kv8 ? go(d_tag, F_{}, T_{}, T_{}) : go(d_tag, F_{}, F_{}, T_{});
-    else p.kv8 ? go(d_tag, F_{}, T_{}, F_{}) : go(d_tag, F_{}, F_{}, F_{});
+    using I = std::integral_constant<int, 0>;
+    if (decode_only) return go(d_tag, T_{}, k_tag, I{});
+    const int feat = (p.alibi ? kFeatAlibi : 0) | (p.rel_bf16 ? kFeatRelBf16 : 0);
+    switch (feat) {
+      case 0: go(d_tag, F_{}, k_tag, std::integral_constant<int, 0>{}); break;
+      case 1: go(d_tag, F_{}, k_tag, std::integral_constant<int, 1>{}); break;
+      case 2: go(d_tag, F_{}, k_tag, std::integral_constant<int, 2>{}); break;
+      default: go(d_tag, F_{}, k_tag, std::integral_constant<int, 3>{}); break;
+    }
+  };
+  auto go_d = [&](auto d_tag) {
+    if (p.kv8) go_k(d_tag, std::true_type{});
+    else go_k(d_tag, std::false_type{});
   };
   if (head_dim == 128) go_d(std::integral_constant<int, 128>{});
   else go_d(std::integral_constant<int, 64>{});

@@ -187,7 +187,7 @@ def test_ex_entry_validates_like_the_others(L):
     f = L.rpa_attn_varlen_ex
     def call(kv, ks, vs, D=128, S=1, ws=None, wsb=0, q=FAKE, T=2, B=2):
         return f(q, FAKE, FAKE, kv, ks, vs, FAKE, 4, FAKE, FAKE, B, T, 32, 8, D, 8, 16, 1, 0.125, 1, -1, -1,
-                 0, None, FAKE, S, ws, wsb, FAKE, None, None)
+                 0, None, 0, FAKE, S, ws, wsb, FAKE, None, None)
     assert call(1, 0.0, 1.0) == SHAPE        # E4M3 caches need positive scales
     assert call(0, 0.0, 1.0, D=96) == UNSUP  # bf16 caches ignore them
     assert call(1, 1.0, 1.0, S=4) == WS
