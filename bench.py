@@ -313,7 +313,7 @@ def main(argv=None):
     ap.add_argument("--only", default=None, help="run one workload: batched_decode, chunked_prefill, "
                                                   "long_decode, continuous_batch, batched_decode_fp8, "
                                                   "chunked_prefill_fp8, long_decode_fp8, batched_decode_alibi, "
-                                                  "chunked_prefill_alibi, kv_write")
+                                                  "chunked_prefill_alibi, chunked_prefill_relbf16, kv_write")
     ap.add_argument("--splits", type=int, default=None,
                     help="override the planner's num_splits (0 = balanced decode) for the headline decode batch "
                          "(or for long_decode with --only long_decode)")
@@ -430,14 +430,18 @@ def main(argv=None):
             del r7, w7
             torch.cuda.empty_cache()
         for name, make, S_a in (("batched_decode_alibi", wl.batched_decode, 0),
-                                ("chunked_prefill_alibi", wl.chunked_prefill, 1)):
+                                ("chunked_prefill_alibi", wl.chunked_prefill, 1),
+                                ("chunked_prefill_relbf16", wl.chunked_prefill, 1)):
             if a.only not in (None, name):
                 continue
             wa = make(device="cpu").to(dev)
             ra = Runner(wa, S_a, pools=3 if S_a == 0 else 1)
             H = wa.num_heads
-            ra.alibi = torch.tensor([2.0 ** (-8.0 * (i + 1) / H) for i in range(H)], dtype=torch.float32,
-                                    device=dev)
+            if name.endswith("_alibi"):
+                ra.alibi = torch.tensor([2.0 ** (-8.0 * (i + 1) / H) for i in range(H)], dtype=torch.float32,
+                                        device=dev)
+            else:
+                wa.rel_logits = wa.rel_logits.to(torch.bfloat16)
             ms, ms_c, wk = measure(ra, max(5, a.steps // 2), a.warmup, SETTLE_S)
             results[name] = (wa, S_a, ms, ms_c, wk)
             log(f"{name}: {ms * 1e3:.1f} us/step, {wk['bytes'] / ms / 1e6:.1f} GB/s, "
@@ -460,6 +464,8 @@ def main(argv=None):
         extra = {}
         if name.endswith("_alibi"):
             extra = {"alibi_slopes": "2^(-8 (h + 1) / H)"}
+        if name.endswith("_relbf16"):
+            extra = {"rel_logits": "bf16"}
         if name.endswith("_fp8"):
             kern = ("attn_kernel<128, false, true>" if S == 1 else
                     "decode_heads_kernel<128, true, true> + combine_heads_kernel<128>")

@@ -4,7 +4,8 @@ bytes = K and V of every key visible to at least one row of a request, read
         once per kv head (2 * Hkv * D * kv_elem_bytes B per key: 2 for bf16
         caches, 1 for E4M3 caches)
       + q and out (bf16), lse (fp32)
-      + the rel_logits entries inside the bias band of visible keys (fp32)
+      + the rel_logits entries inside the bias band of visible keys (4 B each,
+        2 B when the workload's rel_logits are bf16)
       + one int32 block_table entry per page touched, and the length arrays.
 flops = 4 * D * (number of visible (query row, key) pairs) * H  (Q·Kᵀ and P·V;
         exp, bias and masking are not counted).
@@ -54,7 +55,9 @@ def work(w, kv_elem_bytes: int = 2) -> dict:
     T = sum(w.q_lens)
     qo_bytes = 2 * T * H * D * 2
     lse_bytes = T * H * 4
-    rel_bytes = band * H * 4
+    rel = getattr(w, "rel_logits", None)
+    rel_eb = 2 if rel is not None and str(getattr(rel, "dtype", "")) == "torch.bfloat16" else 4
+    rel_bytes = band * H * rel_eb
     meta_bytes = (2 * len(w.q_lens) + 1) * 4
     total = kv_bytes + qo_bytes + lse_bytes + rel_bytes + page_bytes + meta_bytes
     return {
