@@ -322,3 +322,28 @@ def test_fp8_full_size_batched_decode_sampled():
                                           sub.cu_seqlens_q, sub.softmax_scale, sub.causal, sub.window_size,
                                           sub.rel_extent, sub.rel_logits)
     _compare(out[qi], lse[qi], ref_out, ref_lse, "batched_decode fp8")
+
+
+@pytest.mark.parametrize("H,S", [(16, 0), (16, 1), (64, 1)])
+def test_fp8_every_code_decodes_exactly(H, S):
+    """One key per request: out = v exactly, so every E4M3 code (two kv heads
+    of head_dim 128 hold all 256) must come out as its value in bf16, bit for
+    bit (NaN codes as NaN), through the balanced decode (S=0), the split-mode
+    decode items (S=1, G=8) and the prefill tiles (G=32)."""
+    w = wl.build([1, 1], [1, 1], num_heads=H, num_kv_heads=2, head_dim=128, seed=27)
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    k8 = torch.full(w.key_cache.shape, 0x38, dtype=torch.uint8)  # keys 1.0: any finite score
+    v8 = torch.zeros(w.key_cache.shape, dtype=torch.uint8)
+    for b in range(2):
+        pg = int(w.block_table[b, 0])
+        v8[pg, 0] = codes.view(2, 128)
+    out, lse = _run_fp8(w, k8, v8, 1.0, 1.0, S=S)
+    want = ofp8.e4m3_decode(codes).view(2, 128)
+    G = H // 2
+    for tok in range(2):
+        for h in range(H):
+            got = out[tok, h]
+            exp = want[h // G]
+            nan = torch.isnan(exp)
+            assert torch.equal(torch.isnan(got), nan), f"tok {tok} head {h}: NaN pattern"
+            assert torch.equal(got[~nan], exp[~nan]), f"tok {tok} head {h}: decoded values differ"
