@@ -47,9 +47,11 @@ def kernel_hash() -> str:
 def load_traffic(workload: str):
     """HBM traffic per launch from committed rocprofv3 --pmc summaries, if they
     were taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
-    if not os.path.exists(path):
+    hits = [f for f in os.listdir(os.path.join(ROOT, "profiles")) if f.endswith(f"_{workload}_traffic.json")
+            and f[: -len(f"_{workload}_traffic.json")].endswith("_kernel")]
+    if len(hits) != 1:
         return None
+    path = os.path.join(ROOT, "profiles", hits[0])
     with open(path) as f:
         t = json.load(f)
     if t.get("kernel_hash") != kernel_hash():
