@@ -124,6 +124,16 @@ __device__ __forceinline__ void lds_write_b128x2_now(uint32_t a0, uint32_t a1, u
                : "v"(a0), "v"(a1), "v"(v0), "v"(v1)
                : "memory");
 }
+__device__ __forceinline__ void lds_write_b128x8_now(const uint32_t (&a)[8], const u32x4 (&v)[8]) {
+  asm volatile(
+      "ds_write_b128 %0, %8\n\tds_write_b128 %1, %9\n\tds_write_b128 %2, %10\n\tds_write_b128 %3, %11\n\t"
+      "ds_write_b128 %4, %12\n\tds_write_b128 %5, %13\n\tds_write_b128 %6, %14\n\tds_write_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      :
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(v[0]),
+        "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7])
+      : "memory");
+}
 __device__ __forceinline__ void lds_write_b128x4_now(const uint32_t (&a)[4], const u32x4 (&v)[4]) {
   asm volatile(
       "ds_write_b128 %0, %4\n\tds_write_b128 %1, %5\n\tds_write_b128 %2, %6\n\tds_write_b128 %3, %7\n\t"
@@ -936,6 +946,32 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
                            e4m3x8_to_bf16(raw[0][2], raw[0][3]));
     }
   };
+  // Both landings at once: the four (D = 128) raw reads go out together and
+  // the eight bf16 writes complete in one wait.
+  auto decode8_kv = [&](int k_slot_off, int v_slot_off) __attribute__((always_inline)) {
+    u32x4 rk[NI8], rv[NI8];
+#pragma unroll
+    for (int n = 0; n < NI8; ++n) rk[n] = lds_read_b128_asm(smem_u + L::land8K + (kbw + RPI8 * n) * D + 16 * lane);
+#pragma unroll
+    for (int n = 0; n < NI8; ++n) rv[n] = lds_read_b128_asm(smem_u + L::land8V + (kbw + RPI8 * n) * D + 16 * lane);
+    lgkm_wait_n<0>(rk);
+    lgkm_wait_n<0>(rv);
+    const uint32_t kb_ = smem_u + k_slot_off, vb_ = smem_u + v_slot_off;
+    if constexpr (NI8 == 2) {
+      const uint32_t a[8] = {kb_ + dst_k8[0], kb_ + dst_k8[1], kb_ + dst_k8[2], kb_ + dst_k8[3],
+                             vb_ + dst_v8[0], vb_ + dst_v8[1], vb_ + dst_v8[2], vb_ + dst_v8[3]};
+      const u32x4 vv[8] = {e4m3x8_to_bf16(rk[0][0], rk[0][1]), e4m3x8_to_bf16(rk[0][2], rk[0][3]),
+                           e4m3x8_to_bf16(rk[1][0], rk[1][1]), e4m3x8_to_bf16(rk[1][2], rk[1][3]),
+                           e4m3x8_to_bf16(rv[0][0], rv[0][1]), e4m3x8_to_bf16(rv[0][2], rv[0][3]),
+                           e4m3x8_to_bf16(rv[1][0], rv[1][1]), e4m3x8_to_bf16(rv[1][2], rv[1][3])};
+      lds_write_b128x8_now(a, vv);
+    } else {
+      const uint32_t a[4] = {kb_ + dst_k8[0], kb_ + dst_k8[1], vb_ + dst_v8[0], vb_ + dst_v8[1]};
+      const u32x4 vv[4] = {e4m3x8_to_bf16(rk[0][0], rk[0][1]), e4m3x8_to_bf16(rk[0][2], rk[0][3]),
+                           e4m3x8_to_bf16(rv[0][0], rv[0][1]), e4m3x8_to_bf16(rv[0][2], rv[0][3])};
+      lds_write_b128x4_now(a, vv);
+    }
+  };
   // The LDS writes of direct loads are tracked by vmcnt only: wait for them
   // before the barrier that publishes a tile.  When the 32 bias loads of a
   // later tile were issued after them, those may stay in flight.
@@ -1128,10 +1164,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       if (!band2) wait_vm0();
       else if (bias_fast) wait_vm8();
       else wait_vm32();
-      if constexpr (KV8) {
-        decode8(L::land8K, L::kOff(PAR), dst_k8);
-        decode8(L::land8V, L::vOff(1 - PAR), dst_v8);
-      }
+      if constexpr (KV8) decode8_kv(L::kOff(PAR), L::vOff(1 - PAR));
       barrier_raw();
       if (has_next) update_max(xor32_max(mx));
     };
