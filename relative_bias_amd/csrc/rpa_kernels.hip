@@ -903,7 +903,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   // wave decodes its rows into the tile's bf16 slot at the places the bf16
   // loads would have filled, so the rest of the pipeline is unchanged.
   constexpr int U8 = D / 16, RPI8 = 64 / U8, NI8 = 16 / RPI8;
-  uint32_t voff8[KV8 ? NI8 : 1], dst_k8[KV8 ? 2 * NI8 : 1], dst_v8[KV8 ? 2 * NI8 : 1];
+  uint32_t voff8[NI8], dst_k8[2 * NI8], dst_v8[2 * NI8];  // set and used for E4M3 caches only
   if constexpr (KV8) {
 #pragma unroll
     for (int n = 0; n < NI8; ++n) {
