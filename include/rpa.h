@@ -27,6 +27,10 @@
  *     kernels on `stream` (a hipStream_t; NULL = the default stream) and
  *     return.  Any error status is returned BEFORE anything is enqueued,
  *     except RPA_ERR_HIP, which reports a failed launch.
+ *   - Calls enqueue kernel launches only (no memset, copy, allocation or
+ *     host read of device data) and size their grids from host arguments
+ *     alone, so a call can be captured in a HIP graph and replayed after
+ *     the device-resident lengths, block table and inputs change in place.
  *   - bf16 means IEEE bfloat16 bit patterns (uint16 storage); outputs are
  *     rounded to nearest even from fp32.
  *   - Results are bitwise repeatable for fixed inputs and num_splits.
