@@ -272,6 +272,19 @@ def hbm_read_ceiling(gib=4, reps=10):
             "best_gbs": round(nbytes / min(times) / 1e6, 1), "median_gbs": round(nbytes / statistics.median(times) / 1e6, 1)}
 
 
+def cpu_baseline_one_thread(w, budget_s=4.0):
+    """The same oracle on one host thread (a shorter sample), for the
+    per-core rate."""
+    import torch
+    n = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        r = cpu_baseline(w, budget_s)
+    finally:
+        torch.set_num_threads(n)
+    return r
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The fp64 oracle on a bounded sample of the decode batch: whole requests
     in order, passing over the batch again until about budget_s of CPU time
@@ -538,6 +551,7 @@ def main(argv=None):
     if not a.no_cpu and head == "batched_decode":
         log("timing the CPU oracle on a sample ...")
         line["cpu_baseline"] = cpu_baseline(w)
+        line["cpu_baseline_one_thread"] = cpu_baseline_one_thread(w)
     line["kernel_hash"] = kernel_hash()
     print(json.dumps(line), flush=True)
     return 0
