@@ -161,3 +161,24 @@ def test_k_scale_multiplies_keys_only_and_v_scale_values_only():
     o4, l4 = fp8.attention_fp8(w.q, k8, v8, 1.0, 4.0, *args, w.softmax_scale, *tail)
     o5, l5 = fp8.attention_fp8(w.q, k8, v8, 1.0, 1.0, *args, w.softmax_scale, *tail)
     assert torch.allclose(o4, 4 * o5, atol=1e-12, rtol=0) and torch.equal(l4, l5)
+
+
+@pytest.mark.parametrize("x,scale_bits,two_step,direct", [
+    (50.25, 0x40EE38E4, 0x4E, 0x4D),
+    (57.0, 0x40EB5AD7, 0x50, 0x4F),
+])
+def test_quantize_rounds_the_fp32_quotient(x, scale_bits, two_step, direct):
+    """Reading F3: x / scale is rounded to fp32 first.  For these values the
+    exact quotient lies just below the midpoint of two E4M3 values and its
+    fp32 rounding lands on the midpoint, so rounding once from the exact
+    quotient would give the lower code (found by search, checked here with
+    exact rationals)."""
+    from fractions import Fraction
+    scale = float(np.array([scale_bits], dtype=np.uint32).view(np.float32)[0])
+    got = fp8.quantize(torch.tensor([x], dtype=torch.bfloat16), scale).item()
+    assert got == two_step
+    q = Fraction(x) / Fraction(scale)
+    lo, hi = fp8.e4m3_decode(torch.tensor([direct], dtype=torch.uint8)).item(), \
+        fp8.e4m3_decode(torch.tensor([two_step], dtype=torch.uint8)).item()
+    assert Fraction(lo) < q < (Fraction(lo) + Fraction(hi)) / 2  # exact rounding would give `direct`
+    assert float(np.float32(x) / np.float32(scale)) == (lo + hi) / 2  # the fp32 quotient is the midpoint

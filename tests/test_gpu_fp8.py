@@ -347,3 +347,24 @@ def test_fp8_every_code_decodes_exactly(H, S):
             nan = torch.isnan(exp)
             assert torch.equal(torch.isnan(got), nan), f"tok {tok} head {h}: NaN pattern"
             assert torch.equal(got[~nan], exp[~nan]), f"tok {tok} head {h}: decoded values differ"
+
+
+def test_kv_write_fp8_rounds_the_fp32_quotient():
+    """The two values whose exact quotient sits just below an E4M3 midpoint
+    while the fp32 quotient is the midpoint: the kernel's codes are the
+    oracle's (one fp32 division, then ties to even), not those of rounding
+    the exact quotient."""
+    import numpy as np
+    ks = float(np.array([0x40EE38E4], dtype=np.uint32).view(np.float32)[0])
+    vs = float(np.array([0x40EB5AD7], dtype=np.uint32).view(np.float32)[0])
+    key = torch.full((1, 1, 128), 50.25, dtype=torch.bfloat16)
+    val = torch.full((1, 1, 128), 57.0, dtype=torch.bfloat16)
+    slots = torch.zeros((1,), dtype=torch.int64)
+    kc = torch.zeros((1, 16, 1, 128), dtype=torch.uint8)
+    vc = torch.zeros_like(kc)
+    want_k, want_v = ofp8.kv_cache_write_fp8(key, val, slots, kc, vc, ks, vs)
+    assert int(want_k[0, 0, 0, 0]) == 0x4E and int(want_v[0, 0, 0, 0]) == 0x50
+    kg, vg = kc.cuda(), vc.cuda()
+    bnd.rpa_kv_cache_write_fp8(key.cuda(), val.cuda(), slots.cuda(), kg, vg, ks, vs)
+    torch.cuda.synchronize()
+    assert torch.equal(kg.cpu(), want_k) and torch.equal(vg.cpu(), want_v)
