@@ -118,3 +118,19 @@ def test_zero_slopes_are_no_alibi():
     o1, l1 = orc.attention(w.q, w.key_cache, w.value_cache, *_args(w), alibi_slopes=torch.zeros(4))
     o2, l2 = orc.attention(w.q, w.key_cache, w.value_cache, *_args(w))
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_alibi_equals_a_relative_bias_of_minus_slope_times_distance():
+    """Causal rows see only d = q_abs - t >= 0, so with a band that covers
+    every key (R >= Lk) ALiBi is the relative bias rel_logits[tok, h, d] =
+    -slope_h * d: two different code paths of the oracle must agree."""
+    w = wl.build([1, 6, 2], [60, 40, 9], num_heads=4, num_kv_heads=2, head_dim=16, seed=21)
+    sl = torch.tensor([0.5, 0.25, 0.125, 1.0], dtype=torch.float32)
+    R = 64
+    d = torch.arange(R, dtype=torch.float64)
+    rel = (-(sl.double()[None, :, None]) * d[None, None, :]).expand(w.num_tokens, 4, R).contiguous()
+    o1, l1 = orc.attention(w.q, w.key_cache, w.value_cache, w.block_table, w.cache_seqlens, w.cu_seqlens_q,
+                           w.softmax_scale, True, (-1, -1), 0, None, alibi_slopes=sl)
+    o2, l2 = orc.attention(w.q, w.key_cache, w.value_cache, w.block_table, w.cache_seqlens, w.cu_seqlens_q,
+                           w.softmax_scale, True, (-1, -1), R, rel)
+    assert torch.allclose(o1, o2, atol=1e-12, rtol=0) and torch.allclose(l1, l2, atol=1e-12, rtol=0)

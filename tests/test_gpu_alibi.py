@@ -98,3 +98,27 @@ def test_alibi_with_fp8_cache(S):
         rel_logits=wg.rel_logits, num_splits=S, return_lse=True, alibi_slopes=sl.cuda())
     torch.cuda.synchronize()
     _compare(out.float().cpu().double(), lse.cpu().double(), ref_out, ref_lse, f"fp8 alibi S={S}")
+
+
+@pytest.mark.parametrize("S", [0, 1])
+def test_alibi_matches_the_equivalent_relative_bias_on_gpu(S):
+    """With causal rows and a band covering every key, ALiBi equals the
+    relative bias -slope_h * d: the GPU's two bias paths agree with each
+    other and with the oracle."""
+    ql, kl = ([1] * 5, [100, 900, 37, 500, 1]) if S == 0 else ([1, 70, 1], [300, 200, 500])
+    w = wl.build(ql, kl, num_heads=16, num_kv_heads=8, head_dim=128, seed=35)
+    sl = _slopes(16, "geometric")
+    R = 1024
+    d = torch.arange(R, dtype=torch.float32)
+    rel = (-(sl[None, :, None]) * d[None, None, :]).expand(w.num_tokens, 16, R).contiguous()
+    wg = w.to("cuda")
+    a_out, a_lse = bnd.attn_workload(wg, num_splits=S, alibi_slopes=sl.cuda())
+    wg.rel_extent, wg.rel_logits = R, rel.cuda()
+    b_out, b_lse = bnd.attn_workload(wg, num_splits=S)
+    torch.cuda.synchronize()
+    assert (a_out.float() - b_out.float()).abs().max().item() <= 1e-2
+    assert (a_lse - b_lse).abs().max().item() <= 1e-3
+    ref_out, ref_lse = orc.attention(w.q, w.key_cache, w.value_cache, w.block_table, w.cache_seqlens,
+                                     w.cu_seqlens_q, w.softmax_scale, w.causal, w.window_size, 0, None,
+                                     alibi_slopes=sl)
+    _compare(a_out.float().cpu().double(), a_lse.cpu().double(), ref_out, ref_lse, f"alibi as rel S={S}")
