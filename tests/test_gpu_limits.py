@@ -1,6 +1,7 @@
-"""GPU parity at the size limits of the balanced decode: 2048 requests (the
-most its LDS prefix holds) and 2049 (num_splits = 0 then runs as one split),
-with bf16 and E4M3 caches, checked against the oracle on sampled requests."""
+"""GPU parity at size limits: the balanced decode at 2048 requests (the most
+its LDS prefix holds) and 2049 (num_splits = 0 then runs as one split), with
+bf16 and E4M3 caches, checked against the oracle on sampled requests; pages
+of up to 272 slots."""
 import pytest
 import torch
 
@@ -68,3 +69,20 @@ def test_balanced_decode_batch_limits(B, Hkv, fp8):
     idx = torch.tensor(sample, dtype=torch.long)
     _compare(out.float().cpu().double(), lse.cpu().double(), ref_out, ref_lse, idx,
              f"B={B} Hkv={Hkv} fp8={fp8}")
+
+
+@pytest.mark.parametrize("BS", [128, 256, 272])
+@pytest.mark.parametrize("S", [0, 1, 3])
+def test_large_block_sizes(BS, S):
+    """Pages of 128, 256 and 272 slots (272: not a power of two) on a mixed
+    batch, the balanced decode and split decode items, against the oracle."""
+    ql, kl = ([1, 1, 1, 1], [1, 300, 1000, 2700]) if S == 0 else ([1, 90, 1, 33], [2700, 300, 1, 600])
+    w = wl.build(ql, kl, num_heads=16, num_kv_heads=8, head_dim=128, block_size=BS, rel_extent=40, seed=60 + BS,
+                 extra_pages=1, poison=True)
+    ref_out, ref_lse = orc.attention(w.q, w.key_cache, w.value_cache, w.block_table, w.cache_seqlens,
+                                     w.cu_seqlens_q, w.softmax_scale, w.causal, w.window_size, w.rel_extent,
+                                     w.rel_logits)
+    out, lse = bnd.attn_workload(w.to("cuda"), num_splits=S)
+    torch.cuda.synchronize()
+    idx = torch.arange(w.num_tokens)
+    _compare(out.float().cpu().double(), lse.cpu().double(), ref_out, ref_lse, idx, f"BS={BS} S={S}")
