@@ -59,6 +59,20 @@ def load_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def load_mfma(workload: str):
+    """MFMA busy fraction and executed/algorithmic flop ratio from the
+    committed rocprofv3 counter summary of a prefill workload, if taken on
+    the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"attn_kernel_{workload}_mfma.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    return {"mfma_busy_fraction": t["mfma_busy_fraction"], "executed_over_algorithmic": t["executed_over_algorithmic"]}
+
+
 def time_calls(fn, steps, warmup, stream):
     import torch
     for _ in range(warmup):
@@ -493,7 +507,8 @@ def main(argv=None):
                 "gbs": round(wk["bytes"] / ms / 1e6, 2), "tflops": round(wk["flops"] / ms / 1e9, 2),
                 "hbm_frac": round(wk["bytes"] / ms / 1e6 / HBM_PEAK_GBS, 4),
                 "mfma_frac": round(wk["flops"] / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
-                "alg_bytes": wk["bytes"], "alg_flops": wk["flops"]}
+                "alg_bytes": wk["bytes"], "alg_flops": wk["flops"],
+                **({"mfma_counters": load_mfma(name)} if load_mfma(name) else {})}
 
     if a.only == "kv_write":
         print(json.dumps({"kv_write": kv_summary, "kernel_hash": kernel_hash()}))
