@@ -137,7 +137,10 @@ size_t rpa_workspace_bytes(int32_t num_splits, int32_t num_tokens, int32_t num_h
  * PagedAttention V2", dev.modelhub.org.cn, with NORMALISED partials):
  *     M = max_s lse_s,  LSE = M + ln sum_s exp(lse_s - M),
  *     out = sum_s exp(lse_s - LSE) * o_s;
- * rows whose every lse_s is -inf give out = 0, lse = -inf.
+ * rows whose every lse_s is -inf give out = 0, lse = -inf.  A split whose
+ * weight exp(lse_s - LSE) is 0 (lse_s = -inf: an empty chunk) is skipped, so
+ * its partial_out row may hold any value, NaN included.  Every lse_s must be
+ * finite or -inf (+inf and NaN are outside the contract).
  *
  *   partial_out  fp32 [num_splits, num_tokens, num_heads, head_dim]
  *   partial_lse  fp32 [num_splits, num_tokens, num_heads], natural log

@@ -119,29 +119,25 @@ def rpa_choose_splits(batch: int, max_seqlen_q: int, num_heads: int, num_kv_head
     return s
 
 
-def rpa_attn_varlen(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor, *,
-                    block_table: torch.Tensor, cache_seqlens: torch.Tensor,
-                    cu_seqlens_q: torch.Tensor, max_seqlen_q: int, softmax_scale: float,
-                    causal: bool = True, window_size: Tuple[int, int] = (-1, -1),
-                    rel_extent: int = 0, rel_logits: Optional[torch.Tensor] = None,
-                    num_splits: Optional[int] = None, max_seqlen_k: Optional[int] = None,
-                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                    return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
-                    alibi_slopes: Optional[torch.Tensor] = None):
-    """Paged varlen causal attention with the additive relative bias
-    (rel_logits fp32 or bf16; optional ALiBi slopes, fp32 [H]: both through
-    rpa_attn_varlen_ex).
+def _attn(where: str, kv8: bool, k_scale: float, v_scale: float, q, key_cache, value_cache, block_table,
+          cache_seqlens, cu_seqlens_q, max_seqlen_q, softmax_scale, causal, window_size, rel_extent, rel_logits,
+          num_splits, max_seqlen_k, out, lse, return_lse, workspace, alibi_slopes):
+    """Checks shared by both attention wrappers, then the C call.
 
-    Returns ``out`` (bf16 [T, H, D]), or ``(out, lse)`` when ``return_lse``
-    or an ``lse`` tensor is given.  ``num_splits=None`` uses
-    rpa_choose_splits, which needs ``max_seqlen_k`` (host int) to be given.
-    """
+    Every tensor is checked for dtype, device, contiguity and shape before
+    anything is launched: the kernels write T*H*D bf16 values to ``out`` and
+    T*H fp32 values to ``lse``, so a buffer of another shape is refused here
+    rather than written past its end."""
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("q must be a GPU tensor")
     _check(q, "q", torch.bfloat16, dev, 3)
-    _check(key_cache, "key_cache", torch.bfloat16, dev, 4)
-    _check(value_cache, "value_cache", torch.bfloat16, dev, 4)
+    if kv8:
+        key_cache = _fp8_cache(key_cache, "key_cache", dev)
+        value_cache = _fp8_cache(value_cache, "value_cache", dev)
+    else:
+        _check(key_cache, "key_cache", torch.bfloat16, dev, 4)
+        _check(value_cache, "value_cache", torch.bfloat16, dev, 4)
     if key_cache.shape != value_cache.shape:
         raise ValueError("key_cache and value_cache shapes differ")
     _check(block_table, "block_table", torch.int32, dev, 2)
@@ -172,35 +168,62 @@ def rpa_attn_varlen(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
     if out is None:
         out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
     _check(out, "out", torch.bfloat16, dev, 3)
+    if tuple(out.shape) != (T, H, D):
+        raise ValueError(f"out must be {(T, H, D)}, got {tuple(out.shape)}")
     want_lse = return_lse or lse is not None
     if want_lse and lse is None:
         lse = torch.empty((T, H), dtype=torch.float32, device=dev)
     if lse is not None:
         _check(lse, "lse", torch.float32, dev, 2)
+        if tuple(lse.shape) != (T, H):
+            raise ValueError(f"lse must be {(T, H)}, got {tuple(lse.shape)}")
     ws_bytes = rpa_workspace_bytes(S, T, H, D) if S != 1 else 0
     if ws_bytes and workspace is None:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+    ws_given = 0 if workspace is None else workspace.numel() * workspace.element_size()
     alibi = _alibi(alibi_slopes, H, dev)
     rel_bf16 = int(R > 0 and rel_logits.dtype == torch.bfloat16)
-    if alibi is None and not rel_bf16:
-        st = lib().rpa_attn_varlen(
-            _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(block_table), block_table.shape[1],
-            _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB, BS, int(max_seqlen_q),
-            float(softmax_scale), int(bool(causal)), int(window_size[0]), int(window_size[1]), R,
-            _ptr(rel_logits) if R > 0 else None, S, _ptr(workspace),
-            0 if workspace is None else workspace.numel() * workspace.element_size(),
-            _ptr(out), _ptr(lse), _stream(dev))
+    rel = _ptr(rel_logits) if R > 0 else None
+    caches = (_ptr(q), _ptr(key_cache), _ptr(value_cache))
+    meta = (_ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB,
+            BS, int(max_seqlen_q), float(softmax_scale), int(bool(causal)), int(window_size[0]),
+            int(window_size[1]), R)
+    tail = (S, _ptr(workspace), ws_given, _ptr(out), _ptr(lse), _stream(dev))
+    L = lib()
+    if alibi is not None or rel_bf16:
+        st = L.rpa_attn_varlen_ex(*caches, int(kv8), float(k_scale), float(v_scale), *meta, rel, rel_bf16,
+                                  _ptr(alibi), *tail)
+    elif kv8:
+        st = L.rpa_attn_varlen_fp8(*caches, float(k_scale), float(v_scale), *meta, rel, *tail)
     else:
-        st = lib().rpa_attn_varlen_ex(
-            _ptr(q), _ptr(key_cache), _ptr(value_cache), 0, 1.0, 1.0, _ptr(block_table), block_table.shape[1],
-            _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB, BS, int(max_seqlen_q),
-            float(softmax_scale), int(bool(causal)), int(window_size[0]), int(window_size[1]), R,
-            _ptr(rel_logits) if R > 0 else None, rel_bf16, _ptr(alibi), S, _ptr(workspace),
-            0 if workspace is None else workspace.numel() * workspace.element_size(),
-            _ptr(out), _ptr(lse), _stream(dev))
+        st = L.rpa_attn_varlen(*caches, *meta, rel, *tail)
     if st != RPA_OK:
-        raise RpaError(st, "rpa_attn_varlen")
+        raise RpaError(st, where)
     return (out, lse) if want_lse else out
+
+
+def rpa_attn_varlen(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor, *,
+                    block_table: torch.Tensor, cache_seqlens: torch.Tensor,
+                    cu_seqlens_q: torch.Tensor, max_seqlen_q: int, softmax_scale: float,
+                    causal: bool = True, window_size: Tuple[int, int] = (-1, -1),
+                    rel_extent: int = 0, rel_logits: Optional[torch.Tensor] = None,
+                    num_splits: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
+                    alibi_slopes: Optional[torch.Tensor] = None):
+    """Paged varlen causal attention with the additive relative bias
+    (rel_logits fp32 or bf16; optional ALiBi slopes, fp32 [H]: both through
+    rpa_attn_varlen_ex).
+
+    Returns ``out`` (bf16 [T, H, D]), or ``(out, lse)`` when ``return_lse``
+    or an ``lse`` tensor is given.  ``num_splits=None`` uses
+    rpa_choose_splits, which needs ``max_seqlen_k`` (host int) to be given.
+    """
+    return _attn("rpa_attn_varlen", False, 1.0, 1.0, q, key_cache, value_cache, block_table, cache_seqlens,
+                 cu_seqlens_q, max_seqlen_q, softmax_scale, causal, window_size, rel_extent, rel_logits,
+                 num_splits, max_seqlen_k, out, lse, return_lse, workspace, alibi_slopes)
 
 
 def _fp8_cache(t: torch.Tensor, name: str, device) -> torch.Tensor:
@@ -216,71 +239,15 @@ def rpa_attn_varlen_fp8(q: torch.Tensor, key_cache: torch.Tensor, value_cache: t
                         cu_seqlens_q: torch.Tensor, max_seqlen_q: int, softmax_scale: float,
                         causal: bool = True, window_size: Tuple[int, int] = (-1, -1),
                         rel_extent: int = 0, rel_logits: Optional[torch.Tensor] = None,
-                        num_splits: int = 0, out: Optional[torch.Tensor] = None,
-                        lse: Optional[torch.Tensor] = None, return_lse: bool = False,
-                        workspace: Optional[torch.Tensor] = None, alibi_slopes: Optional[torch.Tensor] = None):
+                        num_splits: Optional[int] = 0, max_seqlen_k: Optional[int] = None,
+                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                        return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
+                        alibi_slopes: Optional[torch.Tensor] = None):
     """rpa_attn_varlen over E4M3 caches (uint8 codes or float8_e4m3fn) with
     per-cache scales: k = e4m3(code) * k_scale, v = e4m3(code) * v_scale."""
-    dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("q must be a GPU tensor")
-    _check(q, "q", torch.bfloat16, dev, 3)
-    key_cache = _fp8_cache(key_cache, "key_cache", dev)
-    value_cache = _fp8_cache(value_cache, "value_cache", dev)
-    if key_cache.shape != value_cache.shape:
-        raise ValueError("key_cache and value_cache shapes differ")
-    _check(block_table, "block_table", torch.int32, dev, 2)
-    _check(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
-    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, 1)
-    T, H, D = q.shape
-    NB, BS, Hkv, Dk = key_cache.shape
-    if Dk != D:
-        raise ValueError("head_dim of q and the caches differ")
-    B = cache_seqlens.shape[0]
-    if cu_seqlens_q.shape[0] != B + 1 or block_table.shape[0] != B:
-        raise ValueError("batch sizes of cu_seqlens_q / block_table / cache_seqlens disagree")
-    R = int(rel_extent)
-    if R > 0:
-        if rel_logits is None:
-            raise ValueError("rel_extent > 0 needs rel_logits")
-        rel_logits = rel_logits.contiguous()
-        _check(rel_logits, "rel_logits", torch.bfloat16 if rel_logits.dtype == torch.bfloat16 else torch.float32,
-               dev, 3)
-        if tuple(rel_logits.shape) != (T, H, R):
-            raise ValueError(f"rel_logits must be {(T, H, R)}, got {tuple(rel_logits.shape)}")
-    S = int(num_splits)
-    if out is None:
-        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
-    _check(out, "out", torch.bfloat16, dev, 3)
-    want_lse = return_lse or lse is not None
-    if want_lse and lse is None:
-        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
-    if lse is not None:
-        _check(lse, "lse", torch.float32, dev, 2)
-    ws_bytes = rpa_workspace_bytes(S, T, H, D) if S != 1 else 0
-    if ws_bytes and workspace is None:
-        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
-    alibi = _alibi(alibi_slopes, H, dev)
-    rel_bf16 = int(R > 0 and rel_logits.dtype == torch.bfloat16)
-    if alibi is None and not rel_bf16:
-        st = lib().rpa_attn_varlen_fp8(
-            _ptr(q), _ptr(key_cache), _ptr(value_cache), float(k_scale), float(v_scale), _ptr(block_table),
-            block_table.shape[1], _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB, BS,
-            int(max_seqlen_q), float(softmax_scale), int(bool(causal)), int(window_size[0]), int(window_size[1]),
-            R, _ptr(rel_logits) if R > 0 else None, S, _ptr(workspace),
-            0 if workspace is None else workspace.numel() * workspace.element_size(),
-            _ptr(out), _ptr(lse), _stream(dev))
-    else:
-        st = lib().rpa_attn_varlen_ex(
-            _ptr(q), _ptr(key_cache), _ptr(value_cache), 1, float(k_scale), float(v_scale), _ptr(block_table),
-            block_table.shape[1], _ptr(cache_seqlens), _ptr(cu_seqlens_q), B, T, H, Hkv, D, NB, BS,
-            int(max_seqlen_q), float(softmax_scale), int(bool(causal)), int(window_size[0]), int(window_size[1]),
-            R, _ptr(rel_logits) if R > 0 else None, rel_bf16, _ptr(alibi), S, _ptr(workspace),
-            0 if workspace is None else workspace.numel() * workspace.element_size(),
-            _ptr(out), _ptr(lse), _stream(dev))
-    if st != RPA_OK:
-        raise RpaError(st, "rpa_attn_varlen_fp8")
-    return (out, lse) if want_lse else out
+    return _attn("rpa_attn_varlen_fp8", True, k_scale, v_scale, q, key_cache, value_cache, block_table,
+                 cache_seqlens, cu_seqlens_q, max_seqlen_q, softmax_scale, causal, window_size, rel_extent,
+                 rel_logits, num_splits, max_seqlen_k, out, lse, return_lse, workspace, alibi_slopes)
 
 
 def rpa_kv_cache_write_fp8(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,
@@ -322,6 +289,8 @@ def rpa_split_combine(partial_out: torch.Tensor, partial_lse: torch.Tensor,
         lse = torch.empty((T, H), dtype=torch.float32, device=dev)
     _check(out, "out", torch.bfloat16, dev, 3)
     _check(lse, "lse", torch.float32, dev, 2)
+    if tuple(out.shape) != (T, H, D) or tuple(lse.shape) != (T, H):
+        raise ValueError(f"out must be {(T, H, D)} and lse {(T, H)}, got {tuple(out.shape)} and {tuple(lse.shape)}")
     st = lib().rpa_split_combine(_ptr(partial_out), _ptr(partial_lse), S, T, H, D, _ptr(out),
                                  _ptr(lse), _stream(dev))
     if st != RPA_OK:
@@ -330,9 +299,14 @@ def rpa_split_combine(partial_out: torch.Tensor, partial_lse: torch.Tensor,
 
 
 def rpa_slot_mapping(block_table: torch.Tensor, cache_seqlens: torch.Tensor, cu_seqlens_q: torch.Tensor,
-                     block_size: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     block_size: int, out: Optional[torch.Tensor] = None,
+                     num_tokens: Optional[int] = None) -> torch.Tensor:
     """Cache slot (int64) of every packed query token; -1 where a request has
-    fewer keys than queries."""
+    fewer keys than queries.
+
+    The token count is a host value: pass ``out`` (int64 [T]) or
+    ``num_tokens``.  It is never read back from ``cu_seqlens_q`` on the
+    device, so the call stays asynchronous and can be captured in a graph."""
     dev = cu_seqlens_q.device
     _check(block_table, "block_table", torch.int32, dev, 2)
     _check(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
@@ -340,9 +314,13 @@ def rpa_slot_mapping(block_table: torch.Tensor, cache_seqlens: torch.Tensor, cu_
     B = cache_seqlens.shape[0]
     if cu_seqlens_q.shape[0] != B + 1 or block_table.shape[0] != B:
         raise ValueError("batch sizes of block_table / cache_seqlens / cu_seqlens_q disagree")
-    T = int(cu_seqlens_q[-1].item()) if out is None else out.shape[0]
     if out is None:
-        out = torch.empty((T,), dtype=torch.int64, device=dev)
+        if num_tokens is None:
+            raise ValueError("rpa_slot_mapping needs out or num_tokens (the host-side token count)")
+        out = torch.empty((int(num_tokens),), dtype=torch.int64, device=dev)
+    elif num_tokens is not None and out.shape[0] != int(num_tokens):
+        raise ValueError(f"out holds {out.shape[0]} slots, num_tokens is {num_tokens}")
+    T = out.shape[0]
     _check(out, "slot_mapping", torch.int64, dev, 1)
     st = lib().rpa_slot_mapping(_ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), _ptr(cu_seqlens_q),
                                 B, T, block_size, _ptr(out), _stream(dev))

@@ -2951,9 +2951,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   wts[w][lane] = e0 * invW;
   wts[w][lane + 64] = e1 * invW;
   wave_lds_sync();
+  // A split with weight 0 (an empty chunk, lse = -inf, or one whose weight
+  // underflows) is skipped, not multiplied: its partial may hold anything,
+  // NaN included, without reaching the output.
   for (int d = lane; d < p.D; d += 64) {
     float acc = 0.f;
-    for (int s = 0; s < p.S; ++s) acc += wts[w][s] * p.part_out[((int64_t)s * p.rows + row) * p.D + d];
+#pragma unroll 8
+    for (int s = 0; s < p.S; ++s) {
+      const float wt = wts[w][s];
+      const float v = p.part_out[((int64_t)s * p.rows + row) * p.D + d];
+      acc += wt != 0.f ? wt * v : 0.f;
+    }
     op[d] = __builtin_bit_cast(uint16_t, (__bf16)acc);
   }
   if (lane == 0 && p.lse) p.lse[row] = M + log2_fast(W) * kLn2;

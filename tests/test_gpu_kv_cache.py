@@ -26,7 +26,7 @@ def test_slot_mapping_matches_oracle(name):
     w = wl.build(ql, kl, num_heads=2, num_kv_heads=1, head_dim=64, block_size=BS, seed=5)
     want = okv.slot_mapping(w.block_table, w.k_lens, w.cu_seqlens_q.tolist(), BS)
     wg = w.to("cuda")
-    got = bnd.rpa_slot_mapping(wg.block_table, wg.cache_seqlens, wg.cu_seqlens_q, BS)
+    got = bnd.rpa_slot_mapping(wg.block_table, wg.cache_seqlens, wg.cu_seqlens_q, BS, num_tokens=w.num_tokens)
     torch.cuda.synchronize()
     assert torch.equal(got.cpu(), want)
 
@@ -39,7 +39,7 @@ def test_slot_mapping_many_requests():
     w = wl.build(ql, kl, num_heads=2, num_kv_heads=1, head_dim=64, block_size=16, seed=6)
     want = okv.slot_mapping(w.block_table, w.k_lens, w.cu_seqlens_q.tolist(), 16)
     wg = w.to("cuda")
-    got = bnd.rpa_slot_mapping(wg.block_table, wg.cache_seqlens, wg.cu_seqlens_q, 16)
+    got = bnd.rpa_slot_mapping(wg.block_table, wg.cache_seqlens, wg.cu_seqlens_q, 16, num_tokens=w.num_tokens)
     torch.cuda.synchronize()
     assert torch.equal(got.cpu(), want)
 
@@ -82,7 +82,7 @@ def test_kv_cache_write_chunked_prefill_shape():
     slots = okv.slot_mapping(w.block_table, w.k_lens, w.cu_seqlens_q.tolist(), 16)
     want_k, want_v = okv.kv_cache_write(key, val, slots, w.key_cache, w.value_cache)
     wg = w.to("cuda")
-    got_slots = bnd.rpa_slot_mapping(wg.block_table, wg.cache_seqlens, wg.cu_seqlens_q, 16)
+    got_slots = bnd.rpa_slot_mapping(wg.block_table, wg.cache_seqlens, wg.cu_seqlens_q, 16, num_tokens=T)
     bnd.rpa_kv_cache_write(key.cuda(), val.cuda(), got_slots, wg.key_cache, wg.value_cache)
     torch.cuda.synchronize()
     assert torch.equal(got_slots.cpu(), slots)
@@ -97,7 +97,8 @@ def test_write_then_attend_reproduces_the_cache():
                  rel_extent=32, seed=8)
     wg = w.to("cuda")
     ref_out, ref_lse = bnd.attn_workload(wg, num_splits=1)
-    slots = bnd.rpa_slot_mapping(wg.block_table, wg.cache_seqlens, wg.cu_seqlens_q, w.block_size)
+    slots = bnd.rpa_slot_mapping(wg.block_table, wg.cache_seqlens, wg.cu_seqlens_q, w.block_size,
+                                 num_tokens=w.num_tokens)
     torch.cuda.synchronize()
     s = slots.cpu()
     bs = w.block_size

@@ -223,6 +223,47 @@ def test_split_combine_entry_point():
     _compare(out.float().cpu().double(), lse.cpu().double(), ref_o, ref_l, tag="combine")
 
 
+def test_split_combine_ignores_nan_in_empty_splits():
+    """A split with lse = -inf has weight 0: its partial row is skipped, so a
+    NaN there (external partials need not zero their empty splits) does not
+    reach the output."""
+    g = torch.Generator().manual_seed(4)
+    S, T, H, D = 6, 9, 4, 128
+    po = torch.randn((S, T, H, D), generator=g, dtype=torch.float32)
+    pl = 2 * torch.randn((S, T, H), generator=g, dtype=torch.float32)
+    pl[:, 0, 0] = -math.inf       # every split empty
+    pl[1:, 1, 1] = -math.inf      # one split only
+    pl[::2, 3] = -math.inf        # every other split of a token
+    empty = pl == -math.inf
+    clean = po.clone()
+    clean[empty] = 0
+    ref_o, ref_l = orc.combine(clean.double(), pl.double())
+    po[empty] = math.nan
+    out, lse = bnd.rpa_split_combine(po.cuda(), pl.cuda())
+    torch.cuda.synchronize()
+    _compare(out.float().cpu().double(), lse.cpu().double(), ref_o, ref_l, tag="combine with NaN partials")
+
+
+def test_wrappers_refuse_wrong_output_shapes():
+    """Caller-supplied out / lse of another shape are refused before any
+    launch (the kernels would write T*H*D and T*H values)."""
+    w = wl.build([1, 3], [40, 70], num_heads=4, num_kv_heads=2, head_dim=64, rel_extent=8, seed=2)
+    wg = w.to("cuda")
+    T, H, D = w.q.shape
+    small_out = torch.empty((T - 1, H, D), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="out must be"):
+        bnd.attn_workload(wg, num_splits=1, out=small_out)
+    small_lse = torch.empty((T, H - 1), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="lse must be"):
+        bnd.attn_workload(wg, num_splits=1, lse=small_lse)
+    po = torch.zeros((2, T, H, D), device="cuda")
+    pl = torch.zeros((2, T, H), device="cuda")
+    with pytest.raises(ValueError, match="out must be"):
+        bnd.rpa_split_combine(po, pl, out=small_out)
+    with pytest.raises(ValueError, match="needs out or num_tokens"):
+        bnd.rpa_slot_mapping(wg.block_table, wg.cache_seqlens, wg.cu_seqlens_q, 16)
+
+
 # --------------------------------------------------------------- invariants
 
 def test_bitwise_repeatable_and_page_permutation_exact():
