@@ -22,7 +22,8 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers to contiguous row-major data
  *     on the current HIP device; the caller owns them.  The library
- *     allocates nothing and keeps no state between calls.
+ *     allocates nothing and keeps no state between calls, except the static
+ *     scratch array of rpa_attn_varlen_noalloc (below).
  *   - Calls are asynchronous: they validate host-visible arguments, enqueue
  *     kernels on `stream` (a hipStream_t; NULL = the default stream) and
  *     return.  Any error status is returned BEFORE anything is enqueued,
@@ -277,6 +278,43 @@ int rpa_attn_varlen_ex(const void *q, const void *key_cache, const void *value_c
                        int32_t rel_extent, const void *rel_logits, int rel_logits_bf16,
                        const float *alibi_slopes, int32_t num_splits, void *workspace,
                        size_t workspace_bytes, void *out, float *lse, void *stream);
+
+/*
+ * rpa_attn_varlen_noalloc: rpa_attn_varlen_ex without the workspace
+ * arguments, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * It calls no allocating routine.  The workspace it needs (num_splits > 1
+ * partials, or the balanced decode's records and partial slots) is a static
+ * device array of RPA_NOALLOC_SCRATCH_BYTES that every GPU loading the
+ * library holds until the process ends; its address is looked up once per
+ * device, on that device's first call that needs it.
+ *
+ * Limit: the call returns RPA_ERR_WORKSPACE, before anything is enqueued,
+ * when it needs more than RPA_NOALLOC_SCRATCH_BYTES: for num_splits > 1,
+ * num_splits * num_tokens * num_heads * (head_dim + 1) * 4 bytes (rounded up
+ * to 256); for the balanced decode (num_splits = 0 on a decode batch),
+ * 16 KiB + (compute units of the device) * 16 * 16 * (head_dim + 1) * 4
+ * bytes, about 34 MB for head_dim 128 on 256 compute units.  num_splits = 1
+ * needs no workspace.
+ *
+ * Every call on one GPU shares that GPU's array, and nothing in it needs to
+ * start at zero.  Calls that overlap on one GPU (on different streams, or
+ * from different host threads without ordering) race on the array and give
+ * undefined results; calls serialised on one stream do not.  Every other
+ * argument, the result and the error behaviour are those of
+ * rpa_attn_varlen_ex with the same num_splits.
+ */
+#define RPA_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+int rpa_attn_varlen_noalloc(const void *q, const void *key_cache, const void *value_cache, int kv_e4m3,
+                            float k_scale, float v_scale, const int32_t *block_table,
+                            int32_t max_pages_per_seq, const int32_t *cache_seqlens,
+                            const int32_t *cu_seqlens_q, int32_t batch, int32_t num_tokens,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t num_blocks, int32_t block_size, int32_t max_seqlen_q,
+                            float softmax_scale, int causal, int32_t window_left,
+                            int32_t window_right, int32_t rel_extent, const void *rel_logits,
+                            int rel_logits_bf16, const float *alibi_slopes, int32_t num_splits,
+                            void *out, float *lse, void *stream);
 
 /*
  * rpa_kv_cache_write_fp8: rpa_kv_cache_write into E4M3 caches.  Element x of

@@ -71,6 +71,10 @@ def lib():
                                      i32, i32, i32, f32, ctypes.c_int, i32, i32, i32, vp, ctypes.c_int, vp, i32, vp,
                                      sz, vp, vp, vp]
     L.rpa_attn_varlen_ex.restype = ctypes.c_int
+    L.rpa_attn_varlen_noalloc.argtypes = [vp, vp, vp, ctypes.c_int, f32, f32, vp, i32, vp, vp, i32, i32, i32, i32,
+                                          i32, i32, i32, i32, f32, ctypes.c_int, i32, i32, i32, vp, ctypes.c_int, vp,
+                                          i32, vp, vp, vp]
+    L.rpa_attn_varlen_noalloc.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -121,13 +125,21 @@ def rpa_choose_splits(batch: int, max_seqlen_q: int, num_heads: int, num_kv_head
 
 def _attn(where: str, kv8: bool, k_scale: float, v_scale: float, q, key_cache, value_cache, block_table,
           cache_seqlens, cu_seqlens_q, max_seqlen_q, softmax_scale, causal, window_size, rel_extent, rel_logits,
-          num_splits, max_seqlen_k, out, lse, return_lse, workspace, alibi_slopes):
-    """Checks shared by both attention wrappers, then the C call.
+          num_splits, max_seqlen_k, out, lse, return_lse, workspace, alibi_slopes, noalloc=False):
+    """Checks shared by the attention wrappers, then the C call.
 
     Every tensor is checked for dtype, device, contiguity and shape before
     anything is launched: the kernels write T*H*D bf16 values to ``out`` and
     T*H fp32 values to ``lse``, so a buffer of another shape is refused here
-    rather than written past its end."""
+    rather than written past its end.  ``noalloc`` calls
+    rpa_attn_varlen_noalloc and allocates nothing: ``out`` must be given."""
+    if noalloc:
+        if out is None:
+            raise ValueError(f"{where} allocates nothing: pass out (and lse to get the LSE)")
+        if workspace is not None:
+            raise ValueError(f"{where} takes no workspace (it uses the library's static scratch)")
+        if return_lse and lse is None:
+            raise ValueError(f"{where} allocates nothing: pass lse to get the LSE")
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("q must be a GPU tensor")
@@ -154,6 +166,8 @@ def _attn(where: str, kv8: bool, k_scale: float, v_scale: float, q, key_cache, v
     if R > 0:
         if rel_logits is None:
             raise ValueError("rel_extent > 0 needs rel_logits")
+        if noalloc and not rel_logits.is_contiguous():
+            raise ValueError(f"{where} allocates nothing: rel_logits must be contiguous")
         rel_logits = rel_logits.contiguous()  # the walkthrough's wrapper does the same
         _check(rel_logits, "rel_logits", torch.bfloat16 if rel_logits.dtype == torch.bfloat16 else torch.float32,
                dev, 3)
@@ -177,7 +191,7 @@ def _attn(where: str, kv8: bool, k_scale: float, v_scale: float, q, key_cache, v
         _check(lse, "lse", torch.float32, dev, 2)
         if tuple(lse.shape) != (T, H):
             raise ValueError(f"lse must be {(T, H)}, got {tuple(lse.shape)}")
-    ws_bytes = rpa_workspace_bytes(S, T, H, D) if S != 1 else 0
+    ws_bytes = rpa_workspace_bytes(S, T, H, D) if S != 1 and not noalloc else 0
     if ws_bytes and workspace is None:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
     if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
@@ -192,7 +206,10 @@ def _attn(where: str, kv8: bool, k_scale: float, v_scale: float, q, key_cache, v
             int(window_size[1]), R)
     tail = (S, _ptr(workspace), ws_given, _ptr(out), _ptr(lse), _stream(dev))
     L = lib()
-    if alibi is not None or rel_bf16:
+    if noalloc:
+        st = L.rpa_attn_varlen_noalloc(*caches, int(kv8), float(k_scale), float(v_scale), *meta, rel, rel_bf16,
+                                       _ptr(alibi), S, _ptr(out), _ptr(lse), _stream(dev))
+    elif alibi is not None or rel_bf16:
         st = L.rpa_attn_varlen_ex(*caches, int(kv8), float(k_scale), float(v_scale), *meta, rel, rel_bf16,
                                   _ptr(alibi), *tail)
     elif kv8:
@@ -224,6 +241,26 @@ def rpa_attn_varlen(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
     return _attn("rpa_attn_varlen", False, 1.0, 1.0, q, key_cache, value_cache, block_table, cache_seqlens,
                  cu_seqlens_q, max_seqlen_q, softmax_scale, causal, window_size, rel_extent, rel_logits,
                  num_splits, max_seqlen_k, out, lse, return_lse, workspace, alibi_slopes)
+
+
+def rpa_attn_varlen_noalloc(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor, *,
+                            out: torch.Tensor, block_table: torch.Tensor, cache_seqlens: torch.Tensor,
+                            cu_seqlens_q: torch.Tensor, max_seqlen_q: int, softmax_scale: float,
+                            causal: bool = True, window_size: Tuple[int, int] = (-1, -1), rel_extent: int = 0,
+                            rel_logits: Optional[torch.Tensor] = None, num_splits: int = 0,
+                            lse: Optional[torch.Tensor] = None, kv_e4m3: bool = False, k_scale: float = 1.0,
+                            v_scale: float = 1.0, alibi_slopes: Optional[torch.Tensor] = None):
+    """rpa_attn_varlen_ex without a workspace or any allocation (the library's
+    static per-device scratch holds the split partials): for callers that
+    cannot allocate.  ``out`` (and ``lse`` when wanted) are the caller's; E4M3
+    caches are passed with ``kv_e4m3=True`` and their scales.  Returns ``out``,
+    or ``(out, lse)`` when ``lse`` is given."""
+    if kv_e4m3:
+        key_cache = _fp8_cache(key_cache, "key_cache", q.device)
+        value_cache = _fp8_cache(value_cache, "value_cache", q.device)
+    return _attn("rpa_attn_varlen_noalloc", bool(kv_e4m3), k_scale, v_scale, q, key_cache, value_cache,
+                 block_table, cache_seqlens, cu_seqlens_q, max_seqlen_q, softmax_scale, causal, window_size,
+                 rel_extent, rel_logits, num_splits, None, out, lse, False, None, alibi_slopes, noalloc=True)
 
 
 def _fp8_cache(t: torch.Tensor, name: str, device) -> torch.Tensor:

@@ -96,14 +96,25 @@ int rpa_split_combine(const float *partial_out, const float *partial_lse, int32_
 
 namespace {
 
-// Both attention entry points: kv8 selects E4M3 caches with their scales.
+// Workspace of the balanced decode with `wgs` workgroups: the per-workgroup
+// records (sized for kBalMaxWGs), then two partial slots per workgroup.
+size_t bal_workspace_bytes(int wgs, int head_dim) {
+  return round_up(rpa::bal_desc_bytes() + rpa::bal_part_bytes(head_dim, wgs), kAlign);
+}
+
+// Every attention entry point: kv8 selects E4M3 caches with their scales.
+// use_scratch (rpa_attn_varlen_noalloc): the workspace is the current
+// device's static scratch array, looked up after every argument check and
+// only when the call needs a workspace; its size is checked against what
+// the call needs on this device.
 int attn_impl(const void *q, const void *key_cache, const void *value_cache, bool kv8, float k_scale,
               float v_scale, const int32_t *block_table, int32_t max_pages_per_seq,
               const int32_t *cache_seqlens, const int32_t *cu_seqlens_q, int32_t batch, int32_t num_tokens,
               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
               int32_t max_seqlen_q, float softmax_scale, int causal, int32_t window_left, int32_t window_right,
               int32_t rel_extent, const float *rel_logits, bool rel_bf16, const float *alibi_slopes,
-              int32_t num_splits, void *workspace, size_t workspace_bytes, void *out, float *lse, void *stream) {
+              int32_t num_splits, void *workspace, size_t workspace_bytes, void *out, float *lse, void *stream,
+              bool use_scratch = false) {
   if (kv8 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
     return RPA_ERR_SHAPE;
   // Sizes.
@@ -123,8 +134,9 @@ int attn_impl(const void *q, const void *key_cache, const void *value_cache, boo
   if (!q || !key_cache || !value_cache || !block_table || !cache_seqlens || !cu_seqlens_q || !out)
     return RPA_ERR_NULL;
   if (rel_extent > 0 && !rel_logits) return RPA_ERR_NULL;
-  // Workspace for split partials.
-  if (num_splits != 1) {
+  // Workspace for split partials (a caller-given buffer: the size that
+  // rpa_workspace_bytes states, whatever the device).
+  if (num_splits != 1 && !use_scratch) {
     if (!workspace) return RPA_ERR_WORKSPACE;
     if (workspace_bytes < rpa_workspace_bytes(num_splits, num_tokens, num_heads, head_dim))
       return RPA_ERR_WORKSPACE;
@@ -148,6 +160,18 @@ int attn_impl(const void *q, const void *key_cache, const void *value_cache, boo
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       return RPA_ERR_HIP;
     bal_wgs = cus < rpa::kBalMaxWGs ? cus : rpa::kBalMaxWGs;
+  }
+  if (use_scratch) {
+    const size_t need = balanced ? bal_workspace_bytes(bal_wgs, head_dim)
+                        : num_splits > 1 ? rpa_workspace_bytes(num_splits, num_tokens, num_heads, head_dim)
+                                         : 0;
+    if (need > rpa::kScratchBytes) return RPA_ERR_WORKSPACE;
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      if (rpa::scratch_device_ptr(&workspace) != hipSuccess) return RPA_ERR_HIP;
+      workspace_bytes = rpa::kScratchBytes;
+    }
   }
 
   rpa::AttnParams p;
@@ -261,6 +285,21 @@ int rpa_attn_varlen_ex(const void *q, const void *key_cache, const void *value_c
                    block_size, max_seqlen_q, softmax_scale, causal, window_left, window_right, rel_extent,
                    static_cast<const float *>(rel_logits), rel_logits_bf16 != 0, alibi_slopes, num_splits, workspace,
                    workspace_bytes, out, lse, stream);
+}
+
+int rpa_attn_varlen_noalloc(const void *q, const void *key_cache, const void *value_cache, int kv_e4m3,
+                            float k_scale, float v_scale, const int32_t *block_table, int32_t max_pages_per_seq,
+                            const int32_t *cache_seqlens, const int32_t *cu_seqlens_q, int32_t batch,
+                            int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t num_blocks, int32_t block_size, int32_t max_seqlen_q, float softmax_scale,
+                            int causal, int32_t window_left, int32_t window_right, int32_t rel_extent,
+                            const void *rel_logits, int rel_logits_bf16, const float *alibi_slopes,
+                            int32_t num_splits, void *out, float *lse, void *stream) {
+  return attn_impl(q, key_cache, value_cache, kv_e4m3 != 0, k_scale, v_scale, block_table, max_pages_per_seq,
+                   cache_seqlens, cu_seqlens_q, batch, num_tokens, num_heads, num_kv_heads, head_dim, num_blocks,
+                   block_size, max_seqlen_q, softmax_scale, causal, window_left, window_right, rel_extent,
+                   static_cast<const float *>(rel_logits), rel_logits_bf16 != 0, alibi_slopes, num_splits, nullptr, 0,
+                   out, lse, stream, true);
 }
 
 int rpa_slot_mapping(const int32_t *block_table, int32_t max_pages_per_seq, const int32_t *cache_seqlens,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rpa.h"
+
 namespace rpa {
 
 // Work decomposition shared by host and device.
@@ -25,9 +27,18 @@ constexpr int kBalHeads = 8;        // kv heads streamed side by side (one per w
 // (head_dim + 1) fp32 (outputs, then LSEs).  The one-head-per-workgroup
 // form uses the first entry of each slot.
 __host__ __device__ inline size_t bal_desc_bytes() { return (size_t)kBalMaxWGs * kBalDescInts * 4; }
-__host__ __device__ inline size_t bal_part_bytes(int head_dim) {
-  return (size_t)2 * kBalMaxWGs * kBalHeads * kDecCols * (size_t)(head_dim + 1) * 4;
+__host__ __device__ inline size_t bal_part_bytes(int head_dim, int wgs = kBalMaxWGs) {
+  return (size_t)2 * wgs * kBalHeads * kDecCols * (size_t)(head_dim + 1) * 4;
 }
+
+// Scratch of rpa_attn_varlen_noalloc: a static device array of this many
+// bytes on every GPU the library runs on (enough for the balanced decode of
+// head_dim 128 on up to 300 compute units, or for split partials of that
+// size).
+constexpr size_t kScratchBytes = RPA_NOALLOC_SCRATCH_BYTES;
+// Device address of the current GPU's scratch array, looked up once per
+// device (hipGetSymbolAddress) and cached.
+hipError_t scratch_device_ptr(void **ptr);
 
 struct AttnParams {
   const uint16_t *q;            // bf16 [T, H, D]

@@ -34,6 +34,8 @@
 // uses the same running max, so the result is unchanged.
 #include <type_traits>
 
+#include <mutex>
+
 #include "rpa_internal.h"
 
 namespace rpa {
@@ -3178,6 +3180,35 @@ hipError_t launch_balanced_decode(const AttnParams &p, int head_dim, hipStream_t
     hipLaunchKernelGGL((combine_balanced_kernel<64>), cgrid, cblock, 0, stream, p);
   }
   return hipGetLastError();
+}
+
+// ----------------------------------------------------- no-alloc scratch
+//
+// The workspace of rpa_attn_varlen_noalloc.  Each GPU that loads the library
+// holds one copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: the kernels only ever receive the
+// device address that hipGetSymbolAddress returns for the current device.
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+hipError_t scratch_device_ptr(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream) {

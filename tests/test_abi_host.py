@@ -246,3 +246,26 @@ def test_planner_balances_decode_batches(L):
     assert L.rpa_choose_splits(1, 1, 64, 8, 1 << 20, 0, 256) == 0
     # More requests than the balanced decode takes: one split each.
     assert L.rpa_choose_splits(3000, 1, 32, 8, 8192, 0, 256) == 1
+
+
+def _attn_noalloc(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, P=4, seqlens=FAKE, cu=FAKE, B=2, T=3, H=4, Hkv=2, D=64,
+             NB=8, BS=16, maxq=2, scale=0.125, causal=1, left=-1, right=-1, R=0, rel=None, S=1, out=FAKE)
+    a.update(kw)
+    return L.rpa_attn_varlen_noalloc(a["q"], a["k"], a["v"], 0, 1.0, 1.0, a["bt"], a["P"], a["seqlens"], a["cu"],
+                                     a["B"], a["T"], a["H"], a["Hkv"], a["D"], a["NB"], a["BS"], a["maxq"],
+                                     a["scale"], a["causal"], a["left"], a["right"], a["R"], a["rel"], 0, None,
+                                     a["S"], a["out"], None, None)
+
+
+def test_noalloc_argument_errors(L):
+    """The no-alloc entry validates like the others before it looks up its
+    scratch, and refuses partials larger than the scratch (no HIP call)."""
+    assert _attn_noalloc(L, q=None) == NULL
+    assert _attn_noalloc(L, out=None) == NULL
+    assert _attn_noalloc(L, H=6, Hkv=4) == SHAPE
+    assert _attn_noalloc(L, S=129) == SHAPE
+    assert _attn_noalloc(L, D=96) == UNSUP
+    assert _attn_noalloc(L, T=0, B=0, q=None, out=None) == OK
+    # 64 splits x 600 tokens x 32 heads x 129 fp32 values: about 630 MB.
+    assert _attn_noalloc(L, B=2, T=600, H=32, Hkv=8, D=128, maxq=300, S=64) == WS
