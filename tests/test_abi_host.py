@@ -17,9 +17,17 @@ OK, NULL, SHAPE, UNSUP, WS = 0, -1, -2, -3, -4
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
 
 
+# RPA_TEST_LIB selects another build of the same C ABI (the sanitizer build
+# of the host layer that tests/test_host_sanitizer.py runs these tests on).
+_TEST_LIB = os.environ.get("RPA_TEST_LIB")
+
+
 @pytest.fixture(scope="module")
 def L():
-    if not os.path.exists(bnd.LIB_PATH):
+    if _TEST_LIB:
+        bnd._lib = None
+        bnd.LIB_PATH = _TEST_LIB
+    elif not os.path.exists(bnd.LIB_PATH):
         from relative_bias_amd import build
         build.build()
     return bnd.lib()
@@ -269,3 +277,16 @@ def test_noalloc_argument_errors(L):
     assert _attn_noalloc(L, T=0, B=0, q=None, out=None) == OK
     # 64 splits x 600 tokens x 32 heads x 129 fp32 values: about 630 MB.
     assert _attn_noalloc(L, B=2, T=600, H=32, Hkv=8, D=128, maxq=300, S=64) == WS
+
+
+def test_requested_build_is_the_one_loaded(L):
+    """When another build of the ABI is requested (RPA_TEST_LIB), that file is
+    the one mapped into this process, and a sanitizer build runs with its
+    runtime present."""
+    if not _TEST_LIB:
+        pytest.skip("testing the default build")
+    with open("/proc/self/maps") as f:
+        maps = f.read()
+    assert os.path.realpath(_TEST_LIB) in maps
+    if "hostsan" in os.path.basename(_TEST_LIB):
+        assert "libasan" in maps and "libubsan" in maps
