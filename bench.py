@@ -332,6 +332,142 @@ def cpu_baseline(w, budget_s=12.0):
                       f"of the batched decode batch, all {wc.num_heads} heads, {spent:.1f} s of fp64 CPU work"}
 
 
+def host_cpu():
+    """Model name and thread counts of the host the oracle runs on."""
+    import torch
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count(), "torch_threads": torch.get_num_threads()}
+
+
+def _rows_flops(w, b, local, heads):
+    """4 * D * (visible (row, key) pairs) over the given rows of request b and heads."""
+    from relative_bias_amd import metrics
+    lq, lk = w.q_lens[b], w.k_lens[b]
+    pairs = 0
+    for i in local:
+        lo, hi = metrics._row_bounds(i + lk - lq, lk, w.causal, *w.window_size)
+        pairs += max(hi - lo + 1, 0)
+    return 4 * w.head_dim * len(heads) * pairs
+
+
+def cpu_baseline_rows(w, rows_per_request, budget_s, what):
+    """The fp64 oracle on a bounded sample of a prefill-type workload: the
+    last `rows_per_request` query rows of each request (all heads), request
+    after request until about budget_s of CPU time, in GFLOP/s of the same
+    algorithmic flops (4 * D * visible pairs * heads)."""
+    import torch
+    from oracle import attention as orc
+    wc = w if w.q.device.type == "cpu" else w.to("cpu")
+    cu = wc.cu_seqlens_q.tolist()
+    heads = list(range(wc.num_heads))
+    flops, spent, nrows, nreq = 0, 0.0, 0, 0
+    while spent < budget_s:
+        for b in range(wc.batch):
+            lq = wc.q_lens[b]
+            local = list(range(max(lq - rows_per_request, 0), lq))
+            if not local:
+                continue
+            toks = [cu[b] + i for i in local]
+            t0 = time.perf_counter()
+            orc.attention(wc.q, wc.key_cache, wc.value_cache, wc.block_table, wc.cache_seqlens, wc.cu_seqlens_q,
+                          wc.softmax_scale, wc.causal, wc.window_size, wc.rel_extent, wc.rel_logits, tokens=toks)
+            spent += time.perf_counter() - t0
+            flops += _rows_flops(wc, b, local, heads)
+            nrows += len(local)
+            nreq += 1
+            if spent >= budget_s:
+                break
+    return {"value": round(flops / spent / 1e9, 3), "unit": "GFLOP/s", "cores": torch.get_num_threads(),
+            "kind": "oracle",
+            "sample": f"{what}: the last {rows_per_request} query rows of each request, all {wc.num_heads} heads; "
+                      f"{nreq} request evaluations, {nrows} rows, {flops / 1e9:.1f} GFLOP in {spent:.1f} s of "
+                      f"fp64 CPU work"}
+
+
+def cpu_baseline_whole(w, budget_s, what):
+    """The fp64 oracle on a whole small workload, repeated for about budget_s,
+    in GB/s of the same algorithmic bytes."""
+    import torch
+    from oracle import attention as orc
+    from relative_bias_amd import metrics
+    wc = w if w.q.device.type == "cpu" else w.to("cpu")
+    nbytes = metrics.work(wc)["bytes"]
+    passes, spent = 0, 0.0
+    while spent < budget_s:
+        t0 = time.perf_counter()
+        orc.attention(wc.q, wc.key_cache, wc.value_cache, wc.block_table, wc.cache_seqlens, wc.cu_seqlens_q,
+                      wc.softmax_scale, wc.causal, wc.window_size, wc.rel_extent, wc.rel_logits)
+        spent += time.perf_counter() - t0
+        passes += 1
+    return {"value": round(passes * nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": torch.get_num_threads(),
+            "kind": "oracle",
+            "sample": f"{what}: {passes} passes over the whole workload in {spent:.1f} s of fp64 CPU work"}
+
+
+def cpu_baseline_heads(w, budget_s, what):
+    """The fp64 oracle on the q heads of one kv head at a time (kv head 0,
+    then 1, ...) of a decode workload, until about budget_s of CPU time, in
+    GB/s of those heads' algorithmic bytes (their kv head's K and V, their
+    q, out, lse and rel_logits rows, the block table)."""
+    import torch
+    from oracle import attention as orc
+    from relative_bias_amd import metrics
+    wc = w if w.q.device.type == "cpu" else w.to("cpu")
+    G = wc.num_heads // wc.num_kv_heads
+    sub = type("W", (), {})()
+    for k in ("q_lens", "k_lens", "head_dim", "block_size", "rel_extent", "window_size", "causal"):
+        setattr(sub, k, getattr(wc, k))
+    sub.num_heads, sub.num_kv_heads = G, 1
+    slice_bytes = metrics.work(sub)["bytes"]
+    done, spent, g = 0, 0.0, 0
+    while spent < budget_s and g < wc.num_kv_heads:
+        t0 = time.perf_counter()
+        orc.attention(wc.q, wc.key_cache, wc.value_cache, wc.block_table, wc.cache_seqlens, wc.cu_seqlens_q,
+                      wc.softmax_scale, wc.causal, wc.window_size, wc.rel_extent, wc.rel_logits,
+                      heads=range(g * G, (g + 1) * G))
+        spent += time.perf_counter() - t0
+        done += slice_bytes
+        g += 1
+    return {"value": round(done / spent / 1e9, 4), "unit": "GB/s", "cores": torch.get_num_threads(),
+            "kind": "oracle",
+            "sample": f"{what}: {g} of {wc.num_kv_heads} kv heads (each with its {G} q heads), "
+                      f"{done / 1e9:.2f} GB of algorithmic bytes in {spent:.1f} s of fp64 CPU work"}
+
+
+def roofline_of(name, w, ms, wk, kv_elem_bytes=2):
+    """Roofline block of one workload: its bound (the larger of its HBM time
+    at 8 TB/s and its MFMA time at 2.5 PFLOP/s), the achieved rate over the
+    whole timed step and its fraction of the peak, and the HBM traffic from
+    committed counter summaries of the current kernel source (else None)."""
+    t_hbm = wk["bytes"] / (HBM_PEAK_GBS * 1e6)          # ms
+    t_mfma = wk["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e9)  # ms
+    if t_mfma >= t_hbm:
+        achieved = wk["flops"] / ms / 1e9
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        achieved = wk["bytes"] / ms / 1e6
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["roofline_ms"] = round(max(t_hbm, t_mfma), 5)
+    roof["bound_over_measured"] = round(max(t_hbm, t_mfma) / ms, 4)
+    roof["kernel_ms"] = round(ms, 5)
+    roof["alg_bytes_per_launch"] = wk["bytes"]
+    roof["alg_flops_per_launch"] = wk["flops"]
+    roof["traffic"] = load_traffic(name)
+    if roof["traffic"]:
+        roof["traffic_over_alg_bytes"] = round(roof["traffic"] / wk["bytes"], 4)
+    return roof
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -375,6 +511,9 @@ def main(argv=None):
     results = {}
     kv_summary = None
     graph_summary = None
+    split_sweep = {}
+    cpu_extra = {}
+    want_cpu = not a.no_cpu and a.only is None and not a.no_extra
 
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
@@ -407,10 +546,13 @@ def main(argv=None):
     if not a.no_extra or a.only:
         if a.only in (None, "chunked_prefill"):
             w3 = wl.chunked_prefill(device="cpu").to(dev)
-            r3 = Runner(w3, 1)
+            r3 = Runner(w3, 1, pools=3)
             ms, ms_c, wk = measure(r3, max(5, a.steps // 2), a.warmup, SETTLE_S)
             results["chunked_prefill"] = (w3, 1, ms, ms_c, wk)
             log(f"chunked_prefill: {ms * 1e3:.1f} us/step, {wk['flops'] / ms / 1e9:.1f} TFLOP/s")
+            if want_cpu:
+                cpu_extra["chunked_prefill"] = cpu_baseline_rows(w3, 8, 8.0, "chunked prefill batch")
+                log(f"  oracle: {cpu_extra['chunked_prefill']['value']} GFLOP/s")
             del r3, w3
         if a.only in (None, "long_decode"):
             w4 = wl.long_decode(device=dev)
@@ -421,16 +563,37 @@ def main(argv=None):
             ms, ms_c, wk = measure(r4, max(5, a.steps // 2), a.warmup, SETTLE_S)
             results["long_decode"] = (w4, S4, ms, ms_c, wk)
             log(f"long_decode S={S4}: {ms * 1e3:.1f} us/step, {wk['bytes'] / ms / 1e6:.1f} GB/s")
-            del r4, w4
+            del r4
+            if a.only is None:
+                # The split counts the walkthrough's planner caps at for this
+                # range (16 to 128 partitions), beside the planner's choice.
+                for Sx in (16, 32, 64, 128):
+                    rx = Runner(w4, Sx)
+                    msx, msx_c, wkx = measure(rx, max(5, a.steps // 2), a.warmup, 0.05)
+                    split_sweep[str(Sx)] = {"num_splits": Sx, "ms_per_step": round(msx, 5),
+                                            "combine_ms": round(msx_c, 5),
+                                            "gbs": round(wkx["bytes"] / msx / 1e6, 2),
+                                            "hbm_frac": round(wkx["bytes"] / msx / 1e6 / HBM_PEAK_GBS, 4)}
+                    log(f"long_decode S={Sx}: {msx * 1e3:.1f} us/step (combine {msx_c * 1e3:.1f} us), "
+                        f"{wkx['bytes'] / msx / 1e6:.1f} GB/s")
+                    del rx
+            if want_cpu:
+                cpu_extra["long_decode"] = cpu_baseline_heads(w4, 8.0, "1M-token decode")
+                log(f"  oracle: {cpu_extra['long_decode']['value']} GB/s")
+            del w4
             torch.cuda.empty_cache()
         if a.only in (None, "continuous_batch"):
             w5 = wl.continuous_batch(device=dev)
-            r5 = Runner(w5, 1)
+            r5 = Runner(w5, 1, pools=3)
             ms, ms_c, wk = measure(r5, max(5, a.steps // 2), a.warmup, SETTLE_S)
             results["continuous_batch"] = (w5, 1, ms, ms_c, wk)
             log(f"continuous_batch: {ms * 1e3:.1f} us/step, {wk['bytes'] / ms / 1e6:.1f} GB/s, "
                 f"{wk['flops'] / ms / 1e9:.1f} TFLOP/s")
-            del r5, w5
+            del r5
+            if want_cpu:
+                cpu_extra["continuous_batch"] = cpu_baseline_rows(w5, 8, 8.0, "continuous-batching mix")
+                log(f"  oracle: {cpu_extra['continuous_batch']['value']} GFLOP/s")
+            del w5
             torch.cuda.empty_cache()
         if a.only in (None, "batched_decode_fp8"):
             w6 = wl.batched_decode(device="cpu").to(dev)
@@ -442,7 +605,7 @@ def main(argv=None):
             torch.cuda.empty_cache()
         if a.only in (None, "chunked_prefill_fp8"):
             w8 = wl.chunked_prefill(device="cpu").to(dev)
-            r8 = Fp8Runner(w8, 1)
+            r8 = Fp8Runner(w8, 1, pools=3)
             ms, ms_c, wk = measure(r8, max(5, a.steps // 2), a.warmup, SETTLE_S)
             results["chunked_prefill_fp8"] = (w8, 1, ms, ms_c, wk)
             log(f"chunked_prefill_fp8: {ms * 1e3:.1f} us/step, {wk['flops'] / ms / 1e9:.1f} TFLOP/s")
@@ -464,7 +627,7 @@ def main(argv=None):
             if a.only not in (None, name):
                 continue
             wa = make(device="cpu").to(dev)
-            ra = Runner(wa, S_a, pools=3 if S_a == 0 else 1)
+            ra = Runner(wa, S_a, pools=3)
             H = wa.num_heads
             if name.endswith("_alibi"):
                 ra.alibi = torch.tensor([2.0 ** (-8.0 * (i + 1) / H) for i in range(H)], dtype=torch.float32,
@@ -508,7 +671,10 @@ def main(argv=None):
                 "hbm_frac": round(wk["bytes"] / ms / 1e6 / HBM_PEAK_GBS, 4),
                 "mfma_frac": round(wk["flops"] / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
                 "alg_bytes": wk["bytes"], "alg_flops": wk["flops"],
-                **({"mfma_counters": load_mfma(name)} if load_mfma(name) else {})}
+                "roofline": roofline_of(name, w, ms, wk),
+                **({"mfma_counters": load_mfma(name)} if load_mfma(name) else {}),
+                **({"cpu_baseline": cpu_extra[name]} if name in cpu_extra else {}),
+                **({"split_sweep": split_sweep} if name == "long_decode" and split_sweep else {})}
 
     if a.only == "kv_write":
         print(json.dumps({"kv_write": kv_summary, "kernel_hash": kernel_hash()}))
@@ -566,7 +732,10 @@ def main(argv=None):
     if not a.no_cpu and head == "batched_decode":
         log("timing the CPU oracle on a sample ...")
         line["cpu_baseline"] = cpu_baseline(w)
+        line["cpu_baseline"]["host_cpu"] = host_cpu()
         line["cpu_baseline_one_thread"] = cpu_baseline_one_thread(w)
+        if want_cpu:
+            line["tiny_mixed_cpu_baseline"] = cpu_baseline_whole(wl.tiny(), 3.0, "tiny mixed batch")
     line["kernel_hash"] = kernel_hash()
     print(json.dumps(line), flush=True)
     return 0

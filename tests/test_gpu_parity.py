@@ -376,13 +376,15 @@ def test_continuous_batch_sampled():
 @pytest.mark.timeout(600)
 def test_long_decode_sampled_heads():
     """1,048,576-token decode, generated on the GPU; the oracle checks two kv
-    groups (16 q heads) for the split counts the benchmark uses."""
+    groups (16 q heads) for the split counts the benchmark times: the
+    planner's (balanced) and 16, 32, 64 and 128 partitions (the range the
+    walkthrough's planner caps at through 1M KV tokens)."""
     wg = wl.long_decode(device="cuda")
     heads = list(range(0, 8)) + list(range(56, 64))
     wc = wg.to("cpu")
     ref = _oracle(wc, heads=heads)
     del wc
-    for S in (bnd.rpa_choose_splits(1, 1, 64, 8, 1 << 20), 16):
+    for S in (bnd.rpa_choose_splits(1, 1, 64, 8, 1 << 20), 16, 32, 64, 128):
         out, lse = _gpu_run(wg, S)
         _compare(out, lse, *ref, heads=heads, tag=f"long_decode S={S}")
 
