@@ -72,6 +72,7 @@ struct CombineParams {
   uint16_t *out;                // bf16 [T, H, D]
   float *lse;                   // [T, H] or null
   int32_t S, rows, D;           // rows = T * H
+  int32_t wr;                   // waves per row (set by launch_combine)
 };
 
 struct SlotParams {

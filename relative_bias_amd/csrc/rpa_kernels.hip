@@ -2926,47 +2926,70 @@ __global__ __launch_bounds__(kThreads) void combine_heads_kernel(AttnParams p) {
 
 // ---------------------------------------------------------------- combine
 
-// One wave per (token, head) row: weights exp(lse_s - LSE) over the splits,
-// then a weighted sum of the normalised partials.
+// One row (token, head) per p.wr waves of a workgroup (one, two or four:
+// more when there are many splits, so that few rows with many partials
+// still spread over many waves).  Every wave of a row reduces all S LSEs to
+// the weights exp(lse_s - LSE); wave `sub` of the row sums the normalised
+// partials of its slice of the splits, and the slices are added through LDS.
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   __shared__ float wts[4][128];
+  __shared__ float part[4][256];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + w;
-  if (row >= p.rows) return;
-  const float l0 = lane < p.S ? p.part_lse[(int64_t)lane * p.rows + row] : neg_inf();
-  const float l1 = lane + 64 < p.S ? p.part_lse[(int64_t)(lane + 64) * p.rows + row] : neg_inf();
+  const int WR = p.wr, sub = w % WR;
+  const int row = blockIdx.x * (4 / WR) + w / WR;
+  const bool live = row < p.rows;
+  const int S = p.S, D = p.D;
+  const float l0 = live && lane < S ? p.part_lse[(int64_t)lane * p.rows + row] : neg_inf();
+  const float l1 = live && lane + 64 < S ? p.part_lse[(int64_t)(lane + 64) * p.rows + row] : neg_inf();
   float M = fmaxf(l0, l1);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  uint16_t *op = p.out + (int64_t)row * p.D;
-  if (M == neg_inf()) {
-    for (int d = lane; d < p.D; d += 64) op[d] = 0;
-    if (lane == 0 && p.lse) p.lse[row] = neg_inf();
-    return;
-  }
   const float e0 = l0 == neg_inf() ? 0.f : exp2_fast((l0 - M) * kLog2e);
   const float e1 = l1 == neg_inf() ? 0.f : exp2_fast((l1 - M) * kLog2e);
   float W = e0 + e1;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) W += __shfl_xor(W, o);
-  const float invW = 1.f / W;
+  const float invW = W > 0.f ? 1.f / W : 0.f;
   wts[w][lane] = e0 * invW;
   wts[w][lane + 64] = e1 * invW;
   wave_lds_sync();
   // A split with weight 0 (an empty chunk, lse = -inf, or one whose weight
   // underflows) is skipped, not multiplied: its partial may hold anything,
   // NaN included, without reaching the output.
-  for (int d = lane; d < p.D; d += 64) {
-    float acc = 0.f;
+  const int s0 = sub * S / WR, s1 = (sub + 1) * S / WR;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (live && M != neg_inf()) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int d = lane + 64 * k;
+      if (d >= D) break;
+      const float *src = p.part_out + (int64_t)row * D + d;
 #pragma unroll 8
-    for (int s = 0; s < p.S; ++s) {
-      const float wt = wts[w][s];
-      const float v = p.part_out[((int64_t)s * p.rows + row) * p.D + d];
-      acc += wt != 0.f ? wt * v : 0.f;
+      for (int s = s0; s < s1; ++s) {
+        const float wt = wts[w][s];
+        const float v = src[(int64_t)s * p.rows * D];
+        acc[k] += wt != 0.f ? wt * v : 0.f;
+      }
     }
-    op[d] = __builtin_bit_cast(uint16_t, (__bf16)acc);
   }
-  if (lane == 0 && p.lse) p.lse[row] = M + log2_fast(W) * kLn2;
+  if (WR > 1) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (lane + 64 * k < D) part[w][lane + 64 * k] = acc[k];
+    __syncthreads();
+    if (sub == 0) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        for (int ww = 1; ww < WR; ++ww)
+          if (lane + 64 * k < D) acc[k] += part[w + ww][lane + 64 * k];
+    }
+  }
+  if (!live || sub != 0) return;
+  uint16_t *op = p.out + (int64_t)row * D;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (lane + 64 * k < D) op[lane + 64 * k] = __builtin_bit_cast(uint16_t, (__bf16)acc[k]);
+  if (lane == 0 && p.lse) p.lse[row] = M == neg_inf() ? neg_inf() : M + log2_fast(W) * kLn2;
 }
 
 // ------------------------------------------------------- paged KV write
@@ -3213,8 +3236,11 @@ hipError_t scratch_device_ptr(void **ptr) {
 
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream) {
   if (p.rows <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((p.rows + 3) / 4)), block(kThreads);
-  hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, p);
+  CombineParams q = p;
+  q.wr = p.S > 64 ? 4 : p.S > 16 ? 2 : 1;  // waves per row
+  const int rows_per_wg = 4 / q.wr;
+  const dim3 grid((unsigned)((p.rows + rows_per_wg - 1) / rows_per_wg)), block(kThreads);
+  hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, q);
   return hipGetLastError();
 }
 
