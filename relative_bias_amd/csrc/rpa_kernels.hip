@@ -868,11 +868,12 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     voff_k[n] = (uint32_t)rev4(rr) * slot_bytes + (uint32_t)((pu ^ swz_k<D>(kbw + rr)) << 4);
     voff_v[n] = (uint32_t)rev4(rr) * slot_bytes + (uint32_t)((pu ^ swz_v<D>(kbw + rr)) << 4);
   }
-  // Tiles are visited from the top of the range down: tile jt starts at key
-  // tile_kb(jt), so the diagonal and the bias band come first.
+  // Tiles are visited from the bottom of the range up: tile jt starts at key
+  // tile_kb(jt).  The bias band sits just under the diagonal, so its tiles
+  // come last and each item starts with plain tiles (measured 5 % faster on
+  // the chunked prefill batch than visiting the band first).
   const int nt = t0 < t1 ? (t1 - t0 + kTileKeys - 1) / kTileKeys : 0;
-  const int t_top = t0 + (nt - 1) * kTileKeys;
-  auto tile_kb = [&](int jt) { return t_top - jt * kTileKeys; };
+  auto tile_kb = [&](int jt) { return t0 + jt * kTileKeys; };
   // Page ids of this wave's 16-key block for a window of 64 tiles, one per
   // lane, read back with readlane (no memory access in the loop); the next
   // window is loaded 64 tiles ahead.
@@ -1046,28 +1047,6 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     sacc[1] = f32x16{};
   };
 
-  // Prologue prefetch: the band tiles come first, so pull this wave's
-  // rel_logits rows into the cache while the first tiles load, with dword
-  // direct loads whose LDS writes land in V slot 1 (unused until iteration
-  // 0).  Line i of row r is fetched by lane (i + r * LPR) % 64
-  // of load (i + r * LPR) / 64.
-  auto prefetch_band_rows = [&]() __attribute__((always_inline)) {
-    if (bias_fast && band_hi >= t0 && band_lo < t1) {
-      const int lpr = (p.R * 4 + 127) / 128 + 1;  // 128-byte lines per row
-      const int nload = (32 * lpr + 63) / 64;
-      for (int n = 0; n < nload; ++n) {
-        const int ln = 64 * n + lane;
-        const int rw = ln / lpr;  // row of this wave's 32
-        int rr = min(row0 + 32 * w + rw, row_last);
-        const int tk = tok0 + rr / G, hd = g * G + rr % G;
-        const int64_t off = ((int64_t)tk * p.H + hd) * p.R * 4 - bias_lo * 4 + 128 * (ln - rw * lpr);
-        const uint32_t voff = rw < 32 ? (uint32_t)off : 0xFFFFFFF0u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            bias_rs, (__attribute__((address_space(3))) void *)(smem + L::vOff(1) + 256 * w), 4, voff, 0, 0, 0);
-      }
-    }
-  };
-
   if (nt > 0) {
     // Software pipeline over 64-key tiles.  Tile j's K sits in K slot j%2,
     // its V in V slot j%2, its scores in register set j%2 (sa or sb).  While
@@ -1102,7 +1081,6 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       }
       zero(sa);
       begin(sa, tile_kb(0));
-      prefetch_band_rows();
       wait_vm0();
       __syncthreads();
       finish(sa, tile_kb(0));
