@@ -441,7 +441,6 @@ __device__ __forceinline__ void tile_bf16_widen(f32x16 *sacc) {
 // get the bias.
 struct TileBounds {
   int vis_lo, vis_hi, band_lo, band_hi;
-  float al0, al_s;  // ALiBi in raw score units: al0 + al_s * offset (0 and 0 without ALiBi)
 };
 
 // Initial value of the score accumulator of a general tile (a mask edge or
@@ -490,39 +489,11 @@ __device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t a, uint32_t 
 enum { kInitEdge, kInitBand, kInitFull };
 // Key offset (without the 4 hf shift) of accumulator element (kb2, j).
 __device__ __forceinline__ constexpr int offset_of(int kb2, int j) { return 32 * kb2 + 8 * (j >> 2) + 3 - (j & 3); }
-// ALiBi ramp al0 + al_s * offset_of(kb2, j) of the 32 elements, by additions
-// from a few registers (per-element constants would each need a register).
-__device__ __forceinline__ void alibi_ramp(float (&r)[2][16], float al0, float al_s) {
-  const float s8 = 8.f * al_s, s32 = 32.f * al_s;
-  float g0 = __builtin_fmaf(3.f, al_s, al0);
-#pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
-    float gb = kb2 ? g0 + s32 : g0;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float b = g ? gb + (float)g * s8 : gb;
-      r[kb2][4 * g] = b;
-      r[kb2][4 * g + 1] = b - al_s;
-      r[kb2][4 * g + 2] = b - 2.f * al_s;
-      r[kb2][4 * g + 3] = b - 3.f * al_s;
-    }
-  }
-}
-
 template <int MODE>
-__device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv_scale, float masked,
-                                          bool alibi = false) {
+__device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv_scale, float masked) {
   if constexpr (MODE == kInitFull) {
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) sacc[kb2] *= inv_scale;
-    if (alibi) {
-      float r[2][16];
-      alibi_ramp(r, tb.al0, tb.al_s);
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[kb2][j] += r[kb2][j];
-    }
     return;
   }
   constexpr bool USE_VIS = true;
@@ -530,23 +501,6 @@ __device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv
   const uint32_t vis = USE_VIS ? range_bits(tb.vis_lo, tb.vis_hi) : 0u;
   const uint32_t band = USE_BAND ? range_bits(tb.band_lo, tb.band_hi) : 0u;
   const uint32_t mbits = __float_as_uint(masked);
-  if (alibi) {
-    float r[2][16];
-    alibi_ramp(r, tb.al0, tb.al_s);
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int pos = order_of(kb2, j);
-        uint32_t v = 0u;
-        if constexpr (MODE != kInitEdge) v = __float_as_uint(sacc[kb2][j] * inv_scale);
-        if constexpr (USE_BAND) v &= bit_mask(band, pos);
-        const float f = __uint_as_float(v) + r[kb2][j];
-        sacc[kb2][j] = __uint_as_float(bit_select(bit_mask(vis, pos), __float_as_uint(f), mbits));
-      }
-    }
-    return;
-  }
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
@@ -559,6 +513,22 @@ __device__ __forceinline__ void tile_init(f32x16 *sacc, TileBounds tb, float inv
       sacc[kb2][j] = __uint_as_float(v);
     }
   }
+}
+
+// ALiBi inside a tile: slope * (t - qa) = al_s * offset_of(kb2, j), the
+// same for every tile, plus al_s * (kb + 4 hf - qa), a per-row constant of
+// the tile (al_s: the slope in raw score units).  The first part is added
+// to the scores once the QK is done (an fma with a constant per element, so
+// that nothing per element is held across the tile loop), the second joins
+// the exp's subtrahend and the tile's row max.
+__device__ __forceinline__ float alibi_ramp_add(float al_s, int kb2, int j, float s) {
+  return __builtin_fmaf(al_s, (float)offset_of(kb2, j), s);
+}
+__device__ __forceinline__ void tile_alibi_ramp(f32x16 *sacc, float al_s) {
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sacc[kb2][j] = alibi_ramp_add(al_s, kb2, j, sacc[kb2][j]);
 }
 
 // Row max of a tile in raw score units (the scale is positive).
@@ -678,7 +648,7 @@ __device__ __forceinline__ float phase_a(const char *Kb, const bf16x8 *qf, f32x1
 // Phase B: O^T += V^T·P^T on the MFMA pipe (the V^T operand of row
 // d = lane%32 and eight slot-order keys comes from two transposing reads of
 // the row-major V tile), and the row max (raw units) of the next tile on the
-// VALU.
+// VALU, after adding the ALiBi ramp of slope al_s to its scores when ALIBI.
 //
 // The transposing reads are issued as inline asm: the compiler cannot tell
 // them apart from the direct loads in flight into the other V slot and would
@@ -697,9 +667,9 @@ __device__ __forceinline__ void lgkm_wait_for(u32x4 &a) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
 }
 
-template <int D, int VOFF>
-__device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32x16 *oacc, int lane,
-                                         const f32x16 *sn) {
+template <int D, int VOFF, bool ALIBI>
+__device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32x16 *oacc, int lane, f32x16 *sn,
+                                         float al_s) {
   constexpr int DB = D / 32;
   constexpr int NM = 4 * DB;
   constexpr int EPM = 32 / NM;
@@ -737,6 +707,7 @@ __device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32
 #pragma unroll
     for (int e = 0; e < EPM; ++e) {
       const int x = i * EPM + e;
+      if constexpr (ALIBI) sn[x >> 4][x & 15] = alibi_ramp_add(al_s, x >> 4, x & 15, sn[x >> 4][x & 15]);
       mx[i & 3] = fmaxf(mx[i & 3], sn[x >> 4][x & 15]);
     }
     pin(mx[i & 3]);
@@ -822,9 +793,26 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   const float c = zero_scale ? kLog2e : fabsf(p.scale_log2);
   const float inv_scale = zero_scale ? 1.f : 1.f / fabsf(p.scale);
   const float masked = neg_inf();
-  // ALiBi enters the accumulator like the bias: slope * (t - qa) / scale.
+  // ALiBi joins the scores in raw units, like the bias: slope * (t - qa) /
+  // scale, as a ramp added after each tile's QK plus a per-row constant.
   constexpr bool alibi = (FEAT & kFeatAlibi) != 0;
   const float al_s = alibi ? p.alibi[head] * inv_scale : 0.f;
+  // The per-row ALiBi constant of the tile at kb, in log2 units: it joins the
+  // exp's subtrahend and the tile's row max (the scores hold only the
+  // tile-invariant ramp).  kb - qa is formed in integers, so the product is
+  // exact to one rounding however long the sequence.
+  const float al_c = al_s * c;
+  auto crow = [&](int kb) { return al_c * (float)(kb + 4 * hf - qa); };
+  // The exp's subtrahend and the row max of the tile at kb (without ALiBi
+  // these are the running max and the max as they are).
+  auto m_at = [&](float m, int kb) {
+    if constexpr (alibi) return m - crow(kb);
+    else return m;
+  };
+  auto mx_at = [&](float mx, int kb) {
+    if constexpr (alibi) return mx + crow(kb);
+    else return mx;
+  };
 
   bf16x8 qf[KSTEPS];
   {
@@ -860,14 +848,15 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   constexpr int RPI = 64 / UNITS;      // rows per load instruction
   constexpr int NI = 16 / RPI;         // load instructions per wave per operand
   const int kbw = 16 * w;
-  uint32_t voff_k[NI], voff_v[NI];
-#pragma unroll
-  for (int n = 0; n < NI; ++n) {
-    const int rr = RPI * n + lane / UNITS;  // row within the wave's block
-    const int pu = lane % UNITS;
-    voff_k[n] = (uint32_t)rev4(rr) * slot_bytes + (uint32_t)((pu ^ swz_k<D>(kbw + rr)) << 4);
-    voff_v[n] = (uint32_t)rev4(rr) * slot_bytes + (uint32_t)((pu ^ swz_v<D>(kbw + rr)) << 4);
-  }
+  // Lane l of load n brings row rr = RPI n + l / UNITS of the wave's block,
+  // unit (l % UNITS) ^ swz(kbw + rr), from key slot rev4(rr) of the page.
+  // RPI is a multiple of 4, so rev4(rr) = RPI n + rev4(l / UNITS); the V
+  // swizzle does not depend on n, and the K swizzle of load n is that of
+  // load 0 XOR 4 n.  Three registers per lane give every load's offset.
+  const int lx = lane / UNITS, pu = lane % UNITS;
+  const uint32_t vrow = (uint32_t)rev4(lx) * slot_bytes;
+  const uint32_t uk16 = (uint32_t)((pu ^ swz_k<D>(kbw + lx)) << 4);
+  const uint32_t vrow_v = vrow + (uint32_t)((pu ^ swz_v<D>(kbw + lx)) << 4);
   // Tiles are visited from the bottom of the range up: tile jt starts at key
   // tile_kb(jt).  The bias band sits just under the diagonal, so its tiles
   // come last and each item starts with plain tiles (measured 5 % faster on
@@ -888,17 +877,27 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   auto page_t = [&](int jt) { return __builtin_amdgcn_readlane(pc, jt - pc_base); };
   const char *kcache = reinterpret_cast<const char *>(p.k) + (uint64_t)g * D * EB;
   const char *vcache = reinterpret_cast<const char *>(p.v) + (uint64_t)g * D * EB;
-  // Direct loads of tile jt (zeros past the last tile).
-  auto dma = [&](const char *cache, int jt, int page, int lds_off, const uint32_t *voff) __attribute__((always_inline)) {
+  // Direct loads of tile jt (zeros past the last tile) into the K (IS_K) or
+  // V slot at lds_off.  The offsets are formed at each call from the three
+  // lane registers (pinned there, so that the compiler does not hoist NI
+  // offsets per operand out of the tile loop and hold them throughout).
+  auto dma = [&](auto is_k_tag, const char *cache, int jt, int page, int lds_off) __attribute__((always_inline)) {
+    constexpr bool IS_K = decltype(is_k_tag)::value;
     const bool live = jt < nt;
     const int key = (live ? tile_kb(jt) : t0) + kbw;
     const int nvalid = live ? min(max(kend - key, 0), 16) : 0;
     const char *src = cache + (uint64_t)(uint32_t)page * page_bytes + (uint64_t)(uint32_t)pslot(key) * slot_bytes;
     const auto rs = make_rsrc(src, (uint32_t)nvalid * slot_bytes);
+    uint32_t vb = IS_K ? vrow : vrow_v;
+    uint32_t u = uk16;
+    asm volatile("" : "+v"(vb), "+v"(u));
 #pragma unroll
-    for (int n = 0; n < NI; ++n)
+    for (int n = 0; n < NI; ++n) {
+      const uint32_t rows = (uint32_t)(RPI * n) * slot_bytes;
+      const uint32_t voff = IS_K ? vb + (u ^ (uint32_t)(64 * n)) + rows : vb + rows;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void *)(smem + lds_off + (kbw + RPI * n) * ROWB), 16, voff[n], 0, 0, 0);
+          rs, (__attribute__((address_space(3))) void *)(smem + lds_off + (kbw + RPI * n) * ROWB), 16, voff, 0, 0, 0);
+    }
   };
   // E4M3 caches: the direct loads bring the raw rows of a tile (key order,
   // D bytes a row) to a landing area, wave w its own 16 keys; once they
@@ -988,18 +987,16 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   };
 
   auto is_band = [&](int kb) { return p.R > 0 && kb <= band_hi && kb + kTileKeys - 1 >= band_lo; };
-  // Plain: every key visible to every row, outside the band.  With ALiBi no
-  // tile is plain (each needs its ALiBi start), but such a tile only needs
-  // the ALiBi ramp, no mask.
-  auto is_plain_geo = [&](int kb) { return kb >= in_lo && kb + kTileKeys - 1 <= in_hi && !is_band(kb); };
-  auto is_plain = [&](int kb) { return !alibi && is_plain_geo(kb); };
+  // Plain: every key visible to every row, outside the band (the ALiBi ramp
+  // is added after the QK, so it does not make a tile general).
+  auto is_plain = [&](int kb) { return kb >= in_lo && kb + kTileKeys - 1 <= in_hi && !is_band(kb); };
   // Every key of the tile visible to, and in the band of, every row.
   const int full_lo = __builtin_amdgcn_readfirstlane(max(in_lo, qa_max - p.R + 1));
   const int full_hi = __builtin_amdgcn_readfirstlane(min(in_hi, qa_min));
   auto is_full_band = [&](int kb) { return kb >= full_lo && kb + kTileKeys - 1 <= full_hi; };
   auto bounds = [&](int kb) {
     const int off = kb + 4 * hf;
-    return TileBounds{lo_r - off, hi_r - off, qa - p.R + 1 - off, qa - off, al_s * (float)(off - qa), al_s};
+    return TileBounds{lo_r - off, hi_r - off, qa - p.R + 1 - off, qa - off};
   };
   // Lazy max update after the row max mx of a tile: O and l are rescaled
   // only when some row's max grew by more than kTau.
@@ -1019,17 +1016,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   // of an edge tile; a plain tile's set is zeroed first), finish() once
   // those loads have landed (band tiles only).
   auto start_general = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
-    if (alibi && is_plain_geo(kb)) {
-      const TileBounds tb = bounds(kb);
-      float r[2][16];
-      alibi_ramp(r, tb.al0, tb.al_s);
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[kb2][j] = r[kb2][j];
-    } else {
-      tile_init<kInitEdge>(sacc, bounds(kb), inv_scale, masked, alibi);
-    }
+    tile_init<kInitEdge>(sacc, bounds(kb), inv_scale, masked);
   };
   auto begin = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
     if (is_band(kb)) load_bias(sacc, kb);
@@ -1038,8 +1025,8 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   auto finish = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
     if (is_band(kb)) {
       if (rel_bf16) tile_bf16_widen(sacc);
-      if (is_full_band(kb)) tile_init<kInitFull>(sacc, bounds(kb), inv_scale, masked, alibi);
-      else tile_init<kInitBand>(sacc, bounds(kb), inv_scale, masked, alibi);
+      if (is_full_band(kb)) tile_init<kInitFull>(sacc, bounds(kb), inv_scale, masked);
+      else tile_init<kInitBand>(sacc, bounds(kb), inv_scale, masked);
     }
   };
   auto zero = [&](f32x16 *sacc) __attribute__((always_inline)) {
@@ -1075,9 +1062,9 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
         wait_vm0();
         decode8(L::land8K, L::kOff(1), dst_k8);
       } else {
-        dma(kcache, 0, pg0, L::kOff(0), voff_k);
-        dma(vcache, 0, pg0, L::vOff(0), voff_v);
-        dma(kcache, 1, pg_v, L::kOff(1), voff_k);
+        dma(BoolTag<true>{}, kcache, 0, pg0, L::kOff(0));
+        dma(BoolTag<false>{}, vcache, 0, pg0, L::vOff(0));
+        dma(BoolTag<true>{}, kcache, 1, pg_v, L::kOff(1));
       }
       zero(sa);
       begin(sa, tile_kb(0));
@@ -1085,7 +1072,8 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       __syncthreads();
       finish(sa, tile_kb(0));
       qk_mfma<D, true>(smem + L::kOff(0), qf, sa, l32, hf);
-      update_max(xor32_max(tile_rowmax(sa) * c));
+      if constexpr (alibi) tile_alibi_ramp(sa, al_s);
+      update_max(xor32_max(mx_at(tile_rowmax(sa) * c, tile_kb(0))));
       zero(sb);
       if (nt > 1) begin(sb, tile_kb(1));
       // Iteration 0 refills K slot 0: every wave must be done reading K(0).
@@ -1118,8 +1106,8 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
         dma8(kcache, j + 2, pg_k, L::land8K);
         dma8(vcache, j + 1, pg_v, L::land8V);
       } else {
-        dma(kcache, j + 2, pg_k, L::kOff(PAR), voff_k);
-        dma(vcache, j + 1, pg_v, L::vOff(1 - PAR), voff_v);
+        dma(BoolTag<true>{}, kcache, j + 2, pg_k, L::kOff(PAR));
+        dma(BoolTag<false>{}, vcache, j + 1, pg_v, L::vOff(1 - PAR));
       }
       if (j + 3 - pc_base == 64) {
         pc = pc_next;
@@ -1131,12 +1119,12 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       const float m_use = m_run == neg_inf() ? 0.f : m_run;
       __builtin_amdgcn_sched_barrier(0);
       // Phase A: QK of tile j+1 (MFMA) || exp of tile j (VALU).
-      l_run += phase_a<D>(smem + L::kOff(1 - PAR), qf, nxt, cur, c, m_use, pb, l32, hf, zc);
+      l_run += phase_a<D>(smem + L::kOff(1 - PAR), qf, nxt, cur, c, m_at(m_use, tile_kb(j)), pb, l32, hf, zc);
       const bool band2 = j + 2 < nt && is_band(tile_kb(j + 2));
       if (band2) load_bias(cur, tile_kb(j + 2));
       __builtin_amdgcn_sched_barrier(0);
       // Phase B: PV of tile j (MFMA) || row max of tile j+1 (VALU).
-      const float mx = phase_b<D, L::vOff(PAR)>(smem, pb, oacc, lane, nxt) * c;
+      const float mx = mx_at(phase_b<D, L::vOff(PAR), alibi>(smem, pb, oacc, lane, nxt, al_s) * c, tile_kb(j + 1));
       // Masks of an edge tile j+2 in the released set, then the barrier that
       // publishes K(j+2) and V(j+1).  Raw bias loads may stay in flight.
       if (!band2 && j + 2 < nt && !is_plain(tile_kb(j + 2))) start_general(cur, tile_kb(j + 2));
@@ -1578,14 +1566,15 @@ constexpr int attn_lds_bytes() {
 // DECODE_ONLY: every request of the batch has Lq*G <= 16 (known on the host
 // from max_seqlen_q), so the prefill path is not compiled in.  Both variants
 // hold two workgroups, i.e. two waves per SIMD, per CU.
-// FEAT: the prefill variant (ALiBi: every tile starts from an initialised
-// accumulator; bf16 rel_logits: band tiles load 16-bit values); the decode
-// items test p.alibi and p.rel_bf16 at run time.  The ALiBi variants run one
-// workgroup per CU: with two they spill about 24 VGPRs inside the tile loop,
-// and the scratch traffic costs more than the second workgroup's overlap
-// gains.
+// FEAT: the prefill variant (ALiBi: the ramp is added to each tile's scores
+// after its QK; bf16 rel_logits: band tiles load 16-bit values); the decode
+// items test p.alibi and p.rel_bf16 at run time.  Register pressure decides
+// where the ALiBi ramp goes: an accumulator initialised before the QK and
+// held across the barrier needs about 20 more VGPRs than the 256 a wave has
+// at two waves per SIMD, and the scratch reloads that the spills put in the
+// tile loop wait for every direct load in flight.
 template <int D, bool DECODE_ONLY, bool KV8, int FEAT>
-__global__ __launch_bounds__(64 * attn_waves<DECODE_ONLY>(), (FEAT & kFeatAlibi) ? 1 : 2) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * attn_waves<DECODE_ONLY>(), 2) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char smem[attn_lds_bytes<D, DECODE_ONLY, KV8>()];
   const int bid = blockIdx.x;
   const int s = bid % p.S;
