@@ -136,6 +136,15 @@ __device__ __forceinline__ void lds_write_b128x8_now(const uint32_t (&a)[8], con
         "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7])
       : "memory");
 }
+// Four 16-byte LDS writes issued, not awaited (their source registers are
+// read at issue; a later lgkmcnt wait covers their completion).
+__device__ __forceinline__ void lds_write_b128x4_issue(const uint32_t (&a)[4], const u32x4 (&v)[4]) {
+  asm volatile(
+      "ds_write_b128 %0, %4\n\tds_write_b128 %1, %5\n\tds_write_b128 %2, %6\n\tds_write_b128 %3, %7"
+      :
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3])
+      : "memory");
+}
 __device__ __forceinline__ void lds_write_b128x4_now(const uint32_t (&a)[4], const u32x4 (&v)[4]) {
   asm volatile(
       "ds_write_b128 %0, %4\n\tds_write_b128 %1, %5\n\tds_write_b128 %2, %6\n\tds_write_b128 %3, %7\n\t"
@@ -667,7 +676,7 @@ __device__ __forceinline__ void lgkm_wait_for(u32x4 &a) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
 }
 
-template <int D, int VOFF, bool ALIBI>
+template <int D, int VOFF, bool ALIBI, bool LANE_PIN>
 __device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32x16 *oacc, int lane, f32x16 *sn,
                                          float al_s) {
   constexpr int DB = D / 32;
@@ -675,8 +684,15 @@ __device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32
   constexpr int EPM = 32 / NM;
   constexpr int AHEAD = 3;
   constexpr int ROWB = PrefillLds<D>::ROWB;
-  const int grp = lane >> 4, h = grp >> 1, dh = grp & 1;
-  const int k = (lane >> 2) & 3, q = lane & 3;
+  // LANE_PIN: the addresses are formed from an opaque copy of the lane id at
+  // each call, so that the compiler does not hoist them out of the tile loop
+  // and hold DB registers there (worth it only where registers are short: the
+  // E4M3 kernel with ALiBi spills without it, while the others run about 1 %
+  // slower with it).
+  int ln = lane;
+  if constexpr (LANE_PIN) asm volatile("" : "+v"(ln));
+  const int grp = ln >> 4, h = grp >> 1, dh = grp & 1;
+  const int k = (ln >> 2) & 3, q = ln & 3;
   const int key_lo = 4 * h + k;           // + 16 c4 (+ 8 for slots 4..7)
   const int sw = swz_v<D>(key_lo);       // same for key_lo + 16 c4 + 8
   // Per-lane address of head_dim block db; the slot, the 16-key chunk c4 and
@@ -905,46 +921,58 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   // wave decodes its rows into the tile's bf16 slot at the places the bf16
   // loads would have filled, so the rest of the pipeline is unchanged.
   constexpr int U8 = D / 16, RPI8 = 64 / U8, NI8 = 16 / RPI8;
-  uint32_t voff8[NI8], dst_k8[2 * NI8], dst_v8[2 * NI8];  // set and used for E4M3 caches only
-  if constexpr (KV8) {
-#pragma unroll
-    for (int n = 0; n < NI8; ++n) {
-      const int kk = RPI8 * n + lane / U8, pc = lane % U8;
-      voff8[n] = (uint32_t)kk * slot_bytes + (uint32_t)(pc << 4);
-      const int R = kbw + rev4(kk);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        dst_k8[2 * n + e] = (uint32_t)(R * ROWB + (((2 * pc + e) ^ swz_k<D>(R)) << 4));
-        dst_v8[2 * n + e] = (uint32_t)(R * ROWB + (((2 * pc + e) ^ swz_v<D>(R)) << 4));
-      }
-    }
-  }
+  // Block n of a wave's E4M3 rows: lane l loads (and later reads back) raw
+  // unit l % U8 of landing row RPI8 n + l / U8, and writes it decoded as the
+  // two bf16 units 2 (l % U8) + e of tile row kbw + rev4(RPI8 n + l / U8),
+  // at the places the swizzle gives them.  RPI8 is a multiple of 4, so
+  // rev4 keeps RPI8 n as it is; the V swizzle does not depend on n, and the
+  // K swizzle of block n is that of block 0 XOR 8 n (head_dim 128; 64 has
+  // one block).  Four lane registers give every address.
+  const int x8 = lane / U8, pc8 = lane % U8;
+  const int r8 = kbw + rev4(x8);
+  const uint32_t row8 = (uint32_t)(r8 * ROWB);
+  const uint32_t uk8 = (uint32_t)(((2 * pc8) ^ swz_k<D>(r8)) << 4);
+  const uint32_t uv8 = (uint32_t)(((2 * pc8) ^ swz_v<D>(r8)) << 4);
+  const uint32_t vb8 = (uint32_t)x8 * slot_bytes + (uint32_t)(pc8 << 4);
+  // Tile-slot byte offset of unit e of block n (K or V), from pinned copies
+  // of the lane registers so that the compiler forms them where they are
+  // used instead of holding 2 NI8 offsets per operand across the tile loop.
+  auto dst8 = [&](bool is_k, int n, int e, uint32_t row, uint32_t u) {
+    const uint32_t flip = (uint32_t)((((is_k && D == 128) ? 8 * n : 0) ^ e) << 4);
+    return row + (uint32_t)(RPI8 * n * ROWB) + (u ^ flip);
+  };
   auto dma8 = [&](const char *cache, int jt, int page, int land_off) __attribute__((always_inline)) {
     const bool live = jt < nt;
     const int key = (live ? tile_kb(jt) : t0) + kbw;
     const int nvalid = live ? min(max(kend - key, 0), 16) : 0;
     const char *src = cache + (uint64_t)(uint32_t)page * page_bytes + (uint64_t)(uint32_t)pslot(key) * slot_bytes;
     const auto rs = make_rsrc(src, (uint32_t)nvalid * slot_bytes);
+    uint32_t vb = vb8;
+    asm volatile("" : "+v"(vb));
 #pragma unroll
     for (int n = 0; n < NI8; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void *)(smem + land_off + (kbw + RPI8 * n) * D), 16, voff8[n], 0, 0,
-          0);
+          rs, (__attribute__((address_space(3))) void *)(smem + land_off + (kbw + RPI8 * n) * D), 16,
+          vb + (uint32_t)(RPI8 * n) * slot_bytes, 0, 0, 0);
   };
   const uint32_t smem_u = (uint32_t)(uintptr_t)smem;
-  auto decode8 = [&](int land_off, int slot_off, const uint32_t *dst) __attribute__((always_inline)) {
+  auto decode8 = [&](int land_off, int slot_off, bool is_k) __attribute__((always_inline)) {
     u32x4 raw[NI8];
 #pragma unroll
     for (int n = 0; n < NI8; ++n) raw[n] = lds_read_b128_asm(smem_u + land_off + (kbw + RPI8 * n) * D + 16 * lane);
     lgkm_wait_n<0>(raw);
-    const uint32_t base = smem_u + slot_off;
+    uint32_t row = smem_u + slot_off + row8, u = is_k ? uk8 : uv8;
+    asm volatile("" : "+v"(row), "+v"(u));
+    uint32_t dst[4];
+#pragma unroll
+    for (int i = 0; i < 2 * NI8; ++i) dst[i] = dst8(is_k, i >> 1, i & 1, row, u);
     if constexpr (NI8 == 2) {
-      const uint32_t a[4] = {base + dst[0], base + dst[1], base + dst[2], base + dst[3]};
+      const uint32_t a[4] = {dst[0], dst[1], dst[2], dst[3]};
       const u32x4 vv[4] = {e4m3x8_to_bf16(raw[0][0], raw[0][1]), e4m3x8_to_bf16(raw[0][2], raw[0][3]),
                            e4m3x8_to_bf16(raw[1][0], raw[1][1]), e4m3x8_to_bf16(raw[1][2], raw[1][3])};
       lds_write_b128x4_now(a, vv);
     } else {
-      lds_write_b128x2_now(base + dst[0], base + dst[1], e4m3x8_to_bf16(raw[0][0], raw[0][1]),
+      lds_write_b128x2_now(dst[0], dst[1], e4m3x8_to_bf16(raw[0][0], raw[0][1]),
                            e4m3x8_to_bf16(raw[0][2], raw[0][3]));
     }
   };
@@ -958,17 +986,23 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     for (int n = 0; n < NI8; ++n) rv[n] = lds_read_b128_asm(smem_u + L::land8V + (kbw + RPI8 * n) * D + 16 * lane);
     lgkm_wait_n<0>(rk);
     lgkm_wait_n<0>(rv);
-    const uint32_t kb_ = smem_u + k_slot_off, vb_ = smem_u + v_slot_off;
+    uint32_t row = smem_u + row8, uk = uk8, uv = uv8;
+    asm volatile("" : "+v"(row), "+v"(uk), "+v"(uv));
+    auto dk = [&](int i) { return dst8(true, i >> 1, i & 1, row + (uint32_t)k_slot_off, uk); };
+    auto dv = [&](int i) { return dst8(false, i >> 1, i & 1, row + (uint32_t)v_slot_off, uv); };
     if constexpr (NI8 == 2) {
-      const uint32_t a[8] = {kb_ + dst_k8[0], kb_ + dst_k8[1], kb_ + dst_k8[2], kb_ + dst_k8[3],
-                             vb_ + dst_v8[0], vb_ + dst_v8[1], vb_ + dst_v8[2], vb_ + dst_v8[3]};
-      const u32x4 vv[8] = {e4m3x8_to_bf16(rk[0][0], rk[0][1]), e4m3x8_to_bf16(rk[0][2], rk[0][3]),
-                           e4m3x8_to_bf16(rk[1][0], rk[1][1]), e4m3x8_to_bf16(rk[1][2], rk[1][3]),
-                           e4m3x8_to_bf16(rv[0][0], rv[0][1]), e4m3x8_to_bf16(rv[0][2], rv[0][3]),
+      // K's four writes go out first, unawaited, so that only four decoded
+      // units are held at a time; V's writes end with the wait for all eight.
+      const uint32_t ak[4] = {dk(0), dk(1), dk(2), dk(3)};
+      const u32x4 vk[4] = {e4m3x8_to_bf16(rk[0][0], rk[0][1]), e4m3x8_to_bf16(rk[0][2], rk[0][3]),
+                           e4m3x8_to_bf16(rk[1][0], rk[1][1]), e4m3x8_to_bf16(rk[1][2], rk[1][3])};
+      lds_write_b128x4_issue(ak, vk);
+      const uint32_t av[4] = {dv(0), dv(1), dv(2), dv(3)};
+      const u32x4 vv[4] = {e4m3x8_to_bf16(rv[0][0], rv[0][1]), e4m3x8_to_bf16(rv[0][2], rv[0][3]),
                            e4m3x8_to_bf16(rv[1][0], rv[1][1]), e4m3x8_to_bf16(rv[1][2], rv[1][3])};
-      lds_write_b128x8_now(a, vv);
+      lds_write_b128x4_now(av, vv);
     } else {
-      const uint32_t a[4] = {kb_ + dst_k8[0], kb_ + dst_k8[1], vb_ + dst_v8[0], vb_ + dst_v8[1]};
+      const uint32_t a[4] = {dk(0), dk(1), dv(0), dv(1)};
       const u32x4 vv[4] = {e4m3x8_to_bf16(rk[0][0], rk[0][1]), e4m3x8_to_bf16(rk[0][2], rk[0][3]),
                            e4m3x8_to_bf16(rv[0][0], rv[0][1]), e4m3x8_to_bf16(rv[0][2], rv[0][3])};
       lds_write_b128x4_now(a, vv);
@@ -1056,11 +1090,11 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
         dma8(kcache, 0, pg0, L::land8K);
         dma8(vcache, 0, pg0, L::land8V);
         wait_vm0();
-        decode8(L::land8K, L::kOff(0), dst_k8);
-        decode8(L::land8V, L::vOff(0), dst_v8);
+        decode8(L::land8K, L::kOff(0), true);
+        decode8(L::land8V, L::vOff(0), false);
         dma8(kcache, 1, pg_v, L::land8K);
         wait_vm0();
-        decode8(L::land8K, L::kOff(1), dst_k8);
+        decode8(L::land8K, L::kOff(1), true);
       } else {
         dma(BoolTag<true>{}, kcache, 0, pg0, L::kOff(0));
         dma(BoolTag<false>{}, vcache, 0, pg0, L::vOff(0));
@@ -1124,7 +1158,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       if (band2) load_bias(cur, tile_kb(j + 2));
       __builtin_amdgcn_sched_barrier(0);
       // Phase B: PV of tile j (MFMA) || row max of tile j+1 (VALU).
-      const float mx = mx_at(phase_b<D, L::vOff(PAR), alibi>(smem, pb, oacc, lane, nxt, al_s) * c, tile_kb(j + 1));
+      const float mx = mx_at(phase_b<D, L::vOff(PAR), alibi, KV8 && alibi>(smem, pb, oacc, lane, nxt, al_s) * c, tile_kb(j + 1));
       // Masks of an edge tile j+2 in the released set, then the barrier that
       // publishes K(j+2) and V(j+1).  Raw bias loads may stay in flight.
       if (!band2 && j + 2 < nt && !is_plain(tile_kb(j + 2))) start_general(cur, tile_kb(j + 2));
@@ -1148,8 +1182,16 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   const float inv = l_tot > 0.f ? (KV8 ? p.v_scale / l_tot : 1.f / l_tot) : 0.f;
   const float lse_v = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : neg_inf();
   if (!row_valid) return;
+  // The lane's token and head once more, from an opaque copy of the lane id:
+  // the compiler would otherwise keep the output offsets from before the
+  // tile loop, in registers spilled across it.
+  int lane_e = l32;
+  asm volatile("" : "+v"(lane_e));
+  const int r_e = row0 + 32 * w + lane_e;
+  const int qi_e = r_e / G;
+  const int64_t row_out = (int64_t)(tok0 + qi_e) * p.H + g * G + (r_e - qi_e * G);
   if (p.S == 1) {
-    uint16_t *op = p.out + ((int64_t)tok * p.H + head) * D;
+    uint16_t *op = p.out + row_out * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -1160,9 +1202,10 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
                   pack2_bf16(oacc[db][4 * jg + 2] * inv, oacc[db][4 * jg + 3] * inv)};
       }
     }
-    if (hf == 0 && p.lse) p.lse[(int64_t)tok * p.H + head] = lse_v;
+    if (hf == 0 && p.lse) p.lse[row_out] = lse_v;
   } else {
-    float *pp = p.part_out + (((int64_t)s * p.num_tokens + tok) * p.H + head) * D;
+    const int64_t part_row = (int64_t)s * p.num_tokens * p.H + row_out;
+    float *pp = p.part_out + part_row * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -1173,7 +1216,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
                   oacc[db][4 * jg + 3] * inv};
       }
     }
-    if (hf == 0) p.part_lse[((int64_t)s * p.num_tokens + tok) * p.H + head] = lse_v;
+    if (hf == 0) p.part_lse[part_row] = lse_v;
   }
 }
 
