@@ -154,16 +154,16 @@ __device__ __forceinline__ void lds_write_b128x4_now(const uint32_t (&a)[4], con
       : "memory");
 }
 
-// E4M3 (OCP) codes to bf16: v_cvt_pk_f32_fp8 decodes two codes exactly to
-// fp32 (every E4M3 value has at most four significant bits, so its upper
-// 16 bits are its bf16 form); v_perm packs those halves.  Four codes of one
-// dword become two dwords of bf16 pairs in element order.
+// E4M3 (OCP) codes to bf16: v_cvt_scalef32_pk_bf16_fp8 turns the two codes
+// of one 16-bit half of a dword into a bf16 pair (first code in the low
+// half), here with scale 1.  The conversion is exact: an E4M3 value has at
+// most four significant bits and an exponent inside bf16's range.  Four
+// codes of one dword become two dwords of bf16 pairs in element order.
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t x) {
-  typedef float f32x2_ __attribute__((ext_vector_type(2)));
-  const f32x2_ a = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, false);
-  const f32x2_ b = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, true);
-  return u32x2{__builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u),
-               __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u)};
+  typedef __bf16 bf16x2_ __attribute__((ext_vector_type(2)));
+  const bf16x2_ lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+  const bf16x2_ hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
+  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t x0, uint32_t x1) {
   const u32x2 lo = e4m3x4_to_bf16(x0), hi = e4m3x4_to_bf16(x1);
