@@ -12,7 +12,8 @@ uses a traffic figure only while the kernel source is unchanged.
 
 trace: per kernel, the calls, the median duration and the mean of the last
 K dispatches (bench.py times exactly K steps after its warm-up and clock
-settle, so these are the timed, steady-state calls), with min and max over
+settle, so these are the timed, steady-state calls: K = --steps for the
+batched decodes, max(5, steps // 2) for the others), with min and max over
 all dispatches (the early ones run before the shader clock has ramped up).
 
 traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, two runs) of the
@@ -47,6 +48,15 @@ DOMINANT = {
     "chunked_prefill_relbf16": "attn_kernel", "continuous_batch": "attn_kernel", "kv_write": "kv_write_kernel",
 }
 
+# bench.py times --steps calls of the batched decodes and max(5, steps // 2)
+# of every other workload.
+FULL_STEPS = ("batched_decode", "batched_decode_fp8")
+
+
+def timed_steps(wl: str, steps: int) -> int:
+    return steps if wl in FULL_STEPS else max(5, steps // 2)
+
+
 COMMANDS = {
     "trace": ("rocprofv3 --kernel-trace --stats --output-format csv -d $GRAFT_REPO_ROOT/gpurun_out/prof/{wl} "
               "-o {wl} -- python3 $GRAFT_REPO_ROOT/bench.py --only {wl} --steps {steps} --warmup 3 --no-cpu"),
@@ -80,6 +90,7 @@ def _one(dir_: str, pattern: str) -> str:
 def trace(wl: str, dir_: str, steps: int) -> str:
     rows = list(csv.DictReader(open(_one(dir_, "*kernel_trace.csv"))))
     per = collections.OrderedDict()
+    kt = timed_steps(wl, steps)
     for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
         if "rpa::" not in r["Kernel_Name"]:
             continue
@@ -88,11 +99,11 @@ def trace(wl: str, dir_: str, steps: int) -> str:
            "Command (on the MI355X box, from /tmp; `$GRAFT_REPO_ROOT` is the repository root):", "", "```",
            COMMANDS["trace"].format(wl=wl, steps=steps), "```", "",
            f"kernel source hash (bench.py kernel_hash): {_kernel_hash()}", "",
-           f"`timed mean` is the mean of the last {steps} dispatches of each kernel (the calls bench.py times, "
+           f"`timed mean` is the mean of the last {kt} dispatches of each kernel (the calls bench.py times, "
            "after its warm-up and clock settle); min and max are over all dispatches.", "",
            "| kernel | calls | median ns | timed mean ns | min ns | max ns |", "|---|---|---|---|---|---|"]
     for k, d in per.items():
-        tail = d[-steps:]
+        tail = d[-kt:]
         out.append(f"| {k} | {len(d)} | {statistics.median(d):.0f} | {sum(tail) / len(tail):.0f} | {min(d)} | "
                    f"{max(d)} |")
     path = os.path.join(PROFILES, f"{DOMINANT[wl]}_{wl}_trace.md")
