@@ -126,25 +126,6 @@ __device__ __forceinline__ void lds_write_b128x2_now(uint32_t a0, uint32_t a1, u
                : "v"(a0), "v"(a1), "v"(v0), "v"(v1)
                : "memory");
 }
-__device__ __forceinline__ void lds_write_b128x8_now(const uint32_t (&a)[8], const u32x4 (&v)[8]) {
-  asm volatile(
-      "ds_write_b128 %0, %8\n\tds_write_b128 %1, %9\n\tds_write_b128 %2, %10\n\tds_write_b128 %3, %11\n\t"
-      "ds_write_b128 %4, %12\n\tds_write_b128 %5, %13\n\tds_write_b128 %6, %14\n\tds_write_b128 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      :
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(v[0]),
-        "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7])
-      : "memory");
-}
-// Four 16-byte LDS writes issued, not awaited (their source registers are
-// read at issue; a later lgkmcnt wait covers their completion).
-__device__ __forceinline__ void lds_write_b128x4_issue(const uint32_t (&a)[4], const u32x4 (&v)[4]) {
-  asm volatile(
-      "ds_write_b128 %0, %4\n\tds_write_b128 %1, %5\n\tds_write_b128 %2, %6\n\tds_write_b128 %3, %7"
-      :
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3])
-      : "memory");
-}
 __device__ __forceinline__ void lds_write_b128x4_now(const uint32_t (&a)[4], const u32x4 (&v)[4]) {
   asm volatile(
       "ds_write_b128 %0, %4\n\tds_write_b128 %1, %5\n\tds_write_b128 %2, %6\n\tds_write_b128 %3, %7\n\t"
@@ -348,11 +329,14 @@ struct PrefillLds {
   static constexpr int tileBytes = kTileKeys * ROWB;  // 16 KB for head_dim 128
   static constexpr int NK = 2, NV = 2;                // double-buffered K and V tiles
   static constexpr int kOff(int i) { return i * tileBytes; }
-  static constexpr int vOff(int i) { return (NK + i) * tileBytes; }
-  // E4M3 caches: landing areas of the raw K and V rows of one tile.
-  static constexpr int land8K = (NK + NV) * tileBytes;
-  static constexpr int land8V = land8K + kTileKeys * D;
-  static constexpr int bytes = (NK + NV) * tileBytes + (KV8 ? 2 * kTileKeys * D : 0);
+  static constexpr int vOff(int i) { return (NK + i) * tileBytes; }  // bf16 caches
+  // E4M3 caches: the V tiles stay raw (rows of D codes, read transposed and
+  // decoded in registers), and the raw K rows of a tile land in one of two
+  // areas, from which each wave decodes its own rows into a bf16 K slot.
+  static constexpr int rawBytes = kTileKeys * D;
+  static constexpr int v8Off(int i) { return NK * tileBytes + i * rawBytes; }
+  static constexpr int landK(int i) { return NK * tileBytes + (2 + i) * rawBytes; }
+  static constexpr int bytes = KV8 ? NK * tileBytes + 4 * rawBytes : (NK + NV) * tileBytes;
 };
 
 // K and V tiles are stored row-major (one key per row) with the 16-byte
@@ -365,6 +349,14 @@ template <int D>
 __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return (4 * (r & 3)) & (D / 8 - 1); }
+// Raw E4M3 V rows (D codes, D / 16 units): unit u of row r sits at
+// u ^ swz_v8(r).  An 8-bit transposing read takes, per half-wave, the same
+// two units of the eight rows {0..3, 8..11} + 4 hf (+ 16 c4); the swizzle
+// moves them onto distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_v8(int r) {
+  return D == 128 ? ((((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2)) : (((r >> 3) & 1) << 1);
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -675,6 +667,33 @@ template <int N>
 __device__ __forceinline__ void lgkm_wait_for(u32x4 &a) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
 }
+template <int N>
+__device__ __forceinline__ void lgkm_wait_for(u32x2 &a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
+}
+// ds_read_b64_tr_b8: within each 16-lane group, lane j receives byte j % 8
+// of the 8-byte rows addressed by lanes j/8, j/8 + 2, ..., j/8 + 14 of the
+// group, in that order.
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr8_asm(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
+  return v;
+}
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read_b128_off(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
+  return v;
+}
+// One 16-byte LDS write, issued and not awaited (its source registers are
+// read at issue).
+template <int OFF>
+__device__ __forceinline__ void lds_write_b128_off(uint32_t addr, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "n"(OFF) : "memory");
+}
+// s_waitcnt operand that waits until at most n vector-memory loads are in flight.
+constexpr int vmcnt_enc(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 template <int D, int VOFF, bool ALIBI, bool LANE_PIN>
 __device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32x16 *oacc, int lane, f32x16 *sn,
@@ -729,6 +748,93 @@ __device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32
     pin(mx[i & 3]);
     __builtin_amdgcn_sched_barrier(0);
   });
+  return fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+}
+
+// Phase B with E4M3 caches.  The V tile stays raw in LDS: the V^T operand
+// of row d and eight slot-order keys is one 8-bit transposing read (lanes of
+// a 16-lane group address the rows 4 hf + {0..3, 8..11} of the 16-key chunk,
+// the lane pairs the two 8-byte halves of one 16-code unit), decoded in
+// registers.  Beside the PV MFMAs and the row max, the wave decodes its own
+// 16 raw K rows of tile j+2, which landed an iteration earlier, into K slot
+// KOFF: after kwait (how many vector-memory loads issued after them may stay
+// in flight: this iteration's V and K direct loads, plus 8 or 32 bias loads),
+// their reads go out before the first V read, and one decoded 16-byte unit is
+// written per group from group 1 on.  LDS reads and writes complete in
+// order, so each operand's lgkmcnt counts the LDS operations issued after it.
+template <int D, int V8OFF, int LANDOFF, int KOFF, bool ALIBI, bool LANE_PIN>
+__device__ __forceinline__ float phase_b8(const char *smem, const bf16x8 *pb, f32x16 *oacc, int lane, f32x16 *sn,
+                                          float al_s, int kwait, uint32_t kraw, uint32_t krow, uint32_t kuk) {
+  constexpr int DB = D / 32;
+  constexpr int NM = 4 * DB;
+  constexpr int EPM = 32 / NM;
+  constexpr int AHEAD = 3;
+  constexpr int U8 = D / 16, RPI8 = 64 / U8, NI8 = 16 / RPI8;
+  constexpr int NKW = 2 * NI8;  // decoded K units per lane
+  constexpr int ROWB = PrefillLds<D>::ROWB;
+  static_assert(NKW + 1 <= NM, "K writes fit the groups");
+  int ln = lane;
+  if constexpr (LANE_PIN) asm volatile("" : "+v"(ln));
+  const int grp = ln >> 4, i16 = ln & 15, hfl = ln >> 5;
+  // Slot row of this lane's address inside each 16-key chunk; its swizzle
+  // does not depend on the chunk.
+  const int r = 4 * hfl + ((i16 >> 1) & 3) + 8 * (i16 >> 3);
+  const int f2 = swz_v8<D>(r) >> 1;
+  uint32_t base[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    base[db] = (uint32_t)(uintptr_t)smem + (uint32_t)(r * D + ((2 * (db ^ f2) + (grp & 1)) << 4) + 8 * (i16 & 1));
+  u32x2 a[NM];
+  auto rd = [&](auto i_tag) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_tag)::value;
+    constexpr int c4 = i / DB, db = i % DB;
+    a[i] = lds_read_tr8_asm<V8OFF + 16 * c4 * D>(base[db]);
+  };
+  if (kwait == 0) __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * NI8));
+  else if (kwait == 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * NI8 + 8));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * NI8 + 32));
+  u32x4 kr[NI8];
+  static_for<0, NI8>([&](auto n_tag) __attribute__((always_inline)) {
+    constexpr int n = decltype(n_tag)::value;
+    kr[n] = lds_read_b128_off<LANDOFF + RPI8 * n * D>(kraw);
+  });
+  float mx[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
+  static_for<0, AHEAD>([&](auto i_tag) __attribute__((always_inline)) { rd(i_tag); });
+  static_for<0, NM>([&](auto i_tag) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_tag)::value;
+    // LDS operations issued after V read i: the V reads of operands i+1 ..
+    // (at most AHEAD - 1 of them) and the K writes of groups m in
+    // [max(1, i - AHEAD), i - 1] (group m writes after its V read m + AHEAD).
+    constexpr int vnew = NM - 1 - i < AHEAD - 1 ? NM - 1 - i : AHEAD - 1;
+    constexpr int mlo = i - AHEAD > 1 ? i - AHEAD : 1;
+    constexpr int mhi = i - 1 < NKW ? i - 1 : NKW;
+    constexpr int knew = mhi >= mlo ? mhi - mlo + 1 : 0;
+    lgkm_wait_for<vnew + knew>(a[i]);
+    const u32x4 v = e4m3x8_to_bf16(a[i][0], a[i][1]);
+    oacc[i % DB] = mfma32(as_bf16x8(v), pb[i / DB], oacc[i % DB]);
+    if constexpr (i + AHEAD < NM) rd(IntTag<i + AHEAD>{});
+    if constexpr (i >= 1 && i <= NKW) {
+      constexpr int m = i - 1, n = m >> 1, e = m & 1;
+      if constexpr (m == 0) {
+        // The K reads are older than every V read, and V read 0 has landed.
+#pragma unroll
+        for (int nn = 0; nn < NI8; ++nn) asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(kr[nn]) : "n"(AHEAD + 1));
+      }
+      const uint32_t flip = (uint32_t)((((D == 128) ? 8 * n : 0) ^ e) << 4);
+      lds_write_b128_off<KOFF + RPI8 * n * ROWB>(krow + (kuk ^ flip),
+                                                  e4m3x8_to_bf16(kr[n][2 * e], kr[n][2 * e + 1]));
+    }
+#pragma unroll
+    for (int e = 0; e < EPM; ++e) {
+      const int x = i * EPM + e;
+      if constexpr (ALIBI) sn[x >> 4][x & 15] = alibi_ramp_add(al_s, x >> 4, x & 15, sn[x >> 4][x & 15]);
+      mx[i & 3] = fmaxf(mx[i & 3], sn[x >> 4][x & 15]);
+    }
+    pin(mx[i & 3]);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  // The decoded K rows are complete before the barrier that publishes them.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   return fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
 }
 
@@ -955,6 +1061,27 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
           rs, (__attribute__((address_space(3))) void *)(smem + land_off + (kbw + RPI8 * n) * D), 16,
           vb + (uint32_t)(RPI8 * n) * slot_bytes, 0, 0, 0);
   };
+  // Raw E4M3 V rows of tile jt into the V slot at off: row kbw + rr of the
+  // slot holds key slot rev4(rr) of the wave's block (the order the bf16
+  // tiles use), its units swizzled by swz_v8.  With RPI8 a multiple of 4 the
+  // key slot is RPI8 n + rev4(l / U8), and the swizzle of block n is that of
+  // block 0 XOR 4 n (head_dim 128; 64 has one block).
+  const uint32_t vrow8 = (uint32_t)rev4(x8) * slot_bytes;
+  const uint32_t u8v = (uint32_t)((pc8 ^ swz_v8<D>(kbw + x8)) << 4);
+  auto dma8v = [&](const char *cache, int jt, int page, int off) __attribute__((always_inline)) {
+    const bool live = jt < nt;
+    const int key = (live ? tile_kb(jt) : t0) + kbw;
+    const int nvalid = live ? min(max(kend - key, 0), 16) : 0;
+    const char *src = cache + (uint64_t)(uint32_t)page * page_bytes + (uint64_t)(uint32_t)pslot(key) * slot_bytes;
+    const auto rs = make_rsrc(src, (uint32_t)nvalid * slot_bytes);
+    uint32_t vb = vrow8, u = u8v;
+    asm volatile("" : "+v"(vb), "+v"(u));
+#pragma unroll
+    for (int n = 0; n < NI8; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void *)(smem + off + (kbw + RPI8 * n) * D), 16,
+          vb + (uint32_t)(RPI8 * n) * slot_bytes + (u ^ (uint32_t)(((D == 128) ? 4 * n : 0) << 4)), 0, 0, 0);
+  };
   const uint32_t smem_u = (uint32_t)(uintptr_t)smem;
   auto decode8 = [&](int land_off, int slot_off, bool is_k) __attribute__((always_inline)) {
     u32x4 raw[NI8];
@@ -974,38 +1101,6 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     } else {
       lds_write_b128x2_now(dst[0], dst[1], e4m3x8_to_bf16(raw[0][0], raw[0][1]),
                            e4m3x8_to_bf16(raw[0][2], raw[0][3]));
-    }
-  };
-  // Both landings at once: the four (D = 128) raw reads go out together and
-  // the eight bf16 writes complete in one wait.
-  auto decode8_kv = [&](int k_slot_off, int v_slot_off) __attribute__((always_inline)) {
-    u32x4 rk[NI8], rv[NI8];
-#pragma unroll
-    for (int n = 0; n < NI8; ++n) rk[n] = lds_read_b128_asm(smem_u + L::land8K + (kbw + RPI8 * n) * D + 16 * lane);
-#pragma unroll
-    for (int n = 0; n < NI8; ++n) rv[n] = lds_read_b128_asm(smem_u + L::land8V + (kbw + RPI8 * n) * D + 16 * lane);
-    lgkm_wait_n<0>(rk);
-    lgkm_wait_n<0>(rv);
-    uint32_t row = smem_u + row8, uk = uk8, uv = uv8;
-    asm volatile("" : "+v"(row), "+v"(uk), "+v"(uv));
-    auto dk = [&](int i) { return dst8(true, i >> 1, i & 1, row + (uint32_t)k_slot_off, uk); };
-    auto dv = [&](int i) { return dst8(false, i >> 1, i & 1, row + (uint32_t)v_slot_off, uv); };
-    if constexpr (NI8 == 2) {
-      // K's four writes go out first, unawaited, so that only four decoded
-      // units are held at a time; V's writes end with the wait for all eight.
-      const uint32_t ak[4] = {dk(0), dk(1), dk(2), dk(3)};
-      const u32x4 vk[4] = {e4m3x8_to_bf16(rk[0][0], rk[0][1]), e4m3x8_to_bf16(rk[0][2], rk[0][3]),
-                           e4m3x8_to_bf16(rk[1][0], rk[1][1]), e4m3x8_to_bf16(rk[1][2], rk[1][3])};
-      lds_write_b128x4_issue(ak, vk);
-      const uint32_t av[4] = {dv(0), dv(1), dv(2), dv(3)};
-      const u32x4 vv[4] = {e4m3x8_to_bf16(rv[0][0], rv[0][1]), e4m3x8_to_bf16(rv[0][2], rv[0][3]),
-                           e4m3x8_to_bf16(rv[1][0], rv[1][1]), e4m3x8_to_bf16(rv[1][2], rv[1][3])};
-      lds_write_b128x4_now(av, vv);
-    } else {
-      const uint32_t a[4] = {dk(0), dk(1), dv(0), dv(1)};
-      const u32x4 vv[4] = {e4m3x8_to_bf16(rk[0][0], rk[0][1]), e4m3x8_to_bf16(rk[0][2], rk[0][3]),
-                           e4m3x8_to_bf16(rv[0][0], rv[0][1]), e4m3x8_to_bf16(rv[0][2], rv[0][3])};
-      lds_write_b128x4_now(a, vv);
     }
   };
   // The LDS writes of direct loads are tracked by vmcnt only: wait for them
@@ -1087,14 +1182,12 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     {
       const int pg0 = page_t(0);
       if constexpr (KV8) {
-        dma8(kcache, 0, pg0, L::land8K);
-        dma8(vcache, 0, pg0, L::land8V);
+        dma8(kcache, 0, pg0, L::landK(0));
+        dma8(kcache, 1, pg_v, L::landK(1));
+        dma8v(vcache, 0, pg0, L::v8Off(0));
         wait_vm0();
-        decode8(L::land8K, L::kOff(0), true);
-        decode8(L::land8V, L::vOff(0), false);
-        dma8(kcache, 1, pg_v, L::land8K);
-        wait_vm0();
-        decode8(L::land8K, L::kOff(1), true);
+        decode8(L::landK(0), L::kOff(0), true);
+        decode8(L::landK(1), L::kOff(1), true);
       } else {
         dma(BoolTag<true>{}, kcache, 0, pg0, L::kOff(0));
         dma(BoolTag<false>{}, vcache, 0, pg0, L::vOff(0));
@@ -1104,14 +1197,20 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       begin(sa, tile_kb(0));
       wait_vm0();
       __syncthreads();
+      // E4M3: the raw K(2), decoded in iteration 0's phase B (this wave's
+      // rows of landing 0 were read by its own decode above).
+      if constexpr (KV8) dma8(kcache, 2, pg_k, L::landK(0));
       finish(sa, tile_kb(0));
       qk_mfma<D, true>(smem + L::kOff(0), qf, sa, l32, hf);
       if constexpr (alibi) tile_alibi_ramp(sa, al_s);
       update_max(xor32_max(mx_at(tile_rowmax(sa) * c, tile_kb(0))));
       zero(sb);
       if (nt > 1) begin(sb, tile_kb(1));
-      // Iteration 0 refills K slot 0: every wave must be done reading K(0).
-      __syncthreads();
+      // Iteration 0 refills K slot 0: every wave must be done reading K(0)
+      // (its reads completed before the QK used them; E4M3: a raw barrier, so
+      // that the raw K(2) may stay in flight).
+      if constexpr (KV8) barrier_raw();
+      else __syncthreads();
     }
 
     // One pipeline iteration; PAR = j % 2 selects slots and register sets.
@@ -1134,22 +1233,33 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       const bool zc = !has_next || is_plain(tile_kb(j + 1));
       if (!zc) finish(nxt, tile_kb(j + 1));
       __builtin_amdgcn_sched_barrier(0);
-      // Direct loads: K(j+2) into K slot PAR (K(j) was consumed before the
-      // last barrier), V(j+1) into V slot 1-PAR.
       if constexpr (KV8) {
-        dma8(kcache, j + 2, pg_k, L::land8K);
-        dma8(vcache, j + 1, pg_v, L::land8V);
+        // Direct loads: raw V(j+1) into V slot 1-PAR, then the raw K(j+3)
+        // into landing 1-PAR (K(j+1) was decoded from it in the last phase
+        // B), so that the waits can leave K in flight for an iteration.
+        if (j + 3 - pc_base == 64) {
+          pc = pc_next;
+          pc_base += 64;
+          pc_next = load_pages(pc_base + 64);
+        }
+        const int pg3 = page_t(j + 3);
+        dma8v(vcache, j + 1, pg_v, L::v8Off(1 - PAR));
+        dma8(kcache, j + 3, pg3, L::landK(1 - PAR));
+        pg_v = pg_k;
+        pg_k = pg3;
       } else {
+        // Direct loads: K(j+2) into K slot PAR (K(j) was consumed before the
+        // last barrier), V(j+1) into V slot 1-PAR.
         dma(BoolTag<true>{}, kcache, j + 2, pg_k, L::kOff(PAR));
         dma(BoolTag<false>{}, vcache, j + 1, pg_v, L::vOff(1 - PAR));
+        if (j + 3 - pc_base == 64) {
+          pc = pc_next;
+          pc_base += 64;
+          pc_next = load_pages(pc_base + 64);
+        }
+        pg_v = pg_k;
+        pg_k = page_t(j + 3);
       }
-      if (j + 3 - pc_base == 64) {
-        pc = pc_next;
-        pc_base += 64;
-        pc_next = load_pages(pc_base + 64);
-      }
-      pg_v = pg_k;
-      pg_k = page_t(j + 3);
       const float m_use = m_run == neg_inf() ? 0.f : m_run;
       __builtin_amdgcn_sched_barrier(0);
       // Phase A: QK of tile j+1 (MFMA) || exp of tile j (VALU).
@@ -1157,16 +1267,32 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       const bool band2 = j + 2 < nt && is_band(tile_kb(j + 2));
       if (band2) load_bias(cur, tile_kb(j + 2));
       __builtin_amdgcn_sched_barrier(0);
-      // Phase B: PV of tile j (MFMA) || row max of tile j+1 (VALU).
-      const float mx = mx_at(phase_b<D, L::vOff(PAR), alibi, KV8 && alibi>(smem, pb, oacc, lane, nxt, al_s) * c, tile_kb(j + 1));
+      // Phase B: PV of tile j (MFMA) || row max of tile j+1 (VALU); E4M3:
+      // also the decode of this wave's rows of the raw K(j+2) into K slot PAR.
+      float mx_raw;
+      if constexpr (KV8) {
+        uint32_t krow = smem_u + row8, kuk = uk8, kraw = smem_u + (uint32_t)(kbw * D + 16 * lane);
+        asm volatile("" : "+v"(krow), "+v"(kuk), "+v"(kraw));
+        mx_raw = phase_b8<D, L::v8Off(PAR), L::landK(PAR), L::kOff(PAR), alibi, alibi>(
+            smem, pb, oacc, lane, nxt, al_s, !band2 ? 0 : bias_fast ? 1 : 2, kraw, krow, kuk);
+      } else {
+        mx_raw = phase_b<D, L::vOff(PAR), alibi, false>(smem, pb, oacc, lane, nxt, al_s);
+      }
+      const float mx = mx_at(mx_raw * c, tile_kb(j + 1));
       // Masks of an edge tile j+2 in the released set, then the barrier that
-      // publishes K(j+2) and V(j+1).  Raw bias loads may stay in flight.
+      // publishes K(j+2) and V(j+1).  Raw bias loads (and with E4M3 caches
+      // the raw K(j+3)) may stay in flight.
       if (!band2 && j + 2 < nt && !is_plain(tile_kb(j + 2))) start_general(cur, tile_kb(j + 2));
       __builtin_amdgcn_sched_barrier(0);
-      if (!band2) wait_vm0();
-      else if (bias_fast) wait_vm8();
-      else wait_vm32();
-      if constexpr (KV8) decode8_kv(L::kOff(PAR), L::vOff(1 - PAR));
+      if constexpr (KV8) {
+        if (!band2) __builtin_amdgcn_s_waitcnt(vmcnt_enc(NI8));
+        else if (bias_fast) __builtin_amdgcn_s_waitcnt(vmcnt_enc(NI8 + 8));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_enc(NI8 + 32));
+      } else {
+        if (!band2) wait_vm0();
+        else if (bias_fast) wait_vm8();
+        else wait_vm32();
+      }
       barrier_raw();
       if (has_next) update_max(xor32_max(mx));
     };
@@ -1175,6 +1301,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       iteration(BoolTag<false>{}, j, sa, sb);
       if (j + 1 < nt) iteration(BoolTag<true>{}, j + 1, sb, sa);
     }
+    if constexpr (KV8) wait_vm0();  // the raw K loads past the last tile
   }
 
   // Epilogue: lane (l32, hf) holds O^T[d = 32 db + 8 (j/4) + 4 hf + j%4][row l32].
