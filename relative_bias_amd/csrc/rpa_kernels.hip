@@ -1021,30 +1021,30 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
           rs, (__attribute__((address_space(3))) void *)(smem + lds_off + (kbw + RPI * n) * ROWB), 16, voff, 0, 0, 0);
     }
   };
-  // E4M3 caches: the direct loads bring the raw rows of a tile (key order,
-  // D bytes a row) to a landing area, wave w its own 16 keys; once they
-  // have arrived (the wait before the barrier that publishes the tile) the
-  // wave decodes its rows into the tile's bf16 slot at the places the bf16
-  // loads would have filled, so the rest of the pipeline is unchanged.
+  // E4M3 caches: the direct loads bring the raw K rows of a tile (key order,
+  // D bytes a row) to one of two landing areas, wave w its own 16 keys, and
+  // the wave decodes its rows into the tile's bf16 K slot at the places the
+  // bf16 loads would have filled (in the prologue, and for later tiles in
+  // the phase B before their QK), so phase A is unchanged.  V rows stay raw
+  // (dma8v, phase_b8).
   constexpr int U8 = D / 16, RPI8 = 64 / U8, NI8 = 16 / RPI8;
-  // Block n of a wave's E4M3 rows: lane l loads (and later reads back) raw
+  // Block n of a wave's raw K rows: lane l loads (and later reads back) raw
   // unit l % U8 of landing row RPI8 n + l / U8, and writes it decoded as the
-  // two bf16 units 2 (l % U8) + e of tile row kbw + rev4(RPI8 n + l / U8),
-  // at the places the swizzle gives them.  RPI8 is a multiple of 4, so
-  // rev4 keeps RPI8 n as it is; the V swizzle does not depend on n, and the
-  // K swizzle of block n is that of block 0 XOR 8 n (head_dim 128; 64 has
-  // one block).  Four lane registers give every address.
+  // two bf16 units 2 (l % U8) + e of K row kbw + rev4(RPI8 n + l / U8), at
+  // the places the swizzle gives them.  RPI8 is a multiple of 4, so rev4
+  // keeps RPI8 n as it is, and the K swizzle of block n is that of block 0
+  // XOR 8 n (head_dim 128; 64 has one block).  Three lane registers give
+  // every address.
   const int x8 = lane / U8, pc8 = lane % U8;
   const int r8 = kbw + rev4(x8);
   const uint32_t row8 = (uint32_t)(r8 * ROWB);
   const uint32_t uk8 = (uint32_t)(((2 * pc8) ^ swz_k<D>(r8)) << 4);
-  const uint32_t uv8 = (uint32_t)(((2 * pc8) ^ swz_v<D>(r8)) << 4);
   const uint32_t vb8 = (uint32_t)x8 * slot_bytes + (uint32_t)(pc8 << 4);
-  // Tile-slot byte offset of unit e of block n (K or V), from pinned copies
-  // of the lane registers so that the compiler forms them where they are
-  // used instead of holding 2 NI8 offsets per operand across the tile loop.
-  auto dst8 = [&](bool is_k, int n, int e, uint32_t row, uint32_t u) {
-    const uint32_t flip = (uint32_t)((((is_k && D == 128) ? 8 * n : 0) ^ e) << 4);
+  // K-slot byte offset of unit e of block n, from pinned copies of the lane
+  // registers so that the compiler forms them where they are used instead
+  // of holding 2 NI8 offsets across the tile loop.
+  auto dst8 = [&](int n, int e, uint32_t row, uint32_t u) {
+    const uint32_t flip = (uint32_t)((((D == 128) ? 8 * n : 0) ^ e) << 4);
     return row + (uint32_t)(RPI8 * n * ROWB) + (u ^ flip);
   };
   auto dma8 = [&](const char *cache, int jt, int page, int land_off) __attribute__((always_inline)) {
@@ -1083,16 +1083,17 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
           vb + (uint32_t)(RPI8 * n) * slot_bytes + (u ^ (uint32_t)(((D == 128) ? 4 * n : 0) << 4)), 0, 0, 0);
   };
   const uint32_t smem_u = (uint32_t)(uintptr_t)smem;
-  auto decode8 = [&](int land_off, int slot_off, bool is_k) __attribute__((always_inline)) {
+  // Prologue form of the K decode (later tiles are decoded inside phase_b8).
+  auto decode8 = [&](int land_off, int slot_off) __attribute__((always_inline)) {
     u32x4 raw[NI8];
 #pragma unroll
     for (int n = 0; n < NI8; ++n) raw[n] = lds_read_b128_asm(smem_u + land_off + (kbw + RPI8 * n) * D + 16 * lane);
     lgkm_wait_n<0>(raw);
-    uint32_t row = smem_u + slot_off + row8, u = is_k ? uk8 : uv8;
+    uint32_t row = smem_u + slot_off + row8, u = uk8;
     asm volatile("" : "+v"(row), "+v"(u));
     uint32_t dst[4];
 #pragma unroll
-    for (int i = 0; i < 2 * NI8; ++i) dst[i] = dst8(is_k, i >> 1, i & 1, row, u);
+    for (int i = 0; i < 2 * NI8; ++i) dst[i] = dst8(i >> 1, i & 1, row, u);
     if constexpr (NI8 == 2) {
       const uint32_t a[4] = {dst[0], dst[1], dst[2], dst[3]};
       const u32x4 vv[4] = {e4m3x8_to_bf16(raw[0][0], raw[0][1]), e4m3x8_to_bf16(raw[0][2], raw[0][3]),
@@ -1186,8 +1187,8 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
         dma8(kcache, 1, pg_v, L::landK(1));
         dma8v(vcache, 0, pg0, L::v8Off(0));
         wait_vm0();
-        decode8(L::landK(0), L::kOff(0), true);
-        decode8(L::landK(1), L::kOff(1), true);
+        decode8(L::landK(0), L::kOff(0));
+        decode8(L::landK(1), L::kOff(1));
       } else {
         dma(BoolTag<true>{}, kcache, 0, pg0, L::kOff(0));
         dma(BoolTag<false>{}, vcache, 0, pg0, L::vOff(0));

@@ -87,7 +87,7 @@ def _one(dir_: str, pattern: str) -> str:
     return hits[0]
 
 
-def trace(wl: str, dir_: str, steps: int) -> str:
+def trace(wl: str, dir_: str, steps: int, out_dir: str = PROFILES) -> str:
     rows = list(csv.DictReader(open(_one(dir_, "*kernel_trace.csv"))))
     per = collections.OrderedDict()
     kt = timed_steps(wl, steps)
@@ -106,7 +106,7 @@ def trace(wl: str, dir_: str, steps: int) -> str:
         tail = d[-kt:]
         out.append(f"| {k} | {len(d)} | {statistics.median(d):.0f} | {sum(tail) / len(tail):.0f} | {min(d)} | "
                    f"{max(d)} |")
-    path = os.path.join(PROFILES, f"{DOMINANT[wl]}_{wl}_trace.md")
+    path = os.path.join(out_dir, f"{DOMINANT[wl]}_{wl}_trace.md")
     with open(path, "w") as f:
         f.write("\n".join(out) + "\n")
     return path
@@ -125,7 +125,7 @@ def _counter(dir_: str, counter: str, kernel_prefix: str):
     return name, list(per.values())
 
 
-def traffic(wl: str, fetch_dir: str, write_dir: str, fetch_copy: str, write_copy: str) -> str:
+def traffic(wl: str, fetch_dir: str, write_dir: str, fetch_copy: str, write_copy: str, out_dir: str = PROFILES) -> str:
     nb = 1 << 30
     _, cf = _counter(fetch_copy, "FETCH_SIZE", "copyBuffer")
     _, cw = _counter(write_copy, "WRITE_SIZE", "copyBuffer")
@@ -145,7 +145,7 @@ def traffic(wl: str, fetch_dir: str, write_dir: str, fetch_copy: str, write_copy
          "commands": [COMMANDS["copy"].format(c="FETCH_SIZE"), COMMANDS["copy"].format(c="WRITE_SIZE"),
                       COMMANDS["pmc"].format(c="FETCH_SIZE", wl=wl), COMMANDS["pmc"].format(c="WRITE_SIZE", wl=wl)],
          "dispatches_sampled": [len(fv), len(wv)]}
-    path = os.path.join(PROFILES, f"{DOMINANT[wl]}_{wl}_traffic.json")
+    path = os.path.join(out_dir, f"{DOMINANT[wl]}_{wl}_traffic.json")
     with open(path, "w") as f:
         json.dump(j, f, indent=1)
     return path
