@@ -1230,6 +1230,11 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     // arrive.
     auto iteration = [&](auto par_tag, int j, f32x16 *cur, f32x16 *nxt) __attribute__((always_inline)) {
       constexpr int PAR = decltype(par_tag)::value ? 1 : 0;
+      // The wave issues at raised priority from here to the end of phase A,
+      // so that the other wave on its SIMD yields while this one is in the
+      // VALU-heavy phase (measured 2-3 % faster on uniform shapes and the
+      // continuous batch, no change on the chunked prefill).
+      __builtin_amdgcn_s_setprio(1);
       const bool has_next = j + 1 < nt;
       const bool zc = !has_next || is_plain(tile_kb(j + 1));
       if (!zc) finish(nxt, tile_kb(j + 1));
@@ -1265,6 +1270,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       __builtin_amdgcn_sched_barrier(0);
       // Phase A: QK of tile j+1 (MFMA) || exp of tile j (VALU).
       l_run += phase_a<D>(smem + L::kOff(1 - PAR), qf, nxt, cur, c, m_at(m_use, tile_kb(j)), pb, l32, hf, zc);
+      __builtin_amdgcn_s_setprio(0);
       const bool band2 = j + 2 < nt && is_band(tile_kb(j + 2));
       if (band2) load_bias(cur, tile_kb(j + 2));
       __builtin_amdgcn_sched_barrier(0);
