@@ -148,13 +148,17 @@ CASES.update({
     "prefill_d64_gqa2": ([64, 200], [64, 333], 4, 2, 64, 40, 0.05, 0.2, (-1, -1)),
     "mixed_window": ([1, 130, 1, 40, 1], [2000, 500, 70, 3000, 1], 16, 2, 128, 100, 1 / 32, 1 / 16, (127, 0)),
     "prefill_nobias_mha": ([100, 3], [400, 3], 4, 4, 128, 0, 0.1, 0.1, (-1, -1)),
+    # one q-tile per request over 1 to 5 key tiles, the last one partial: the
+    # prefill's raw K tiles two ahead of their QK run past the end (zero-filled)
+    "prefill_tile_counts": ([32] * 5, [40, 100, 150, 250, 300], 16, 4, 128, 64, 1 / 32, 1 / 16, (-1, -1)),
+    "prefill_tile_counts_d64_window": ([32] * 4, [70, 130, 200, 260], 8, 2, 64, 32, 0.05, 0.2, (100, 0)),
 })
 
 # Split counts per case: 0 (balanced when it applies, else 1) always, and
 # explicit splits for a few.
 SPLITS = {name: [0] for name in CASES}
 SPLITS.update({"ragged_d128": [0, 1, 3], "gqa4_d128": [0, 4], "prefill_d128": [1, 2], "mixed_window": [1, 3],
-               "two_tokens_g8": [0, 2]})
+               "two_tokens_g8": [0, 2], "prefill_tile_counts": [1, 2], "prefill_tile_counts_d64_window": [1, 2]})
 PARAMS = [(n, S) for n in CASES for S in SPLITS[n]]
 
 
