@@ -251,8 +251,9 @@ def measure_kv_write(steps, warmup):
 
 def hbm_read_ceiling(gib=4, reps=10):
     """Streaming-read rate of the device: one pass of 16-byte nontemporal
-    loads over a `gib` GiB buffer (larger than the 256 MB last-level cache)
-    by libhbmprobe.so's kernel, best and median of `reps` passes."""
+    loads over a `gib` GiB buffer (larger than the 256 MB last-level cache),
+    one contiguous chunk per workgroup, by libhbmprobe.so's kernel, best and
+    median of `reps` passes."""
     import ctypes
     import statistics
     import torch

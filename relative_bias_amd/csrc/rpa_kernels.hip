@@ -694,6 +694,10 @@ __device__ __forceinline__ void lds_write_b128_off(uint32_t addr, u32x4 v) {
 }
 // s_waitcnt operand that waits until at most n vector-memory loads are in flight.
 constexpr int vmcnt_enc(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+// Cache policy of a buffer load (its aux operand): nt, for data read once.
+// The balanced decodes' K/V streams take it; a streaming read probe reads
+// HBM about 10 % faster with it than with the default policy.
+constexpr int kNonTemporal = 2;
 
 template <int D, int VOFF, bool ALIBI, bool LANE_PIN>
 __device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32x16 *oacc, int lane, f32x16 *sn,
@@ -2131,11 +2135,11 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
 #pragma unroll
     for (int n = 0; n < NLD; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void *)(st + n * 1024), 16,
-                                               gk[n], 0, 0, 0);
+                                               gk[n], 0, 0, kNonTemporal);
 #pragma unroll
     for (int n = 0; n < NLD; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void *)(st + VHALF + n * 1024), 16, gv[n], 0, 0, 0);
+          rv, (__attribute__((address_space(3))) void *)(st + VHALF + n * 1024), 16, gv[n], 0, 0, kNonTemporal);
   };
 
   f32x4 oacc[DB];
@@ -2721,11 +2725,11 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
 #pragma unroll
     for (int n = 0; n < NLD; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void *)(st + n * 1024), 16,
-                                               gk[n], 0, 0, 0);
+                                               gk[n], 0, 0, kNonTemporal);
 #pragma unroll
     for (int n = 0; n < NLD; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void *)(st + VHALF + n * 1024), 16, gv[n], 0, 0, 0);
+          rv, (__attribute__((address_space(3))) void *)(st + VHALF + n * 1024), 16, gv[n], 0, 0, kNonTemporal);
   };
 
   f32x4 oacc[DB];
