@@ -3,11 +3,12 @@
     python -m relative_bias_amd.profile_summary trace WORKLOAD DIR [--steps K]
     python -m relative_bias_amd.profile_summary traffic WORKLOAD FETCH_DIR WRITE_DIR FETCH_COPY_DIR WRITE_COPY_DIR
     python -m relative_bias_amd.profile_summary mfma WORKLOAD DIR
+    python -m relative_bias_amd.profile_summary l2 WORKLOAD DIR
 
 Each DIR is the -d directory of one rocprofv3 run of bench.py made with the
 command the summary records (see COMMANDS below); they run committed files
 only.  The summaries land in profiles/ as <kernel>_<workload>_{trace.md,
-traffic.json, mfma.json}, stamped with bench.kernel_hash() so that bench.py
+traffic.json, mfma.json, l2.json}, stamped with bench.kernel_hash() so that bench.py
 uses a traffic figure only while the kernel source is unchanged.
 
 trace: per kernel, the calls, the median duration and the mean of the last
@@ -23,6 +24,10 @@ dominant kernel, each scaled by what the same counter reads for a plain
 mfma: SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16 and
 GRBM_GUI_ACTIVE of the dominant kernel: MFMA pipe busy fraction and executed
 MFMA flops against the algorithmic flops.
+
+l2: TCC_HIT_sum, TCC_MISS_sum, TCC_READ_sum and TCC_REQ_sum (one run) of the
+dominant kernel: L2 requests per launch and the fraction that hit, against
+the kernel's algorithmic bytes in 128-byte lines.
 """
 from __future__ import annotations
 
@@ -67,7 +72,12 @@ COMMANDS = {
     "mfma": ("rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE "
              "--output-format csv -d $GRAFT_REPO_ROOT/gpurun_out/mfma/{wl} -o {wl} -- python3 "
              "$GRAFT_REPO_ROOT/bench.py --only {wl} --steps 3 --warmup 1 --no-cpu"),
+    "l2": ("rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum TCC_READ_sum TCC_REQ_sum --output-format csv "
+           "-d $GRAFT_REPO_ROOT/gpurun_out/l2/{wl} -o {wl} -- python3 $GRAFT_REPO_ROOT/bench.py --only {wl} "
+           "--steps 3 --warmup 1 --no-cpu"),
 }
+
+L2_COUNTERS = ("TCC_HIT_sum", "TCC_MISS_sum", "TCC_READ_sum", "TCC_REQ_sum")
 
 
 def _kernel_hash() -> str:
@@ -191,9 +201,43 @@ def mfma(wl: str, dir_: str) -> str:
     return path
 
 
+def l2(wl: str, dir_: str, out_dir: str = PROFILES, algorithmic_bytes: int = None) -> str:
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    name = None
+    for r in csv.DictReader(open(_one(dir_, "*counter_collection.csv"))):
+        if DOMINANT[wl] not in r["Kernel_Name"] or r["Counter_Name"] not in L2_COUNTERS:
+            continue
+        per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+        name = r["Kernel_Name"]
+    if not per:
+        raise SystemExit(f"no L2 counter samples of {DOMINANT[wl]} under {dir_}")
+    med = {k: statistics.median(d[k] for d in per.values()) for k in L2_COUNTERS}
+    if algorithmic_bytes is None:
+        sys.path.insert(0, ROOT)
+        from relative_bias_amd import metrics, workloads
+        make = {"continuous_batch": workloads.continuous_batch, "batched_decode": workloads.batched_decode,
+                "chunked_prefill": workloads.chunked_prefill}[wl]
+        algorithmic_bytes = metrics.work(make(device="cpu"))["bytes"]
+    hit, miss = med["TCC_HIT_sum"], med["TCC_MISS_sum"]
+    t = {"kernel": _short(name), "workload": wl, "kernel_hash": _kernel_hash(), "dispatches_sampled": len(per),
+         "statistic": "median over dispatches", "counters_per_dispatch": {k: int(round(v)) for k, v in med.items()},
+         "hit_fraction": round(hit / (hit + miss), 4) if hit + miss else None,
+         "algorithmic_bytes": int(algorithmic_bytes),
+         "algorithmic_lines_128b": int(algorithmic_bytes // 128),
+         "requests_per_algorithmic_line": round(med["TCC_REQ_sum"] / (algorithmic_bytes / 128), 3),
+         "notes": "TCC_* are L2 (TCC) request counts summed over the channels of every XCD; a request is one "
+                  "access of up to a 128-byte line, so requests per algorithmic 128-byte line counts how often "
+                  "the kernel's data passes through L2 (re-reads by the q-tiles of a request included)",
+         "command": COMMANDS["l2"].format(wl=wl)}
+    path = os.path.join(out_dir, f"{DOMINANT[wl]}_{wl}_l2.json")
+    with open(path, "w") as f:
+        json.dump(t, f, indent=1)
+    return path
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("kind", choices=("trace", "traffic", "mfma"))
+    ap.add_argument("kind", choices=("trace", "traffic", "mfma", "l2"))
     ap.add_argument("workload", choices=sorted(DOMINANT))
     ap.add_argument("dirs", nargs="+")
     ap.add_argument("--steps", type=int, default=20)
@@ -204,6 +248,8 @@ def main(argv=None):
         if len(a.dirs) != 4:
             raise SystemExit("traffic needs FETCH_DIR WRITE_DIR FETCH_COPY_DIR WRITE_COPY_DIR")
         print(traffic(a.workload, *a.dirs))
+    elif a.kind == "l2":
+        print(l2(a.workload, a.dirs[0]))
     else:
         print(mfma(a.workload, a.dirs[0]))
     return 0

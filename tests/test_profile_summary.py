@@ -69,3 +69,26 @@ def test_traffic_scales_by_the_copy_calibration(tmp_path):
     assert j["hbm_write_bytes_per_launch"] == 20 * 1024
     assert j["hbm_bytes_per_launch"] == 200 * 1024 * 2 + 20 * 1024
     assert j["kernel"] == "attn_kernel<128, false, false, 0>"
+
+
+def test_l2_summary_sums_channels_and_takes_the_median(tmp_path):
+    f = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    rows = []
+    for d, (hit, miss) in {3: (700, 300), 4: (800, 200), 5: (900, 100)}.items():
+        # each counter arrives split over two rows of the dispatch (summed), plus another kernel's rows
+        for c, v in (("TCC_HIT_sum", hit), ("TCC_MISS_sum", miss), ("TCC_READ_sum", hit + miss - 50),
+                     ("TCC_REQ_sum", hit + miss)):
+            rows.append({"Dispatch_Id": d, "Kernel_Name": KN, "Counter_Name": c, "Counter_Value": v / 2})
+            rows.append({"Dispatch_Id": d, "Kernel_Name": KN, "Counter_Name": c, "Counter_Value": v / 2})
+        rows.append({"Dispatch_Id": d + 10, "Kernel_Name": "copyBuffer", "Counter_Name": "TCC_HIT_sum",
+                     "Counter_Value": 1e9})
+    _write(str(tmp_path / "l2" / "k_counter_collection.csv"), rows, f)
+    out = tmp_path / "out"
+    out.mkdir()
+    path = ps.l2("chunked_prefill", str(tmp_path / "l2"), out_dir=str(out), algorithmic_bytes=128 * 500)
+    j = json.load(open(path))
+    assert j["counters_per_dispatch"] == {"TCC_HIT_sum": 800, "TCC_MISS_sum": 200, "TCC_READ_sum": 950,
+                                          "TCC_REQ_sum": 1000}
+    assert j["hit_fraction"] == 0.8 and j["algorithmic_lines_128b"] == 500
+    assert j["requests_per_algorithmic_line"] == 2.0
+    assert os.path.basename(path) == "attn_kernel_chunked_prefill_l2.json"
