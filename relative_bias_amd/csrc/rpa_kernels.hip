@@ -1032,18 +1032,26 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   // the phase B before their QK), so phase A is unchanged.  V rows stay raw
   // (dma8v, phase_b8).
   constexpr int U8 = D / 16, RPI8 = 64 / U8, NI8 = 16 / RPI8;
-  // Block n of a wave's raw K rows: lane l loads (and later reads back) raw
-  // unit l % U8 of landing row RPI8 n + l / U8, and writes it decoded as the
-  // two bf16 units 2 (l % U8) + e of K row kbw + rev4(RPI8 n + l / U8), at
-  // the places the swizzle gives them.  RPI8 is a multiple of 4, so rev4
-  // keeps RPI8 n as it is, and the K swizzle of block n is that of block 0
-  // XOR 8 n (head_dim 128; 64 has one block).  Three lane registers give
-  // every address.
+  // Block n of a wave's raw K rows: lane l loads raw unit l % U8 of landing
+  // row RPI8 n + l / U8.  The decode then reads back raw unit pc8 = l % U8
+  // of landing row RPI8 n + xd and writes it as the two bf16 units 2 pc8 + e
+  // of K row kbw + rev4(RPI8 n + xd), at the places the swizzle gives them.
+  // LDS writes go eight lanes at a time over 32 banks, and the eight lanes of
+  // one row would write only four distinct 16-byte bank groups (2 pc8 + e is
+  // even or odd with e), so with head_dim 128 the lanes of a write group take
+  // eight different rows, xd = (l / U8 + pc8) mod 8: their swizzles then put
+  // the eight units on distinct banks, and the raw reads stay conflict-free.
+  // RPI8 is a multiple of 4, so rev4 keeps RPI8 n as it is, and the K
+  // swizzle of block n is that of block 0 XOR 8 n (head_dim 128; 64 has one
+  // block).  Three lane registers give every address.
   const int x8 = lane / U8, pc8 = lane % U8;
-  const int r8 = kbw + rev4(x8);
+  const int xd = D == 128 ? (x8 + pc8) % RPI8 : x8;
+  const int r8 = kbw + rev4(xd);
   const uint32_t row8 = (uint32_t)(r8 * ROWB);
   const uint32_t uk8 = (uint32_t)(((2 * pc8) ^ swz_k<D>(r8)) << 4);
   const uint32_t vb8 = (uint32_t)x8 * slot_bytes + (uint32_t)(pc8 << 4);
+  // Landing offset (inside a block) of the raw unit this lane decodes.
+  auto raw_at = [&]() { return (uint32_t)(16 * (xd * U8 + pc8)); };
   // K-slot byte offset of unit e of block n, from pinned copies of the lane
   // registers so that the compiler forms them where they are used instead
   // of holding 2 NI8 offsets across the tile loop.
@@ -1091,7 +1099,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   auto decode8 = [&](int land_off, int slot_off) __attribute__((always_inline)) {
     u32x4 raw[NI8];
 #pragma unroll
-    for (int n = 0; n < NI8; ++n) raw[n] = lds_read_b128_asm(smem_u + land_off + (kbw + RPI8 * n) * D + 16 * lane);
+    for (int n = 0; n < NI8; ++n) raw[n] = lds_read_b128_asm(smem_u + land_off + (kbw + RPI8 * n) * D + raw_at());
     lgkm_wait_n<0>(raw);
     uint32_t row = smem_u + slot_off + row8, u = uk8;
     asm volatile("" : "+v"(row), "+v"(u));
@@ -1282,7 +1290,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       // also the decode of this wave's rows of the raw K(j+2) into K slot PAR.
       float mx_raw;
       if constexpr (KV8) {
-        uint32_t krow = smem_u + row8, kuk = uk8, kraw = smem_u + (uint32_t)(kbw * D + 16 * lane);
+        uint32_t krow = smem_u + row8, kuk = uk8, kraw = smem_u + (uint32_t)(kbw * D) + raw_at();
         asm volatile("" : "+v"(krow), "+v"(kuk), "+v"(kraw));
         mx_raw = phase_b8<D, L::v8Off(PAR), L::landK(PAR), L::kOff(PAR), alibi, alibi>(
             smem, pb, oacc, lane, nxt, al_s, !band2 ? 0 : bias_fast ? 1 : 2, kraw, krow, kuk);
