@@ -1823,9 +1823,24 @@ struct BalLds {
 
 // V rows: unit u sits at u ^ swz_vt(r).  A transposing read touches two
 // adjacent units of 16 consecutive rows; the swizzle moves them in pairs so
-// that each half-wave's eight rows cover all banks.
+// that each half-wave's eight rows cover all banks.  Its low bit (head_dim
+// 128) only swaps the two units of a pair, which leaves the reads' banks as
+// they are; it lets the E4M3 decode's writes below reach odd and even bank
+// groups from one instruction.
 template <int D>
-__device__ __forceinline__ int swz_vt(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+__device__ __forceinline__ int swz_vt(int r) {
+  return D == 128 ? (2 * (r & 7)) | (((r >> 2) & 1) ^ 1) : 2 * ((r >> 1) & 3);
+}
+// E4M3 V (head_dim 128): which of the eight raw rows of a block lane l
+// decodes (its raw unit is l % 8).  LDS reads and writes of 16 bytes go eight
+// lanes at a time over 32 banks; with this choice the eight lanes of each
+// group read eight distinct units of their 128-byte raw rows and write eight
+// distinct bank groups of the bf16 rows (four rows whose swizzle has the low
+// bit set, four without), so neither side has bank conflicts.
+__device__ __forceinline__ int v8_row_of(int l) {
+  const int g = l >> 3;
+  return (g >> 1) + 4 * ((g & 1) ^ ((l & 7) >> 2));
+}
 
 // s_waitcnt lgkmcnt(N) that the listed registers wait for (their values
 // arrive by inline-asm LDS reads the compiler does not track).
@@ -2014,10 +2029,12 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
       lk_off[ks] = c16 * ROWB + (((4 * ks + q) ^ swz_k<D>(c16)) << 4);
   }
   uint32_t v8_dst[KV8 ? 2 * NI8 : 1];
+  // E4M3: offset, inside a raw block, of the raw V unit this lane decodes.
+  const uint32_t v8_src = (uint32_t)(16 * (D == 128 ? U8 * v8_row_of(lane) + lane % U8 : lane));
   if constexpr (KV8) {
 #pragma unroll
     for (int n = 0; n < NI8; ++n) {
-      const int r = RPI8 * n + lane / U8, pu = lane % U8;
+      const int r = RPI8 * n + (D == 128 ? v8_row_of(lane) : lane / U8), pu = lane % U8;
 #pragma unroll
       for (int e = 0; e < 2; ++e) v8_dst[2 * n + e] = r * ROWB + (((2 * pu + e) ^ swz_vt<D>(r)) << 4);
     }
@@ -2164,7 +2181,7 @@ __device__ void decode_balanced(const AttnParams &p, char *smem) {
       for (int ks = 0; ks < QK; ++ks) k8[ks] = lds_read_b64_asm(land + lk_off[ks]);
       u32x4 v8[NI8];
 #pragma unroll
-      for (int n = 0; n < NI8; ++n) v8[n] = lds_read_b128_asm(land + 16 * D + n * 1024 + 16 * lane);
+      for (int n = 0; n < NI8; ++n) v8[n] = lds_read_b128_asm(land + 16 * D + n * 1024 + v8_src);
       lgkm_wait_n<0>(v8);
       lgkm_wait_n<0>(k8);
       if constexpr (NI8 == 2) {
@@ -2618,10 +2635,12 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
   }
   // fp8: where this lane's decoded V pieces go in the bf16 V stage.
   uint32_t v8_dst[KV8 ? 2 * NI8 : 1];
+  // E4M3: offset, inside a raw block, of the raw V unit this lane decodes.
+  const uint32_t v8_src = (uint32_t)(16 * (D == 128 ? U8 * v8_row_of(lane) + lane % U8 : lane));
   if constexpr (KV8) {
 #pragma unroll
     for (int n = 0; n < NI8; ++n) {
-      const int r = RPI8 * n + lane / U8, pu = lane % U8;
+      const int r = RPI8 * n + (D == 128 ? v8_row_of(lane) : lane / U8), pu = lane % U8;
 #pragma unroll
       for (int e = 0; e < 2; ++e) v8_dst[2 * n + e] = r * ROWB + (((2 * pu + e) ^ swz_vt<D>(r)) << 4);
     }
@@ -2756,7 +2775,7 @@ __device__ void decode_heads(const AttnParams &p, char *smem) {
       for (int ks = 0; ks < QK; ++ks) k8[ks] = lds_read_b64_asm(land + lk_off[ks]);
       u32x4 v8[NI8];
 #pragma unroll
-      for (int n = 0; n < NI8; ++n) v8[n] = lds_read_b128_asm(land + 16 * D + n * 1024 + 16 * lane);
+      for (int n = 0; n < NI8; ++n) v8[n] = lds_read_b128_asm(land + 16 * D + n * 1024 + v8_src);
       lgkm_wait_n<0>(v8);
       lgkm_wait_n<0>(k8);
       if constexpr (NI8 == 2) {
