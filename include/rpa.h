@@ -50,7 +50,8 @@ typedef enum {
   RPA_OK = 0,
   RPA_ERR_NULL = -1,        /* a required pointer is NULL                         */
   RPA_ERR_SHAPE = -2,       /* inconsistent or negative sizes                     */
-  RPA_ERR_UNSUPPORTED = -3, /* head_dim not 64/128, block_size not a multiple of 16     */
+  RPA_ERR_UNSUPPORTED = -3, /* head_dim not 64/128, block_size not a multiple of 16,
+                               or bf16 rel_logits misaligned or too wide (_ex)       */
   RPA_ERR_WORKSPACE = -4,   /* num_splits != 1 and the workspace is missing/small */
   RPA_ERR_HIP = -5          /* a HIP launch failed                                */
 } rpa_status;
@@ -254,6 +255,13 @@ int rpa_attn_varlen_fp8(const void *q, const void *key_cache, const void *value_
  *   rel_logits_bf16  0: rel_logits is fp32 [num_tokens, num_heads, R];
  *                  nonzero: bf16 of the same shape (half the bias bytes; the
  *                  values are widened exactly to fp32 where they are added).
+ *                  bf16 rel_logits must start on a 4-byte boundary (they
+ *                  are read as dwords), else RPA_ERR_UNSUPPORTED; so does a
+ *                  batch with prefill rows (max_seqlen_q * num_heads /
+ *                  num_kv_heads > 16) when (128 / G + 2) * num_heads * R * 2
+ *                  bytes reach 2 GiB (G = num_heads / num_kv_heads): the
+ *                  rows of one 128-row tile are read through one buffer
+ *                  resource.
  *   alibi_slopes   NULL, or fp32 [num_heads] device array: the logit of key t
  *                  for a row at position qa of q head h gains
  *                  alibi_slopes[h] * (t - qa), added like the relative bias

@@ -28,7 +28,7 @@ const char *rpa_status_string(int status) {
     case RPA_OK: return "ok";
     case RPA_ERR_NULL: return "a required pointer is NULL";
     case RPA_ERR_SHAPE: return "inconsistent or out-of-range sizes";
-    case RPA_ERR_UNSUPPORTED: return "unsupported head_dim or block_size";
+    case RPA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size or bf16 rel_logits layout";
     case RPA_ERR_WORKSPACE: return "workspace missing or too small for num_splits";
     case RPA_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";
@@ -129,6 +129,16 @@ int attn_impl(const void *q, const void *key_cache, const void *value_cache, boo
   if (head_dim != 64 && head_dim != 128) return RPA_ERR_UNSUPPORTED;
   if (block_size % 16 != 0) return RPA_ERR_UNSUPPORTED;
   if ((int64_t)num_tokens * num_heads * head_dim > ((int64_t)1 << 40)) return RPA_ERR_SHAPE;
+  // bf16 rel_logits in prefill tiles: one buffer resource spans the rows of a
+  // 128-row tile (up to 128 / G + 2 tokens of every head), below 2 GiB.
+  if (rel_bf16 && rel_extent > 0) {
+    // bf16 rel_logits are read as dwords: the array must start on one.
+    if (rel_logits && (reinterpret_cast<uintptr_t>(rel_logits) & 3) != 0) return RPA_ERR_UNSUPPORTED;
+    const int64_t g_ = num_heads / num_kv_heads;
+    const bool has_prefill = (int64_t)max_seqlen_q * g_ > rpa::kDecCols || g_ > rpa::kDecCols;
+    if (has_prefill && ((int64_t)rpa::kTileRows / g_ + 2) * num_heads * rel_extent * 2 + 64 >= ((int64_t)1 << 31))
+      return RPA_ERR_UNSUPPORTED;
+  }
   if (num_tokens == 0) return RPA_OK;
   // Pointers.
   if (!q || !key_cache || !value_cache || !block_table || !cache_seqlens || !cu_seqlens_q || !out)

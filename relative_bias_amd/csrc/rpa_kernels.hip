@@ -359,6 +359,7 @@ __device__ __forceinline__ int swz_v8(int r) {
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane j receives 16-bit
@@ -415,25 +416,68 @@ __device__ __forceinline__ void tile_bias_load(f32x16 *sacc, int kb, int qa, con
     }
   }
 }
-// bf16 rel_logits: the raw 16 bits land in the low half of each element (no
-// use of the loaded value here, so the loads stay in flight); tile_bf16_widen
-// turns them into fp32 once they have arrived.
-__device__ __forceinline__ void tile_bias_load_bf16(f32x16 *sacc, int kb, int qa, const uint16_t *rel_row, int R,
-                                                    int hf) {
+// bf16 rel_logits, fast form: the four logits of a group (8 bytes at a
+// 2-byte boundary, lowest distance first) come from one 12-byte load of the
+// three dwords around them, through a buffer resource over the tile's rows
+// with an 8-value margin on either side; el_base is the element offset of
+// this lane's logit at distance qa - 4 hf - 3 (the lowest distance of its
+// first group when kb = 0).  The three raw dwords land in the group's first
+// three elements; tile_bf16_widen4 shifts the pairs into place and widens.
+__device__ __forceinline__ void tile_bias_load4_bf16(f32x16 *sacc, __amdgpu_buffer_rsrc_t rs, int el_base, int kb) {
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int d = qa - (kb + key_of(kb2, j) + 4 * hf);
-      sacc[kb2][j] = __uint_as_float((uint32_t)rel_row[min(max(d, 0), R - 1)]);
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = el_base - (kb + 32 * kb2 + 8 * g4);
+      // The dword holding element d; a negative d wraps far past the
+      // resource, so it reads as zeros.
+      const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rs, 4 * (d >> 1), 0, 0);
+#pragma unroll
+      for (int m = 0; m < 3; ++m) sacc[kb2][4 * g4 + m] = __uint_as_float(v[m]);
     }
   }
 }
-__device__ __forceinline__ void tile_bf16_widen(f32x16 *sacc) {
+// Per-value form of the above for tiles whose rows sit at either end of the
+// array (no margin there): each logit by its own 2-byte load through the
+// same resource, clipped to the array (a load outside it reads zero; every
+// value of the band lies inside it).  The loads are awaited here and the
+// pairs packed into the layout of the fast form with its groups starting at
+// an even element (sh = 0 for tile_bf16_widen4); these tiles are rare.
+__device__ __forceinline__ void tile_bias_load1_bf16(f32x16 *sacc, __amdgpu_buffer_rsrc_t rs, int el_base, int kb) {
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2)
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sacc[kb2][j] = __uint_as_float(__float_as_uint(sacc[kb2][j]) << 16);
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int off = 2 * (el_base - (kb + 32 * kb2 + 8 * g4));
+      uint32_t e[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) e[m] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, off + 2 * m, 0, 0);
+      sacc[kb2][4 * g4] = __uint_as_float(e[0] | (e[1] << 16));
+      sacc[kb2][4 * g4 + 1] = __uint_as_float(e[2] | (e[3] << 16));
+    }
+  }
+}
+// sh: 16 when the groups of the tile start at an odd element (the same for
+// every group of a tile), else 0.
+__device__ __forceinline__ void tile_bf16_widen4(f32x16 *sacc, uint32_t sh) {
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const uint32_t w0 = __float_as_uint(sacc[kb2][4 * g4]), w1 = __float_as_uint(sacc[kb2][4 * g4 + 1]);
+      const uint32_t w2 = __float_as_uint(sacc[kb2][4 * g4 + 2]);
+      const uint32_t x0 = __builtin_amdgcn_alignbit(w1, w0, sh), x1 = __builtin_amdgcn_alignbit(w2, w1, sh);
+      float e0 = __uint_as_float(x0 << 16), e1 = __uint_as_float(x0 & 0xFFFF0000u);
+      float e2 = __uint_as_float(x1 << 16), e3 = __uint_as_float(x1 & 0xFFFF0000u);
+      // One group at a time: otherwise the compiler forms every group's
+      // shifted pairs first and holds them all.
+      asm volatile("" : "+v"(e0), "+v"(e1), "+v"(e2), "+v"(e3));
+      sacc[kb2][4 * g4] = e0;
+      sacc[kb2][4 * g4 + 1] = e1;
+      sacc[kb2][4 * g4 + 2] = e2;
+      sacc[kb2][4 * g4 + 3] = e3;
+    }
+  }
 }
 
 
@@ -892,23 +936,42 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   in_hi = __builtin_amdgcn_readfirstlane(in_hi);
   const int band_lo = __builtin_amdgcn_readfirstlane(qa_min - p.R + 1);
   const int band_hi = __builtin_amdgcn_readfirstlane(qa_max);
-  const float *rel_row = p.R > 0 ? p.rel_logits + ((int64_t)tok * p.H + head) * p.R : nullptr;
   // Fast bias loads: resource over rel_logits rows first .. last of this
   // tile (row index tok * H + head) with a 4-value margin on either side.
   const int64_t first_row = (int64_t)(tok0 + row0 / G) * p.H + g * G + row0 % G;
   const int64_t last_row = (int64_t)(tok0 + row_last / G) * p.H + g * G + row_last % G;
-  const int64_t bias_lo = first_row * p.R - 4, bias_hi = (last_row + 1) * p.R + 4;
   constexpr bool rel_bf16 = (FEAT & kFeatRelBf16) != 0;
-  const uint16_t *rel_row16 =
-      p.R > 0 ? reinterpret_cast<const uint16_t *>(p.rel_logits) + ((int64_t)tok * p.H + head) * p.R : nullptr;
-  const bool bias_fast = !rel_bf16 && p.R > 0 && bias_lo >= 0 && bias_hi <= (int64_t)p.num_tokens * p.H * p.R &&
-                         (bias_hi - bias_lo) * 4 < ((int64_t)1 << 31);
+  // bf16 rel_logits: the same with an 8-value margin (a group's 12-byte
+  // load starts up to one value below it and ends up to two above it); where
+  // the margin runs past either end of the array, the resource is clipped to
+  // the array and each value is loaded on its own (a 12-byte load that
+  // straddles an end would lose the values inside).  The host refuses calls
+  // whose tiles could span 2 GiB of bf16 rel_logits.
+  const int64_t bmargin = rel_bf16 ? 8 : 4, ebytes = rel_bf16 ? 2 : 4;
+  const int64_t total_e = (int64_t)p.num_tokens * p.H * p.R;
+  int64_t bias_lo_e = first_row * p.R - bmargin, bias_hi_e = (last_row + 1) * p.R + bmargin;
+  // bf16: an even start keeps the resource base on a dword (the array starts
+  // on one), so that the dword loads see the pairs of the array.
+  if constexpr (rel_bf16) bias_lo_e &= ~(int64_t)1;
+  const bool bias_in = bias_lo_e >= 0 && bias_hi_e <= total_e;
+  if constexpr (rel_bf16) {
+    bias_lo_e = max(bias_lo_e, (int64_t)0);
+    bias_hi_e = min(bias_hi_e, total_e);
+  }
+  const bool bias_fast = p.R > 0 && bias_in && (bias_hi_e - bias_lo_e) * ebytes < ((int64_t)1 << 31);
+  // Bias loads a band tile leaves in flight until the end of its iteration:
+  // 0 none (the bf16 per-value form waits for its own), 1: 8 per lane (the
+  // fast forms), 2: 32 (the fp32 per-value form).
+  const int band_wait = bias_fast ? 1 : rel_bf16 ? 0 : 2;
   __amdgpu_buffer_rsrc_t bias_rs = make_rsrc(p.rel_logits, 0);
   uint32_t bias_lane_base = 0;
-  if (bias_fast) {
-    bias_rs = make_rsrc(p.rel_logits + bias_lo, (uint32_t)((bias_hi - bias_lo) * 4));
-    const int64_t row_rel = ((int64_t)tok * p.H + head) * p.R - bias_lo;
+  int bias_el_base = 0;
+  if (bias_fast || (rel_bf16 && p.R > 0 && (bias_hi_e - bias_lo_e) * ebytes < ((int64_t)1 << 31))) {
+    bias_rs = make_rsrc(reinterpret_cast<const char *>(p.rel_logits) + bias_lo_e * ebytes,
+                        (uint32_t)((bias_hi_e - bias_lo_e) * ebytes));
+    const int64_t row_rel = ((int64_t)tok * p.H + head) * p.R - bias_lo_e;
     bias_lane_base = (uint32_t)(4 * (row_rel + qa - 4 * hf - 3));
+    bias_el_base = (int)(row_rel + qa - 4 * hf - 3);
   }
   // The bias enters the score accumulator as bias/scale, and the scale is
   // made positive: a negative scale negates Q instead (exact in bf16), and a
@@ -1123,9 +1186,22 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   auto wait_vm8 = [&]() { __builtin_amdgcn_s_waitcnt(0x0F78); };   // vmcnt(8)
   auto wait_vm32 = [&]() { __builtin_amdgcn_s_waitcnt(0x8F70); };  // vmcnt(32)
   auto load_bias = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
-    if (bias_fast) tile_bias_load4(sacc, bias_rs, bias_lane_base, kb);
-    else if (rel_bf16) tile_bias_load_bf16(sacc, kb, qa, rel_row16, p.R, hf);
-    else tile_bias_load(sacc, kb, qa, rel_row, p.R, hf);
+    if constexpr (rel_bf16) {
+      if (bias_fast) tile_bias_load4_bf16(sacc, bias_rs, bias_el_base, kb);
+      else tile_bias_load1_bf16(sacc, bias_rs, bias_el_base, kb);
+    } else if (bias_fast) {
+      tile_bias_load4(sacc, bias_rs, bias_lane_base, kb);
+    } else {
+      // Rows at either end of rel_logits: the lane's row pointer is formed
+      // here from an opaque copy of the lane id, so that nothing of this
+      // rare path is held across the tile loop.
+      int ln = l32;
+      asm volatile("" : "+v"(ln));
+      const int rs_ = min(row0 + 32 * w + ln, row_last);
+      const int qs_ = rs_ / G;
+      const int64_t row_b = ((int64_t)(tok0 + qs_) * p.H + g * G + (rs_ - qs_ * G)) * p.R;
+      tile_bias_load(sacc, kb, qa, p.rel_logits + row_b, p.R, hf);
+    }
   };
 
   auto is_band = [&](int kb) { return p.R > 0 && kb <= band_hi && kb + kTileKeys - 1 >= band_lo; };
@@ -1166,7 +1242,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
   };
   auto finish = [&](f32x16 *sacc, int kb) __attribute__((always_inline)) {
     if (is_band(kb)) {
-      if (rel_bf16) tile_bf16_widen(sacc);
+      if constexpr (rel_bf16) tile_bf16_widen4(sacc, bias_fast ? (uint32_t)((bias_el_base - kb) & 1) << 4 : 0u);
       if (is_full_band(kb)) tile_init<kInitFull>(sacc, bounds(kb), inv_scale, masked);
       else tile_init<kInitBand>(sacc, bounds(kb), inv_scale, masked);
     }
@@ -1293,7 +1369,7 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
         uint32_t krow = smem_u + row8, kuk = uk8, kraw = smem_u + (uint32_t)(kbw * D) + raw_at();
         asm volatile("" : "+v"(krow), "+v"(kuk), "+v"(kraw));
         mx_raw = phase_b8<D, L::v8Off(PAR), L::landK(PAR), L::kOff(PAR), alibi, alibi>(
-            smem, pb, oacc, lane, nxt, al_s, !band2 ? 0 : bias_fast ? 1 : 2, kraw, krow, kuk);
+            smem, pb, oacc, lane, nxt, al_s, !band2 ? 0 : band_wait, kraw, krow, kuk);
       } else {
         mx_raw = phase_b<D, L::vOff(PAR), alibi, false>(smem, pb, oacc, lane, nxt, al_s);
       }
@@ -1303,13 +1379,14 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
       // the raw K(j+3)) may stay in flight.
       if (!band2 && j + 2 < nt && !is_plain(tile_kb(j + 2))) start_general(cur, tile_kb(j + 2));
       __builtin_amdgcn_sched_barrier(0);
+      const int bw = band2 ? band_wait : 0;
       if constexpr (KV8) {
-        if (!band2) __builtin_amdgcn_s_waitcnt(vmcnt_enc(NI8));
-        else if (bias_fast) __builtin_amdgcn_s_waitcnt(vmcnt_enc(NI8 + 8));
+        if (bw == 0) __builtin_amdgcn_s_waitcnt(vmcnt_enc(NI8));
+        else if (bw == 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(NI8 + 8));
         else __builtin_amdgcn_s_waitcnt(vmcnt_enc(NI8 + 32));
       } else {
-        if (!band2) wait_vm0();
-        else if (bias_fast) wait_vm8();
+        if (bw == 0) wait_vm0();
+        else if (bw == 1) wait_vm8();
         else wait_vm32();
       }
       barrier_raw();

@@ -203,6 +203,26 @@ def test_ex_entry_validates_like_the_others(L):
     assert call(1, 1.0, 1.0, T=0, B=0, q=None) == OK
 
 
+def test_ex_entry_limits_the_width_of_bf16_rel_logits(L):
+    # A prefill tile reads its rows' bf16 rel_logits through one buffer
+    # resource: (128 / G + 2) * H * R * 2 bytes must stay below 2 GiB.
+    f = L.rpa_attn_varlen_ex
+    def call(R, bf16, maxq, q=FAKE):
+        return f(q, FAKE, FAKE, 0, 1.0, 1.0, FAKE, 4, FAKE, FAKE, 2, 2, 32, 8, 128, 8, 16, maxq, 0.125, 1, -1, -1,
+                 R, FAKE, bf16, None, 1, None, 0, FAKE, None, None)
+    wide = 1 << 21                            # (32 + 2) * 32 * 2^21 * 2 bytes = 4.6 GB
+    assert call(wide, 1, 64) == UNSUP
+    assert call(wide, 1, 1, q=None) == NULL   # decode-only batches never build prefill tiles
+    assert call(wide, 0, 64, q=None) == NULL  # fp32 rel_logits have a per-value form for such tiles
+    assert call(1 << 14, 1, 64, q=None) == NULL
+    # bf16 rel_logits are read as dwords: the array must start on a 4-byte boundary.
+    odd = ctypes.c_void_p(0x1002)
+    assert f(FAKE, FAKE, FAKE, 0, 1.0, 1.0, FAKE, 4, FAKE, FAKE, 2, 2, 32, 8, 128, 8, 16, 1, 0.125, 1, -1, -1,
+             64, odd, 1, None, 1, None, 0, FAKE, None, None) == UNSUP
+    assert f(None, FAKE, FAKE, 0, 1.0, 1.0, FAKE, 4, FAKE, FAKE, 2, 2, 32, 8, 128, 8, 16, 1, 0.125, 1, -1, -1,
+             64, odd, 0, None, 1, None, 0, FAKE, None, None) == NULL  # fp32 rel_logits: no such check
+
+
 def test_kv_cache_write_fp8_argument_errors(L):
     f = L.rpa_kv_cache_write_fp8
     assert f(FAKE, FAKE, FAKE, 3, 2, 64, 4, 16, 0.0, 1.0, FAKE, FAKE, None) == SHAPE
