@@ -42,6 +42,10 @@ CASES = {
     "prefill_d128": ([300, 77, 129], [900, 77, 1500], 16, 8, 128, 256, (-1, -1), [1, 2]),
     "prefill_d64_odd": ([33, 1], [33, 70], 3, 1, 64, 7, (-1, -1), [1]),  # 34*3*7 = 714 elements
     "mixed_window": ([1, 130, 1, 40, 1], [2000, 500, 70, 3000, 1], 16, 2, 128, 100, (127, 0), [1, 3]),
+    # Many band tiles away from the array's ends (the 12-byte group loads) with an odd R, so that
+    # groups start at odd and even elements; and MHA rows (G = 1) with a window.
+    "prefill_odd_R": ([200, 333], [700, 1000], 8, 2, 128, 257, (-1, -1), [1]),
+    "prefill_mha_odd_R": ([150, 90], [400, 300], 4, 4, 64, 33, (63, 0), [1, 2]),
 }
 PARAMS = [(n, S) for n in CASES for S in CASES[n][-1]]
 
