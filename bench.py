@@ -6,15 +6,20 @@ A step is one rpa_attn_varlen call (attention kernel + split combine) over
 one batch.  The headline workload is the batched decode batch (32 requests
 with 1024..8192 cached tokens, 32 q heads / 8 kv heads, head_dim 128, block
 size 16, rel_extent 128, planner-chosen splits); `value` is its algorithmic
-KV-and-operand bytes per second.  The same JSON line also carries the
-chunked-prefill batch (TFLOP/s against the bf16 MFMA peak), the 1M-token
-decode and the continuous-batching mix.  Inputs are resident in HBM before
-timing; the decode KV pool is rotated over three copies so that the 256 MB
-last-level cache cannot serve repeated steps.  The three extra workloads are
-timed after about 0.3 s of untimed calls, once the shader clock has settled
-(from idle it takes some 50 ms of prefill work to ramp up, and a prefill
-step timed during the ramp reads up to 20 % slow); the headline runs exactly
-the --warmup steps before its timed steps.
+KV-and-operand bytes per second.  The same JSON line also carries, each with
+its roofline block (and HBM traffic from the committed rocprofv3 summaries
+while the kernel source matches them): the chunked-prefill batch (TFLOP/s
+against the bf16 MFMA peak), the 1M-token decode (planner and 16..128
+splits), the continuous-batching mix, the E4M3-cache, ALiBi and bf16
+rel_logits variants, the paged KV write, the headline decode as a HIP graph,
+the measured HBM streaming-read ceiling, and the CPU oracle timed on bounded
+samples (--no-cpu skips it).  Inputs are resident in HBM before timing; KV
+pools are rotated over three copies so that the 256 MB last-level cache
+cannot serve repeated steps.  The extra workloads are timed after about 0.3 s
+of untimed calls, once the shader clock has settled (from idle it takes some
+50 ms of prefill work to ramp up, and a prefill step timed during the ramp
+reads up to 20 % slow); the headline runs exactly the --warmup steps before
+its timed steps.
 """
 from __future__ import annotations
 
