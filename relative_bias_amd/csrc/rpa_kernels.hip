@@ -151,7 +151,6 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t x0, uint32_t x1) {
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-__device__ __forceinline__ u32x4 zero16() { return u32x4{0u, 0u, 0u, 0u}; }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -360,14 +359,10 @@ __device__ __forceinline__ int swz_v8(int r) {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// ds_read_b64_tr_b16: within each 16-lane group, lane j receives 16-bit
-// element j%4 of the 8-byte rows addressed by lanes j/4, 4 + j/4, 8 + j/4
-// and 12 + j/4 of the group.
-__device__ __forceinline__ s16x4 lds_read_tr(const char *addr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(addr));
-}
+// ds_read_b64_tr_b16 (lds_read_tr_asm below): within each 16-lane group,
+// lane j receives 16-bit element j%4 of the 8-byte rows addressed by lanes
+// j/4, 4 + j/4, 8 + j/4 and 12 + j/4 of the group.
 
 // Key offset, within a tile, of accumulator element (kb2, j) of a lane with
 // hf = 0 (lanes with hf = 1 hold keys 4 further on).  K and V rows are staged
@@ -806,7 +801,7 @@ __device__ __forceinline__ float phase_b(const char *smem, const bf16x8 *pb, f32
 // registers.  Beside the PV MFMAs and the row max, the wave decodes its own
 // 16 raw K rows of tile j+2, which landed an iteration earlier, into K slot
 // KOFF: after kwait (how many vector-memory loads issued after them may stay
-// in flight: this iteration's V and K direct loads, plus 8 or 32 bias loads),
+// in flight: this iteration's V and K direct loads, plus 0, 8 or 32 bias loads),
 // their reads go out before the first V read, and one decoded 16-byte unit is
 // written per group from group 1 on.  LDS reads and writes complete in
 // order, so each operand's lgkmcnt counts the LDS operations issued after it.
@@ -1180,8 +1175,8 @@ __device__ void prefill_item(const AttnParams &p, const Item &it, int g, int s, 
     }
   };
   // The LDS writes of direct loads are tracked by vmcnt only: wait for them
-  // before the barrier that publishes a tile.  When the 32 bias loads of a
-  // later tile were issued after them, those may stay in flight.
+  // before the barrier that publishes a tile.  When the 8 or 32 bias loads
+  // of a later tile were issued after them, those may stay in flight.
   auto wait_vm0 = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
   auto wait_vm8 = [&]() { __builtin_amdgcn_s_waitcnt(0x0F78); };   // vmcnt(8)
   auto wait_vm32 = [&]() { __builtin_amdgcn_s_waitcnt(0x8F70); };  // vmcnt(32)
