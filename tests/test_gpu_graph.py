@@ -33,10 +33,10 @@ def _gpu():
     bnd.lib()
 
 
-def _check_oracle(wc, out, lse, tag):
+def _check_oracle(wc, out, lse, tag, alibi=None):
     ref_out, ref_lse = orc.attention(wc.q, wc.key_cache, wc.value_cache, wc.block_table, wc.cache_seqlens,
                                      wc.cu_seqlens_q, wc.softmax_scale, wc.causal, wc.window_size,
-                                     wc.rel_extent, wc.rel_logits)
+                                     wc.rel_extent, wc.rel_logits, alibi_slopes=alibi)
     out = out.float().cpu().double()
     lse = lse.cpu().double()
     err = (out - ref_out).abs()
@@ -48,12 +48,13 @@ def _check_oracle(wc, out, lse, tag):
         assert (lse[~inf] - ref_lse[~inf]).abs().max().item() <= LSE_MAX, f"{tag}: lse"
 
 
-def _run_graph_case(base, S, length_sets, seed):
+def _run_graph_case(base, S, length_sets, seed, alibi=None):
     """base: a CPU workload whose block table covers the longest lengths of
     every set.  length_sets: list of (q_lens, k_lens) with sum(q_lens) and
-    max(q_lens) bounded by base's."""
+    max(q_lens) bounded by base's.  alibi: optional fp32 [H] slopes (CPU)."""
     dev = "cuda"
     w = base.to(dev)
+    slopes = None if alibi is None else alibi.to(dev)
     T, H, D = w.q.shape
     out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((T, H), dtype=torch.float32, device=dev)
@@ -65,7 +66,7 @@ def _run_graph_case(base, S, length_sets, seed):
                             cache_seqlens=w.cache_seqlens, cu_seqlens_q=w.cu_seqlens_q,
                             max_seqlen_q=w.max_seqlen_q, softmax_scale=w.softmax_scale, causal=w.causal,
                             window_size=w.window_size, rel_extent=w.rel_extent, rel_logits=w.rel_logits,
-                            num_splits=S, out=o, lse=l, workspace=ws)
+                            num_splits=S, out=o, lse=l, workspace=ws, alibi_slopes=slopes)
 
     # Warm-up outside the capture (library load, first launches).
     call(out, lse)
@@ -102,7 +103,7 @@ def _run_graph_case(base, S, length_sets, seed):
         wc.cu_seqlens_q = torch.tensor(cu, dtype=torch.int32)
         wc.cache_seqlens = torch.tensor(k_lens, dtype=torch.int32)
         wc.q_lens, wc.k_lens = list(q_lens), list(k_lens)
-        _check_oracle(wc, got_out, got_lse, tag)
+        _check_oracle(wc, got_out, got_lse, tag, alibi)
 
 
 def _decode_sets(B, kmax, seed):
@@ -147,3 +148,19 @@ def test_graph_window_decode():
     base = wl.build([1] * B, [kmax] * B, num_heads=16, num_kv_heads=8, head_dim=128, rel_extent=128,
                     window_size=(511, 0), seed=14, name="graph_window")
     _run_graph_case(base, 1, _decode_sets(B, kmax, 5), seed=7)
+
+
+@pytest.mark.parametrize("S", [1, 3])
+def test_graph_mixed_batch_bf16_rel_and_alibi(S):
+    # The prefill variant with bf16 rel_logits and ALiBi slopes under replay:
+    # band tiles of the moving prefill chunk take the 12-byte group loads in
+    # the middle of the array and the per-value form at its ends.
+    base = wl.build([1, 1, 48, 1, 30], [1200, 1200, 1200, 1200, 1200], num_heads=8, num_kv_heads=2,
+                    head_dim=128, rel_extent=77, window_size=(-1, -1), seed=15, name="graph_mixed_bf16")
+    base.rel_logits = base.rel_logits.to(torch.bfloat16)
+    sets = [([1, 1, 48, 1, 30], [300, 17, 700, 1, 100]),
+            ([48, 1, 1, 30, 1], [1199, 45, 2, 30, 513]),
+            ([30, 48, 1, 1, 1], [31, 48, 900, 65, 5])]
+    H = base.q.shape[1]
+    slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32)
+    _run_graph_case(base, S, sets, seed=8, alibi=slopes)
