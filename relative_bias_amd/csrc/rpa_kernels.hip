@@ -239,28 +239,62 @@ struct Item {
 };
 
 // Maps a linear work-item index to (request, tile).  Items [0, ND) are the
-// decode items in request order, items [ND, ND + NP) the prefill q-tiles in
-// request order, the heaviest (last) tile of a request first.  Decode items
-// go first so that their streaming overlaps the prefill tiles' compute
-// (about 1 % on a mixed batch) instead of running in the tail.  Every
-// wave scans independently (the reads hit cache), so no barrier is needed.
+// decode items in request order, items [ND, ND + NP) the prefill q-tiles,
+// request by request, the heaviest (last) tile of a request first.  Decode
+// items go first so that their streaming overlaps the prefill tiles'
+// compute (about 1 % on a mixed batch) instead of running in the tail.
+// With at most 64 requests the prefill requests are taken longest first:
+// by the key count of their heaviest q-tile (the whole KV length, or the
+// window's span), ties in request order; a request's q-tiles stay
+// together, so its tiles still read the same K/V tiles at about the same
+// time, and the short requests end the grid instead of a long request's
+// tiles.  Every wave scans independently (the reads hit cache), so no
+// barrier is needed.
 __device__ Item resolve_item(const AttnParams &p, int item, bool decode_only, int rows) {
   const int lane = threadIdx.x & 63;
-  int np = 0, kmax = 0, nd = 0;
+  int kmax = 0, nd = 0;
   for (int c = 0; c < p.batch; c += 64) {
     const int b = c + lane;
     if (b < p.batch) {
       kmax = max(kmax, p.cache_seqlens[b]);
       const int lqb = p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b];
-      if (!decode_only) np += prefill_tiles(lqb, p.G, rows);
       nd += is_decode(lqb, p.G) ? 1 : 0;
     }
   }
   kmax = wave_max_i(kmax);
-  np = wave_sum_i(np);
-  nd = wave_sum_i(nd);
+  // Wave-uniform: readfirstlane lets the compiler see it, so that the
+  // branch on it stays scalar.
+  nd = __builtin_amdgcn_readfirstlane(wave_sum_i(nd));
   const bool pre = item >= nd;
   const int target = pre ? item - nd : item;
+  if (pre && p.batch <= 64) {
+    // Rank key of request lane: its heaviest tile's key count, then the
+    // request index (lower first), in one integer; -1 without prefill tiles.
+    const int b = lane;
+    int n = 0, key = -1;
+    if (b < p.batch) {
+      const int lq = p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b];
+      n = prefill_tiles(lq, p.G, rows);
+      int span = p.cache_seqlens[b];
+      if (p.left >= 0) span = min(span, p.left + rows / p.G);
+      if (n > 0) key = (min(max(span, 0), 1 << 24) << 6) | (63 - b);
+    }
+    // Tiles of the requests ranked before this one.
+    int excl = 0;
+    for (int i = 0; i < p.batch; ++i) {
+      const int ki = __builtin_amdgcn_readlane(key, i);
+      const int ni = __builtin_amdgcn_readlane(n, i);
+      excl += ki > key ? ni : 0;
+    }
+    const unsigned long long mask = __ballot(n > 0 && target >= excl && target < excl + n);
+    if (mask) {
+      const int src = __ffsll((long long)mask) - 1;
+      const int k = target - __shfl(excl, src);
+      return Item{__builtin_amdgcn_readfirstlane(src), __builtin_amdgcn_readfirstlane(__shfl(n, src) - 1 - k), 1,
+                  __builtin_amdgcn_readfirstlane(kmax)};
+    }
+    return Item{-1, 0, 0, kmax};
+  }
   int base = 0;
   for (int c = 0; c < p.batch; c += 64) {
     const int b = c + lane;

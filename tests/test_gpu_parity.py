@@ -418,6 +418,29 @@ def _random_case(seed):
                 window=(left, right), scale=scale, S=S)
 
 
+@pytest.mark.parametrize("B", [63, 64, 65])
+def test_prefill_request_order_edges(B):
+    """Batches at the 64-request limit of the longest-first order of prefill
+    requests (65 keeps request order): prefill requests of equal KV lengths
+    (ties), empty query ranges and decode requests mixed in, a window on half
+    of the cases.  Every q-tile must be computed exactly once."""
+    g = torch.Generator().manual_seed(500 + B)
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=g))
+    q_lens, k_lens = [], []
+    for i in range(B):
+        kind = ri(0, 3)
+        lq = 0 if kind == 0 else (ri(1, 4) if kind == 1 else ri(5, 90))
+        lk = (300 if i % 5 == 0 else ri(0, 400)) + lq
+        q_lens.append(lq)
+        k_lens.append(lk)
+    window = (63, 0) if B % 2 else (-1, -1)
+    w = wl.build(q_lens, k_lens, num_heads=8, num_kv_heads=2, head_dim=64, rel_extent=40, window_size=window,
+                 seed=B, extra_pages=2, poison=True)
+    ref = _oracle(w)
+    out, lse = _gpu_run(w.to("cuda"), 1)
+    _compare(out, lse, *ref, tag=f"request order B={B}")
+
+
 @pytest.mark.parametrize("seed", list(range(24)))
 def test_random_configurations(seed):
     """Parity on 24 seeded random configurations (mixed decode and prefill
