@@ -49,7 +49,9 @@ extern "C" {
 typedef enum {
   RPA_OK = 0,
   RPA_ERR_NULL = -1,        /* a required pointer is NULL                         */
-  RPA_ERR_SHAPE = -2,       /* inconsistent or negative sizes                     */
+  RPA_ERR_SHAPE = -2,       /* inconsistent or negative sizes, or key positions
+                               past 32 bits (max_pages_per_seq * block_size
+                               + max_seqlen_q + 128 >= 2^31)                     */
   RPA_ERR_UNSUPPORTED = -3, /* head_dim not 64/128, block_size not a multiple of 16,
                                or bf16 rel_logits misaligned or too wide (_ex)       */
   RPA_ERR_WORKSPACE = -4,   /* num_splits != 1 and the workspace is missing/small */
@@ -83,7 +85,10 @@ typedef enum {
  *                  |rel_logits| must stay below 2^27.
  *   causal         nonzero = bottom-right causal mask.
  *   window_left,
- *   window_right   sliding window; -1 leaves that side unbounded.
+ *   window_right   sliding window; -1 leaves that side unbounded, and so does
+ *                  any side that reaches past every key (left >=
+ *                  max_pages_per_seq * block_size, right >= max_seqlen_q):
+ *                  any value up to 2^31 - 1 is accepted.
  *   rel_extent     R >= 0; 0 means no bias (rel_logits may then be NULL).
  *   rel_logits     fp32 [num_tokens, num_heads, R].
  *   num_splits     S in [0, RPA_MAX_SPLITS].  S >= 1: each work item's

@@ -123,6 +123,16 @@ int attn_impl(const void *q, const void *key_cache, const void *value_cache, boo
       rel_extent < 0 || window_left < -1 || window_right < -1)
     return RPA_ERR_SHAPE;
   if (num_heads % num_kv_heads != 0) return RPA_ERR_SHAPE;
+  // Key positions and row offsets (qa = i + Lk - Lq, with Lk at most
+  // max_pages_per_seq * block_size) are 32-bit on the device.
+  if ((int64_t)max_pages_per_seq * block_size + max_seqlen_q + rpa::kTileRows >= ((int64_t)1 << 31))
+    return RPA_ERR_SHAPE;
+  // A window side that reaches past every key leaves that side unbounded:
+  // no key lies more than max_pages_per_seq * block_size - 1 to the left of
+  // a row, nor more than max_seqlen_q - 1 to its right.  Taken as -1 here,
+  // so that the device never adds a window near 2^31 to a position.
+  if (window_left >= 0 && (int64_t)window_left >= (int64_t)max_pages_per_seq * block_size) window_left = -1;
+  if (window_right >= 0 && window_right >= max_seqlen_q) window_right = -1;
   if (num_splits < 0 || num_splits > RPA_MAX_SPLITS) return RPA_ERR_SHAPE;
   if (!std::isfinite(softmax_scale)) return RPA_ERR_SHAPE;
   if (batch == 0 && num_tokens > 0) return RPA_ERR_SHAPE;

@@ -105,6 +105,15 @@ def test_bad_shapes(L, kw):
     assert _attn(L, **kw) == SHAPE
 
 
+def test_key_positions_must_fit_32_bits(L):
+    # max_pages_per_seq * block_size + max_seqlen_q + 128 must stay below 2^31.
+    P = (2 ** 31 - 130) // 16
+    assert _attn(L, P=P, BS=16, maxq=2, q=None) == NULL
+    assert _attn(L, P=P + 1, BS=16, maxq=2, q=None) == SHAPE
+    # Windows of any size up to 2^31 - 1 are accepted.
+    assert _attn(L, left=2 ** 31 - 1, right=2 ** 31 - 1, q=None) == NULL
+
+
 @pytest.mark.parametrize("kw", [dict(D=96), dict(D=256), dict(D=32), dict(BS=8), dict(BS=24)])
 def test_unsupported(L, kw):
     assert _attn(L, **kw) == UNSUP

@@ -7,6 +7,7 @@ Small cases are compared element by element on every output; the full-size
 workloads, in the split configuration the benchmark times, are compared on
 sampled tokens / heads that the oracle computes one by one.
 """
+import dataclasses
 import math
 
 import pytest
@@ -416,6 +417,29 @@ def _random_case(seed):
     S = [1, 1, 2, 5, 0][ri(0, 4)]
     return dict(q_lens=q_lens, k_lens=k_lens, H=G * Hkv, Hkv=Hkv, D=D, BS=BS, R=R, causal=causal,
                 window=(left, right), scale=scale, S=S)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_windows_past_every_key(causal):
+    """Window sides that reach past every key (up to 2^31 - 1) give exactly
+    the unbounded result, rows with Lk < Lq included; sides just short of
+    that reach still match the oracle."""
+    w = wl.build([1, 40, 3, 90], [300, 97, 3, 60], num_heads=8, num_kv_heads=2, head_dim=64, rel_extent=24,
+                 causal=causal, seed=31)
+    wg = w.to("cuda")
+    base = _gpu_run(dataclasses.replace(wg, window_size=(-1, -1)), 1)
+    big = 2 ** 31 - 1
+    for win in [(big, big), (big, -1), (-1, big), (big, 0)]:
+        got = _gpu_run(dataclasses.replace(wg, window_size=win), 1)
+        if win[1] != 0:
+            assert torch.equal(got[0], base[0]) and torch.equal(got[1], base[1]), f"window {win}"
+        ref = _oracle(dataclasses.replace(w, window_size=win))
+        _compare(*got, *ref, tag=f"window {win} causal={causal}")
+    # The widest sides the device still applies: max_pages_per_seq * block_size - 1
+    # on the left, max_seqlen_q - 1 on the right.
+    win = (w.block_table.shape[1] * w.block_size - 1, w.max_seqlen_q - 1)
+    got = _gpu_run(dataclasses.replace(wg, window_size=win), 1)
+    _compare(*got, *_oracle(dataclasses.replace(w, window_size=win)), tag=f"window {win} causal={causal}")
 
 
 @pytest.mark.parametrize("B", [63, 64, 65])
