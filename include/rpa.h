@@ -51,7 +51,7 @@ typedef enum {
   RPA_ERR_NULL = -1,        /* a required pointer is NULL                         */
   RPA_ERR_SHAPE = -2,       /* inconsistent or negative sizes, or key positions
                                past 32 bits (max_pages_per_seq * block_size
-                               + max_seqlen_q + 128 >= 2^31)                     */
+                               + max_seqlen_q + rel_extent + 128 >= 2^31)        */
   RPA_ERR_UNSUPPORTED = -3, /* head_dim not 64/128, block_size not a multiple of 16,
                                or bf16 rel_logits misaligned or too wide (_ex)       */
   RPA_ERR_WORKSPACE = -4,   /* num_splits != 1 and the workspace is missing/small */

@@ -123,9 +123,10 @@ int attn_impl(const void *q, const void *key_cache, const void *value_cache, boo
       rel_extent < 0 || window_left < -1 || window_right < -1)
     return RPA_ERR_SHAPE;
   if (num_heads % num_kv_heads != 0) return RPA_ERR_SHAPE;
-  // Key positions and row offsets (qa = i + Lk - Lq, with Lk at most
-  // max_pages_per_seq * block_size) are 32-bit on the device.
-  if ((int64_t)max_pages_per_seq * block_size + max_seqlen_q + rpa::kTileRows >= ((int64_t)1 << 31))
+  // Key positions, row offsets (qa = i + Lk - Lq, with Lk at most
+  // max_pages_per_seq * block_size) and the band's lower end qa - R + 1 are
+  // 32-bit on the device.
+  if ((int64_t)max_pages_per_seq * block_size + max_seqlen_q + rel_extent + rpa::kTileRows >= ((int64_t)1 << 31))
     return RPA_ERR_SHAPE;
   // A window side that reaches past every key leaves that side unbounded:
   // no key lies more than max_pages_per_seq * block_size - 1 to the left of

@@ -106,10 +106,13 @@ def test_bad_shapes(L, kw):
 
 
 def test_key_positions_must_fit_32_bits(L):
-    # max_pages_per_seq * block_size + max_seqlen_q + 128 must stay below 2^31.
+    # max_pages_per_seq * block_size + max_seqlen_q + rel_extent + 128 must stay below 2^31.
     P = (2 ** 31 - 130) // 16
     assert _attn(L, P=P, BS=16, maxq=2, q=None) == NULL
     assert _attn(L, P=P + 1, BS=16, maxq=2, q=None) == SHAPE
+    R = 2 ** 31 - 4 * 16 - 2 - 128
+    assert _attn(L, R=R - 1, rel=FAKE, q=None) == NULL
+    assert _attn(L, R=R, rel=FAKE, q=None) == SHAPE
     # Windows of any size up to 2^31 - 1 are accepted.
     assert _attn(L, left=2 ** 31 - 1, right=2 ** 31 - 1, q=None) == NULL
 
