@@ -419,6 +419,19 @@ def _random_case(seed):
                 window=(left, right), scale=scale, S=S)
 
 
+@pytest.mark.parametrize("G", [64, 128, 256])
+def test_large_gqa_groups(G):
+    """GQA groups of 64 to 256 query heads per kv head: a 128-row q-tile
+    holds two tokens, one token or half of one token's heads; decode tokens
+    run as prefill q-tiles (more than 16 columns)."""
+    w = wl.build([3, 1, 20, 0], [50, 200, 40, 7], num_heads=G, num_kv_heads=1, head_dim=64, rel_extent=9,
+                 seed=G, extra_pages=2, poison=True)
+    ref = _oracle(w)
+    for S in (1, 2):
+        out, lse = _gpu_run(w.to("cuda"), S)
+        _compare(out, lse, *ref, tag=f"G={G} S={S}")
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_windows_past_every_key(causal):
     """Window sides that reach past every key (up to 2^31 - 1) give exactly
